@@ -1,0 +1,208 @@
+/*
+ * pa.h -- C ABI of libpa.so: one paged-attention step on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The step follows the attention layer of a continuous-batching inference
+ * step as the pages describe it:
+ *   [P1] "vLLM 推理流程分析" (blog.chen3feng.top): §5.1.2 _prepare_inputs
+ *        (positions, query_start_loc, seq_lens, compute_slot_mapping), §6.1
+ *        attention dispatch (write the new K/V first, then attend), §6.2 the
+ *        paged FlashAttention call, §6.3 the KV-cache write
+ *        (reshape_and_cache_flash with slot_mapping, kv_cache_dtype, k_scale,
+ *        v_scale), §10.1-10.2 the cache's life over prefill and decode.
+ *   [P5] "vLLM 源码完全拆解（十六）：把十五篇机制拼成一张可执行的源码阅读地图"
+ *        (pinghaoyang.com.cn): third walk-through path (slot = physical block
+ *        * S + offset; paging changes where K/V are fetched, not the
+ *        attention definition; partitioned evaluation with a rescaling
+ *        merge), fourth walk-through path (query_start_loc as a prefix sum of
+ *        per-request token counts; the metadata consistency checks).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All sizes are element counts unless a name ends in _bytes.
+ * - "device" pointers are HIP device memory on the current device; "host"
+ *   pointers are ordinary CPU memory.  The library never takes ownership of
+ *   a buffer, never frees one, and keeps no pointer after a call returns.
+ * - Calls that launch work are asynchronous on the given stream (NULL means
+ *   the default stream).  Work enqueued by one call on a stream sees the
+ *   effects of earlier calls on that stream (so pa_write_kv then
+ *   pa_attention on one stream attends over the freshly written rows, as
+ *   [P1] §6.1 orders them).
+ * - Errors are reported through pa_status only; nothing is thrown across
+ *   the ABI.  On any status other than PA_OK the call has enqueued no work
+ *   and pa_last_error() (per thread) describes the problem.  PA_ERR_HIP means
+ *   a HIP runtime call failed.
+ * - The library is thread-compatible: concurrent calls on different streams
+ *   are allowed; the workspace passed to pa_attention must not be shared by
+ *   calls that may run concurrently.
+ *
+ * KV pool layout (chosen for gfx950, differs from the pages' layout)
+ * ------------------------------------------------------------------
+ * The pool is two arrays, k_cache and v_cache, each holding num_blocks
+ * blocks of block_size token slots for num_kv_heads heads of head_dim
+ * elements.  Slot s lives in block s / block_size at offset s % block_size.
+ * Within a block each kv head owns one contiguous tile:
+ *   k_cache: [num_blocks][num_kv_heads][head_dim / E][block_size][E]
+ *            E = 16 / sizeof(element) (4 fp32, 8 bf16, 16 fp8): the key
+ *            row of a slot is cut into 16-byte chunks; chunk c of all
+ *            block_size slots is contiguous.
+ *   v_cache: [num_blocks][num_kv_heads][head_dim][block_size]
+ *            (the tile is stored dimension-major).
+ * pa_kv_elem_offset() returns the element index of any (block, offset,
+ * head, dim) and is the authoritative definition of this layout.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The same type as hipStream_t (an opaque HIP stream handle). */
+struct ihipStream_t;
+typedef struct ihipStream_t *pa_stream_t;
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1,  /* a null pointer, negative size or inconsistent shape  */
+  PA_ERR_UNSUPPORTED = 2,  /* a valid request this build does not implement        */
+  PA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required           */
+  PA_ERR_VALIDATION = 4,   /* metadata failed the consistency checks (PA_VALIDATE) */
+  PA_ERR_HIP = 5           /* a HIP runtime call failed                            */
+} pa_status;
+
+typedef enum pa_dtype {
+  PA_F32 = 0,       /* IEEE binary32                                          */
+  PA_BF16 = 1,      /* bfloat16                                               */
+  PA_FP8_E4M3 = 2   /* OCP FP8 E4M3FN (bias 7, max 448, no inf), pool only    */
+} pa_dtype;
+
+/* A KV pool ([P1] §6.2: key_cache / value_cache, one per K and V).
+ * Supported: block_size 16; head_dim 64 or 128; kv_dtype F32, BF16 or
+ * FP8_E4M3.  k_scale / v_scale are the per-tensor dequantisation scales of
+ * an FP8 pool (stored code * scale = value) and are ignored otherwise. */
+typedef struct pa_kv_pool {
+  void *k_cache;            /* device, pa_kv_cache_bytes() bytes */
+  void *v_cache;            /* device, pa_kv_cache_bytes() bytes */
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  pa_dtype kv_dtype;
+  float k_scale;
+  float v_scale;
+} pa_kv_pool;
+
+/* One step's ragged batch ([P1] §5.1.3 common attention metadata).
+ * Request i owns query rows query_start_loc[i] .. query_start_loc[i+1]-1 of
+ * the flat token stream (its c_i new tokens) and has seq_lens[i] tokens in
+ * total including them, so new token t sits at position
+ * seq_lens[i] - c_i + t.  block_table row i lists the physical blocks of
+ * logical blocks 0, 1, ...; only its first ceil(seq_lens[i] / block_size)
+ * entries are ever read.  The host mirrors must hold the same values as the
+ * device arrays (the caller builds them on the CPU anyway); the library
+ * reads them to plan the launch without a device-to-host copy. */
+typedef struct pa_batch {
+  int32_t num_seqs;                     /* N >= 0                              */
+  int32_t num_tokens;                   /* T = query_start_loc[N]              */
+  const int32_t *query_start_loc;       /* device [N + 1]                      */
+  const int32_t *seq_lens;              /* device [N]                          */
+  const int32_t *block_table;           /* device [N][bt_stride]               */
+  int32_t bt_stride;                    /* elements between block_table rows   */
+  const int32_t *query_start_loc_host;  /* host   [N + 1], same values         */
+  const int32_t *seq_lens_host;         /* host   [N],     same values         */
+} pa_batch;
+
+/* ---------------------------------------------------------------------- */
+
+/* a0 -- step metadata on the host ([P1] §5.1.2; [P5] fourth walk-through
+ * path).  query_start_loc[0] = 0, query_start_loc[i+1] = query_start_loc[i]
+ * + num_scheduled[i]; seq_lens[i] = num_computed[i] + num_scheduled[i].
+ * All pointers are host memory; query_start_loc has num_seqs + 1 entries.
+ * PA_ERR_INVALID_ARG for negative counts or a total above INT32_MAX. */
+pa_status pa_prepare_metadata(int32_t num_seqs, const int32_t *num_computed,
+                              const int32_t *num_scheduled, int32_t *query_start_loc,
+                              int32_t *seq_lens);
+
+/* a1 -- slot derivation on the device ([P1] §5.1.2 compute_slot_mapping;
+ * [P5] third walk-through path).  For every new token t of request i, with
+ * p = seq_lens[i] - c_i + t:
+ *   slot_mapping[query_start_loc[i] + t] =
+ *       block_table[i][p / block_size] * block_size + p % block_size.
+ * slot_mapping: device int64 [batch->num_tokens], written.  block_size must
+ * be 16.  The host mirrors of the batch are used to size the launch. */
+pa_status pa_slot_mapping(const pa_batch *batch, int32_t block_size, int64_t *slot_mapping,
+                          pa_stream_t stream);
+
+/* a2 -- KV scatter ([P1] §6.3 reshape_and_cache_flash).  For every token n
+ * with slot_mapping[n] >= 0, stores key[n] and value[n] (each
+ * [num_kv_heads][head_dim], in_dtype) into that slot of the pool.  Same
+ * dtype: a bit copy (F32 -> F32, BF16 -> BF16).  FP8 pool (in_dtype F32 or
+ * BF16): y = x / scale in IEEE fp32, then the nearest E4M3FN value with ties
+ * to even, |y| > 448 saturating to +-448, NaN -> 0x7F.  Negative slots are
+ * skipped (padding tokens); slots at or beyond num_blocks * block_size are
+ * skipped as well (and reported under PA_VALIDATE).  Duplicate non-negative
+ * slots within one call leave the slot holding one of the rows.
+ * key, value: device [num_tokens][num_kv_heads][head_dim]; slot_mapping:
+ * device int64 [num_tokens]. */
+pa_status pa_write_kv(const pa_kv_pool *pool, const void *key, const void *value,
+                      pa_dtype in_dtype, const int64_t *slot_mapping, int32_t num_tokens,
+                      pa_stream_t stream);
+
+/* Device workspace pa_attention needs for this batch (bytes), or 0 when the
+ * arguments are invalid (pa_last_error() says why). */
+size_t pa_attention_workspace_bytes(const pa_kv_pool *pool, const pa_batch *batch,
+                                    int32_t num_q_heads);
+
+/* a3..a7 -- attention over the paged pool ([P1] §6.2 flash_attn_varlen_func
+ * with block_table and causal=True; [P5] third walk-through path).  For
+ * every new token n = query_start_loc[i] + t of request i and query head h:
+ *   visible keys j = 0 .. p (p = seq_lens[i] - c_i + t) when causal,
+ *                    0 .. seq_lens[i] - 1 when not;
+ *   s_j = softmax_scale * (query[n][h] . K_j[h / g]),  g = num_q_heads / num_kv_heads;
+ *   output[n][h] = sum_j softmax(s)_j * V_j[h / g],
+ * with K_j / V_j read from the pool through block_table (FP8 pools are
+ * dequantised with k_scale / v_scale).  Accumulation is fp32; the output is
+ * rounded to q_dtype.  Supported: q_dtype F32 with an F32 pool; q_dtype
+ * BF16 with a BF16 or FP8 pool; num_q_heads a multiple of num_kv_heads with
+ * g <= 16.
+ * query, output: device [num_tokens][num_q_heads][head_dim] (q_dtype).
+ * workspace: device, at least pa_attention_workspace_bytes() bytes, 256-byte
+ * aligned; its contents need no initialisation and are scratch after the
+ * call.  Requests with c_i = 0 are skipped. */
+pa_status pa_attention(const pa_kv_pool *pool, const pa_batch *batch, const void *query,
+                       pa_dtype q_dtype, int32_t num_q_heads, float softmax_scale,
+                       int32_t causal, void *output, void *workspace, size_t workspace_bytes,
+                       pa_stream_t stream);
+
+/* Bytes of each of k_cache and v_cache for this pool's shape and dtype. */
+size_t pa_kv_cache_bytes(const pa_kv_pool *pool);
+
+/* Element index (not byte offset) of (block, offset, head, dim) in k_cache
+ * (which = 0) or v_cache (which = 1); -1 for out-of-range arguments. */
+int64_t pa_kv_elem_offset(const pa_kv_pool *pool, int32_t which, int64_t block, int32_t offset,
+                          int32_t head, int32_t dim);
+
+/* Human-readable name of a status code (static storage). */
+const char *pa_status_string(pa_status status);
+
+/* Detail of the last failing call on this thread (empty if none). */
+const char *pa_last_error(void);
+
+/* Kernel timing for measurement.  While enabled, every kernel the library
+ * launches is bracketed by a pair of HIP events recorded on the stream it
+ * runs on.  pa_profile_read() waits for the recorded events and returns,
+ * for the kernel named `kernel`, the number of launches and their summed
+ * duration in milliseconds since the last reset.  Enabling or disabling
+ * resets the records.  Not for use under HIP graph capture. */
+pa_status pa_profile_enable(int32_t enable);
+pa_status pa_profile_read(const char *kernel, int32_t *launches, double *total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,543 @@
+// C ABI of libpa.so: argument checks, the host-side plan of a step, the
+// workspace layout, a pinned staging ring for the plan's upload, and the
+// kernel-timing hooks.  Every step of the computation itself runs in the HIP
+// kernels of k_write.hip, k_decode.hip and k_extend.hip.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "pa_internal.h"
+
+namespace pa {
+
+// ------------------------------------------------------------------ errors --
+
+static thread_local std::string g_last_error;
+
+static pa_status fail(pa_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+static pa_status hip_fail(hipError_t e, const char *what) {
+  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// --------------------------------------------------------------- profiling --
+
+struct ProfRec {
+  const char *name;
+  hipEvent_t start, stop;
+};
+
+static std::mutex g_prof_mu;
+static bool g_prof_on = false;
+static std::vector<ProfRec> g_prof;
+static std::vector<hipEvent_t> g_prof_free;
+static thread_local int g_prof_open = -1;
+
+static hipEvent_t prof_event() {
+  if (!g_prof_free.empty()) {
+    hipEvent_t e = g_prof_free.back();
+    g_prof_free.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+void prof_begin(const char *name, hipStream_t s) {
+  if (!g_prof_on) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  ProfRec r{name, prof_event(), prof_event()};
+  if (!r.start || !r.stop) return;
+  hipEventRecord(r.start, s);
+  g_prof.push_back(r);
+  g_prof_open = (int)g_prof.size() - 1;
+}
+
+void prof_end(hipStream_t s) {
+  if (!g_prof_on || g_prof_open < 0) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  hipEventRecord(g_prof[g_prof_open].stop, s);
+  g_prof_open = -1;
+}
+
+static void prof_reset_locked() {
+  for (auto &r : g_prof) {
+    hipEventSynchronize(r.stop);
+    g_prof_free.push_back(r.start);
+    g_prof_free.push_back(r.stop);
+  }
+  g_prof.clear();
+}
+
+// ------------------------------------------------------ pinned staging ring --
+// The plan of a step (work lists) is built on the host and uploaded into the
+// caller's workspace.  Uploads go through pinned buffers so they are truly
+// asynchronous; a buffer is reused only after the copy that last read it has
+// completed (checked with an event).
+
+struct StageSlot {
+  void *host = nullptr;
+  size_t cap = 0;
+  hipEvent_t done = nullptr;
+  bool pending = false;
+};
+
+static std::mutex g_stage_mu;
+static std::vector<StageSlot> g_stage(8);
+static unsigned g_stage_next = 0;
+
+static pa_status upload(void *dst, const void *src, size_t bytes, hipStream_t s) {
+  if (bytes == 0) return PA_OK;
+  std::lock_guard<std::mutex> lk(g_stage_mu);
+  StageSlot &slot = g_stage[g_stage_next++ % g_stage.size()];
+  hipError_t e;
+  if (slot.pending) {
+    if ((e = hipEventSynchronize(slot.done)) != hipSuccess) return hip_fail(e, "staging wait");
+    slot.pending = false;
+  }
+  if (!slot.done && (e = hipEventCreateWithFlags(&slot.done, hipEventDisableTiming)) != hipSuccess)
+    return hip_fail(e, "staging event");
+  if (slot.cap < bytes) {
+    if (slot.host) hipHostFree(slot.host);
+    slot.host = nullptr;
+    size_t cap = std::max<size_t>(bytes, 64 << 10);
+    if ((e = hipHostMalloc(&slot.host, cap, hipHostMallocDefault)) != hipSuccess) {
+      slot.cap = 0;
+      return hip_fail(e, "staging buffer");
+    }
+    slot.cap = cap;
+  }
+  memcpy(slot.host, src, bytes);
+  if ((e = hipMemcpyAsync(dst, slot.host, bytes, hipMemcpyHostToDevice, s)) != hipSuccess)
+    return hip_fail(e, "plan upload");
+  if ((e = hipEventRecord(slot.done, s)) != hipSuccess) return hip_fail(e, "staging record");
+  slot.pending = true;
+  return PA_OK;
+}
+
+// ---------------------------------------------------------------- checks ---
+
+static int elem_bytes(pa_dtype d) { return d == PA_F32 ? 4 : d == PA_BF16 ? 2 : 1; }
+
+static bool env_flag(const char *name) {
+  const char *v = getenv(name);
+  return v && *v && strcmp(v, "0") != 0;
+}
+
+static pa_status check_pool(const pa_kv_pool *p, bool need_ptrs) {
+  if (!p) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
+  if (need_ptrs && (!p->k_cache || !p->v_cache)) return fail(PA_ERR_INVALID_ARG, "pool cache pointer is NULL");
+  if (p->num_blocks <= 0 || p->num_kv_heads <= 0 || p->block_size <= 0 || p->head_dim <= 0)
+    return fail(PA_ERR_INVALID_ARG, "pool sizes must be positive");
+  if (p->kv_dtype != PA_F32 && p->kv_dtype != PA_BF16 && p->kv_dtype != PA_FP8_E4M3)
+    return fail(PA_ERR_INVALID_ARG, "unknown kv_dtype %d", (int)p->kv_dtype);
+  if (p->block_size != kBlock) return fail(PA_ERR_UNSUPPORTED, "block_size %d (only 16)", p->block_size);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d (only 64, 128)", p->head_dim);
+  if (p->kv_dtype == PA_FP8_E4M3) {
+    if (!(std::isfinite(p->k_scale) && p->k_scale > 0 && std::isfinite(p->v_scale) && p->v_scale > 0))
+      return fail(PA_ERR_INVALID_ARG, "fp8 pool needs finite positive k_scale and v_scale");
+  }
+  return PA_OK;
+}
+
+static pa_status check_batch(const pa_batch *b, bool need_dev) {
+  if (!b) return fail(PA_ERR_INVALID_ARG, "batch is NULL");
+  if (b->num_seqs < 0 || b->num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "negative batch size");
+  if (!b->query_start_loc_host || !b->seq_lens_host)
+    return fail(PA_ERR_INVALID_ARG, "batch host mirrors are NULL");
+  if (need_dev && b->num_seqs > 0 &&
+      (!b->query_start_loc || !b->seq_lens || !b->block_table))
+    return fail(PA_ERR_INVALID_ARG, "batch device arrays are NULL");
+  if (b->bt_stride < 0) return fail(PA_ERR_INVALID_ARG, "negative bt_stride");
+  const int32_t *q = b->query_start_loc_host, *L = b->seq_lens_host;
+  if (q[0] != 0) return fail(PA_ERR_INVALID_ARG, "query_start_loc[0] = %d, expected 0", q[0]);
+  for (int32_t i = 0; i < b->num_seqs; ++i) {
+    const int32_t c = q[i + 1] - q[i];
+    if (c < 0) return fail(PA_ERR_INVALID_ARG, "query_start_loc decreases at request %d", i);
+    if (L[i] < c) return fail(PA_ERR_INVALID_ARG, "seq_lens[%d] = %d < %d new tokens", i, L[i], c);
+    const int64_t nb = ((int64_t)L[i] + kBlock - 1) / kBlock;
+    if (nb > b->bt_stride) return fail(PA_ERR_INVALID_ARG, "request %d needs %lld blocks > bt_stride %d", i, (long long)nb, b->bt_stride);
+  }
+  if (q[b->num_seqs] != b->num_tokens)
+    return fail(PA_ERR_INVALID_ARG, "query_start_loc[N] = %d != num_tokens %d", q[b->num_seqs], b->num_tokens);
+  return PA_OK;
+}
+
+// Deep checks of device-side metadata (PA_VALIDATE=1): the block table's
+// needed entries are valid block ids.  Synchronous (device-to-host copy).
+static pa_status validate_block_table(const pa_batch *b, int32_t num_blocks, hipStream_t s) {
+  if (b->num_seqs == 0) return PA_OK;
+  std::vector<int32_t> bt((size_t)b->num_seqs * b->bt_stride);
+  hipError_t e = hipMemcpyAsync(bt.data(), b->block_table, bt.size() * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "validate: block table read");
+  for (int32_t i = 0; i < b->num_seqs; ++i) {
+    const int64_t nb = ((int64_t)b->seq_lens_host[i] + kBlock - 1) / kBlock;
+    for (int64_t j = 0; j < nb; ++j) {
+      const int32_t blk = bt[(size_t)i * b->bt_stride + j];
+      if (blk < 0 || blk >= num_blocks)
+        return fail(PA_ERR_VALIDATION, "block_table[%d][%lld] = %d outside [0, %d)", i, (long long)j, blk, num_blocks);
+    }
+  }
+  return PA_OK;
+}
+
+// ------------------------------------------------------------------ plan ---
+// a3: classify each request's rows (MFMA extend for prefill chunks, split-K
+// token-parallel otherwise), pick the partition length, and lay out the
+// workspace.  Deterministic in the host mirrors, so the workspace query and
+// the call agree.
+
+struct Plan {
+  std::vector<DecodeItem> dec;
+  std::vector<MergeItem> merge;
+  std::vector<ExtendItem> ext;
+  int32_t n_slots = 0;
+  int32_t part_len = 0;
+  size_t off_dec = 0, off_merge = 0, off_ext = 0, off_ml = 0, off_o = 0, bytes = 0;
+};
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Smallest number of prefill rows for which a request goes to the MFMA
+// extend kernel (bf16 pools); shorter ones use the split-K kernel.
+static int extend_min_rows() {
+  const char *v = getenv("PA_EXTEND_MIN_ROWS");
+  return v ? atoi(v) : 16;
+}
+
+static bool extend_supported(const pa_kv_pool &p, pa_dtype q_dtype) {
+  (void)p;
+  (void)q_dtype;
+  return false;
+}
+
+static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dtype q_dtype,
+                       int causal, Plan &plan) {
+  const int32_t *q = b.query_start_loc_host, *L = b.seq_lens_host;
+  const int Hkv = p.num_kv_heads, g = Hq / Hkv;
+  const bool ext_ok = extend_supported(p, q_dtype) && env_flag("PA_DISABLE_EXTEND") == false;
+  const int ext_min = extend_min_rows();
+
+  // total key work of the split-K rows, to size partitions so that the whole
+  // launch has about 16 waves per compute unit
+  int64_t key_work = 0;
+  for (int32_t i = 0; i < b.num_seqs; ++i) {
+    const int32_t c = q[i + 1] - q[i];
+    if (c == 0 || (ext_ok && c >= ext_min)) continue;
+    for (int32_t t = 0; t < c; ++t) key_work += causal ? (L[i] - c + t + 1) : L[i];
+  }
+  const int64_t target_waves = 256 * 16;
+  int64_t part = (key_work * Hkv + target_waves - 1) / target_waves;
+  part = ((part + kKeysPerIter - 1) / kKeysPerIter) * kKeysPerIter;
+  part = std::max<int64_t>(part, 256);
+  if (const char *v = getenv("PA_PARTITION_KEYS")) part = std::max(64, atoi(v) / 64 * 64);
+  plan.part_len = (int32_t)part;
+
+  for (int32_t i = 0; i < b.num_seqs; ++i) {
+    const int32_t c = q[i + 1] - q[i];
+    if (c == 0) continue;
+    if (ext_ok && c >= ext_min) {
+      const int64_t cols = (int64_t)c * g;
+      for (int kvh = 0; kvh < Hkv; ++kvh)
+        for (int64_t c0 = 0; c0 < cols; c0 += kExtCols)
+          plan.ext.push_back(ExtendItem{i, kvh, q[i], c, L[i], (int32_t)c0, {0, 0}});
+      continue;
+    }
+    for (int32_t t = 0; t < c; ++t) {
+      const int32_t tok = q[i] + t;
+      const int32_t nvis = causal ? (L[i] - c + t + 1) : L[i];
+      const int32_t nparts = (int32_t)((nvis + part - 1) / part);
+      if (nparts <= 1) {
+        plan.dec.push_back(DecodeItem{tok, i, 0, nvis, -1, {0, 0, 0}});
+        continue;
+      }
+      plan.merge.push_back(MergeItem{tok, plan.n_slots, nparts, 0});
+      for (int32_t r = 0; r < nparts; ++r) {
+        const int32_t b0 = (int32_t)(r * part), b1 = (int32_t)std::min<int64_t>(nvis, (r + 1) * part);
+        plan.dec.push_back(DecodeItem{tok, i, b0, b1, plan.n_slots + r, {0, 0, 0}});
+      }
+      plan.n_slots += nparts;
+    }
+  }
+  // longest extend tiles first (their key range grows with the column offset)
+  std::stable_sort(plan.ext.begin(), plan.ext.end(), [g](const ExtendItem &x, const ExtendItem &y) {
+    const int64_t kx = (int64_t)x.L - x.c + std::min<int64_t>(x.c, (x.col0 + kExtCols + g - 1) / g);
+    const int64_t ky = (int64_t)y.L - y.c + std::min<int64_t>(y.c, (y.col0 + kExtCols + g - 1) / g);
+    return kx > ky;
+  });
+
+  size_t off = 0;
+  plan.off_dec = off;
+  off = align256(off + plan.dec.size() * sizeof(DecodeItem));
+  plan.off_merge = off;
+  off = align256(off + plan.merge.size() * sizeof(MergeItem));
+  plan.off_ext = off;
+  off = align256(off + plan.ext.size() * sizeof(ExtendItem));
+  plan.off_ml = off;
+  off = align256(off + (size_t)plan.n_slots * Hq * 2 * sizeof(float));
+  plan.off_o = off;
+  off = align256(off + (size_t)plan.n_slots * Hq * p.head_dim * sizeof(float));
+  plan.bytes = std::max<size_t>(off, 256);
+}
+
+static pa_status check_attention_args(const pa_kv_pool *pool, const pa_batch *batch,
+                                      pa_dtype q_dtype, int32_t Hq, bool need_ptrs) {
+  pa_status st = check_pool(pool, need_ptrs);
+  if (st != PA_OK) return st;
+  if ((st = check_batch(batch, need_ptrs)) != PA_OK) return st;
+  if (Hq <= 0 || Hq % pool->num_kv_heads)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads %d not a positive multiple of num_kv_heads %d", Hq, pool->num_kv_heads);
+  if (Hq / pool->num_kv_heads > 16)
+    return fail(PA_ERR_UNSUPPORTED, "more than 16 q heads per kv head");
+  if (q_dtype != PA_F32 && q_dtype != PA_BF16) return fail(PA_ERR_INVALID_ARG, "q_dtype must be F32 or BF16");
+  if ((q_dtype == PA_F32) != (pool->kv_dtype == PA_F32))
+    return fail(PA_ERR_UNSUPPORTED, "q_dtype F32 pairs with an F32 pool, BF16 with BF16/FP8 pools");
+  return PA_OK;
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+// ================================================================== C ABI ===
+
+extern "C" {
+
+pa_status pa_prepare_metadata(int32_t num_seqs, const int32_t *num_computed,
+                              const int32_t *num_scheduled, int32_t *query_start_loc,
+                              int32_t *seq_lens) {
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "negative num_seqs");
+  if (!query_start_loc || (num_seqs > 0 && (!num_computed || !num_scheduled || !seq_lens)))
+    return fail(PA_ERR_INVALID_ARG, "NULL pointer");
+  int64_t acc = 0;
+  query_start_loc[0] = 0;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    if (num_computed[i] < 0 || num_scheduled[i] < 0)
+      return fail(PA_ERR_INVALID_ARG, "negative count at request %d", i);
+    acc += num_scheduled[i];
+    const int64_t len = (int64_t)num_computed[i] + num_scheduled[i];
+    if (acc > INT32_MAX || len > INT32_MAX) return fail(PA_ERR_INVALID_ARG, "counts overflow int32");
+    query_start_loc[i + 1] = (int32_t)acc;
+    seq_lens[i] = (int32_t)len;
+  }
+  return PA_OK;
+}
+
+pa_status pa_slot_mapping(const pa_batch *batch, int32_t block_size, int64_t *slot_mapping,
+                          pa_stream_t stream) {
+  pa_status st = check_batch(batch, true);
+  if (st != PA_OK) return st;
+  if (block_size != kBlock) return fail(PA_ERR_UNSUPPORTED, "block_size %d (only 16)", block_size);
+  if (batch->num_tokens > 0 && !slot_mapping) return fail(PA_ERR_INVALID_ARG, "slot_mapping is NULL");
+  int max_c = 0;
+  for (int32_t i = 0; i < batch->num_seqs; ++i)
+    max_c = std::max(max_c, batch->query_start_loc_host[i + 1] - batch->query_start_loc_host[i]);
+  hipError_t e = launch_slot_mapping(*batch, slot_mapping, max_c, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : hip_fail(e, "k_slot_mapping launch");
+}
+
+pa_status pa_write_kv(const pa_kv_pool *pool, const void *key, const void *value, pa_dtype in_dtype,
+                      const int64_t *slot_mapping, int32_t num_tokens, pa_stream_t stream) {
+  pa_status st = check_pool(pool, true);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "negative num_tokens");
+  if (num_tokens > 0 && (!key || !value || !slot_mapping)) return fail(PA_ERR_INVALID_ARG, "NULL key/value/slot_mapping");
+  if (in_dtype != PA_F32 && in_dtype != PA_BF16) return fail(PA_ERR_INVALID_ARG, "in_dtype must be F32 or BF16");
+  if (pool->kv_dtype != PA_FP8_E4M3 && pool->kv_dtype != in_dtype)
+    return fail(PA_ERR_UNSUPPORTED, "in_dtype must match an F32/BF16 pool");
+  if (env_flag("PA_VALIDATE") && num_tokens > 0) {
+    std::vector<int64_t> sl(num_tokens);
+    hipError_t e = hipMemcpyAsync(sl.data(), slot_mapping, sl.size() * 8, hipMemcpyDeviceToHost, (hipStream_t)stream);
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "validate: slot read");
+    const int64_t cap = (int64_t)pool->num_blocks * pool->block_size;
+    for (int32_t n = 0; n < num_tokens; ++n)
+      if (sl[n] >= cap) return fail(PA_ERR_VALIDATION, "slot_mapping[%d] = %lld >= capacity %lld", n, (long long)sl[n], (long long)cap);
+  }
+  hipError_t e = launch_write_kv(*pool, key, value, in_dtype, slot_mapping, num_tokens, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : hip_fail(e, "k_write_kv launch");
+}
+
+size_t pa_attention_workspace_bytes(const pa_kv_pool *pool, const pa_batch *batch, int32_t num_q_heads) {
+  // the dtype only selects kernels; BF16 gives the largest (extend-capable) plan shape
+  const pa_dtype qd = pool && pool->kv_dtype == PA_F32 ? PA_F32 : PA_BF16;
+  if (check_attention_args(pool, batch, qd, num_q_heads, false) != PA_OK) return 0;
+  Plan plan;
+  build_plan(*pool, *batch, num_q_heads, qd, 1, plan);
+  Plan plan_nc;
+  build_plan(*pool, *batch, num_q_heads, qd, 0, plan_nc);
+  return std::max(plan.bytes, plan_nc.bytes);
+}
+
+pa_status pa_attention(const pa_kv_pool *pool, const pa_batch *batch, const void *query,
+                       pa_dtype q_dtype, int32_t num_q_heads, float softmax_scale, int32_t causal,
+                       void *output, void *workspace, size_t workspace_bytes, pa_stream_t stream) {
+  pa_status st = check_attention_args(pool, batch, q_dtype, num_q_heads, true);
+  if (st != PA_OK) return st;
+  if (batch->num_tokens > 0 && (!query || !output)) return fail(PA_ERR_INVALID_ARG, "NULL query/output");
+  if (!std::isfinite(softmax_scale)) return fail(PA_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (batch->num_tokens == 0) return PA_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (env_flag("PA_VALIDATE") && (st = validate_block_table(batch, pool->num_blocks, s)) != PA_OK) return st;
+
+  Plan plan;
+  build_plan(*pool, *batch, num_q_heads, q_dtype, causal ? 1 : 0, plan);
+  if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL");
+  if (((uintptr_t)workspace & 255) != 0) return fail(PA_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  if (workspace_bytes < plan.bytes)
+    return fail(PA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, plan.bytes);
+
+  // upload the work lists (one contiguous copy)
+  const size_t plan_bytes = plan.off_ml;
+  if (plan_bytes) {
+    std::vector<char> host(plan_bytes, 0);
+    if (!plan.dec.empty()) memcpy(host.data() + plan.off_dec, plan.dec.data(), plan.dec.size() * sizeof(DecodeItem));
+    if (!plan.merge.empty()) memcpy(host.data() + plan.off_merge, plan.merge.data(), plan.merge.size() * sizeof(MergeItem));
+    if (!plan.ext.empty()) memcpy(host.data() + plan.off_ext, plan.ext.data(), plan.ext.size() * sizeof(ExtendItem));
+    if ((st = upload(workspace, host.data(), plan_bytes, s)) != PA_OK) return st;
+  }
+  char *ws = (char *)workspace;
+  const int g_total = num_q_heads / pool->num_kv_heads;
+  const float log2e = 1.4426950408889634f;
+  const float kscale = pool->kv_dtype == PA_FP8_E4M3 ? pool->k_scale : 1.0f;
+  const float vscale = pool->kv_dtype == PA_FP8_E4M3 ? pool->v_scale : 1.0f;
+
+  hipError_t e = hipSuccess;
+  if (!plan.dec.empty()) {
+    DecodeArgs a{};
+    a.q = query;
+    a.out = output;
+    a.k_cache = pool->k_cache;
+    a.v_cache = pool->v_cache;
+    a.block_table = batch->block_table;
+    a.items = (const DecodeItem *)(ws + plan.off_dec);
+    a.part_ml = (float *)(ws + plan.off_ml);
+    a.part_o = (float *)(ws + plan.off_o);
+    a.n_items = (int32_t)plan.dec.size();
+    a.bt_stride = batch->bt_stride;
+    a.num_blocks = pool->num_blocks;
+    a.num_kv_heads = pool->num_kv_heads;
+    a.num_q_heads = num_q_heads;
+    a.g = g_total;
+    a.h0 = 0;
+    a.g_total = g_total;
+    a.scale_log2 = softmax_scale * log2e * kscale;
+    a.v_scale = vscale;
+    const int g_tmpl = g_total <= 1 ? 1 : g_total <= 2 ? 2 : g_total <= 4 ? 4 : g_total <= 8 ? 8 : 16;
+    e = launch_decode(*pool, q_dtype, a, g_tmpl, s);
+    if (e != hipSuccess) return hip_fail(e, "k_decode launch");
+  }
+  if (!plan.merge.empty()) {
+    MergeArgs m{};
+    m.out = output;
+    m.part_ml = (const float *)(ws + plan.off_ml);
+    m.part_o = (const float *)(ws + plan.off_o);
+    m.items = (const MergeItem *)(ws + plan.off_merge);
+    m.n_items = (int32_t)plan.merge.size();
+    m.num_q_heads = num_q_heads;
+    e = launch_merge(q_dtype, pool->head_dim, m, s);
+    if (e != hipSuccess) return hip_fail(e, "k_merge launch");
+  }
+  if (!plan.ext.empty()) {
+    ExtendArgs x{};
+    x.q = query;
+    x.out = output;
+    x.k_cache = pool->k_cache;
+    x.v_cache = pool->v_cache;
+    x.block_table = batch->block_table;
+    x.items = (const ExtendItem *)(ws + plan.off_ext);
+    x.n_items = (int32_t)plan.ext.size();
+    x.bt_stride = batch->bt_stride;
+    x.num_blocks = pool->num_blocks;
+    x.num_kv_heads = pool->num_kv_heads;
+    x.num_q_heads = num_q_heads;
+    x.g = g_total;
+    x.causal = causal ? 1 : 0;
+    x.scale_log2 = softmax_scale * log2e * kscale;
+    x.k_scale = kscale;
+    x.v_scale = vscale;
+    e = launch_extend(*pool, x, s);
+    if (e != hipSuccess) return hip_fail(e, "k_extend launch");
+  }
+  return PA_OK;
+}
+
+size_t pa_kv_cache_bytes(const pa_kv_pool *pool) {
+  if (!pool || pool->num_blocks <= 0 || pool->block_size <= 0 || pool->num_kv_heads <= 0 || pool->head_dim <= 0)
+    return 0;
+  return (size_t)pool->num_blocks * pool->block_size * pool->num_kv_heads * pool->head_dim *
+         elem_bytes(pool->kv_dtype);
+}
+
+int64_t pa_kv_elem_offset(const pa_kv_pool *pool, int32_t which, int64_t block, int32_t offset,
+                          int32_t head, int32_t dim) {
+  if (!pool || block < 0 || block >= pool->num_blocks || offset < 0 || offset >= pool->block_size ||
+      head < 0 || head >= pool->num_kv_heads || dim < 0 || dim >= pool->head_dim || (which != 0 && which != 1))
+    return -1;
+  const int64_t S = pool->block_size, D = pool->head_dim;
+  const int64_t tile = (block * pool->num_kv_heads + head) * S * D;
+  if (which == 1) return tile + (int64_t)dim * S + offset;  // [dim][slot]
+  const int64_t E = 16 / elem_bytes(pool->kv_dtype);
+  return tile + ((dim / E) * S + offset) * E + dim % E;     // [chunk][slot][E]
+}
+
+const char *pa_status_string(pa_status status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
+    case PA_ERR_VALIDATION: return "PA_ERR_VALIDATION";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+  }
+  return "PA_ERR_UNKNOWN";
+}
+
+const char *pa_last_error(void) { return g_last_error.c_str(); }
+
+pa_status pa_profile_enable(int32_t enable) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  prof_reset_locked();
+  g_prof_on = enable != 0;
+  return PA_OK;
+}
+
+pa_status pa_profile_read(const char *kernel, int32_t *launches, double *total_ms) {
+  if (!kernel || !launches || !total_ms) return fail(PA_ERR_INVALID_ARG, "NULL argument");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  int32_t n = 0;
+  double ms = 0;
+  for (auto &r : g_prof) {
+    if (strcmp(r.name, kernel) != 0) continue;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e != hipSuccess) return hip_fail(e, "profile wait");
+    float t = 0;
+    if ((e = hipEventElapsedTime(&t, r.start, r.stop)) != hipSuccess) return hip_fail(e, "profile time");
+    ms += t;
+    ++n;
+  }
+  *launches = n;
+  *total_ms = ms;
+  return PA_OK;
+}
+
+}  // extern "C"

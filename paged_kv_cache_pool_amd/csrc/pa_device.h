@@ -1,0 +1,92 @@
+// Device helpers for the gfx950 kernels of libpa.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+enum KvKind { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
+
+template <int KV> struct KvTraits;
+template <> struct KvTraits<KV_F32> { static constexpr int bytes = 4; };
+template <> struct KvTraits<KV_BF16> { static constexpr int bytes = 2; };
+template <> struct KvTraits<KV_FP8> { static constexpr int bytes = 1; };
+
+__device__ __forceinline__ float bf16_lo(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  __bf16 b = (__bf16)x;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// acc + a.lo * b.lo + a.hi * b.hi with bf16 pairs (v_dot2_f32_bf16; products
+// exact, fp32 accumulation).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
+// Two OCP E4M3FN codes (bytes 2*hi_word, 2*hi_word+1 of w) -> two exact floats.
+__device__ __forceinline__ f32x2_t fp8x2_to_f32(uint32_t w, bool hi_word) {
+  return hi_word ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true)
+                 : __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+}
+
+// OCP E4M3FN encoder (software, integer arithmetic), written from the format:
+// 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, exponent field 0
+// subnormal (m * 2^-9), largest finite magnitude 448 (code 0x7E), code 0x7F
+// (and 0xFF) NaN, no infinity.  Rounding: nearest, ties to even; magnitudes
+// of 448 or more saturate to 448; NaN encodes as 0x7F.
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;                    // NaN
+  if (a >= 0x43e00000u) return sign | 0x7eu;            // >= 448 (incl. inf)
+  if (a < 0x3c800000u) {                                // below 2^-6: subnormal codes
+    // value / 2^-9 rounded to the nearest integer, ties to even (0..8; 8 is
+    // the smallest normal, whose code is also 8)
+    const float q = __builtin_rintf(__uint_as_float(a) * 512.0f);
+    return sign | (uint32_t)q;
+  }
+  const uint32_t exp = (a >> 23) - 127 + 7;             // 1..15
+  const uint32_t man = a & 0x7fffffu;
+  uint32_t code = (exp << 3) | (man >> 20);
+  const uint32_t rem = man & 0xfffffu;
+  // round half to even on the 20 dropped bits; a carry into the exponent is
+  // the correct next code
+  code += (rem > 0x80000u || (rem == 0x80000u && (code & 1u))) ? 1u : 0u;
+  return sign | code;
+}
+
+// Wave-wide reductions (64 lanes).
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+__device__ __forceinline__ int readlane(int x, int lane) {
+  return __builtin_amdgcn_readlane(x, lane);
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+}  // namespace pa

@@ -1,0 +1,118 @@
+// Internal declarations shared by the translation units of libpa.so.
+// Not part of the ABI (include/pa.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "../../include/pa.h"
+
+namespace pa {
+
+constexpr int kBlock = 16;           // tokens per pool block (the only size supported)
+constexpr int kKeysPerIter = 64;     // keys one wave scores per iteration (4 blocks)
+constexpr int kWavesPerGroup = 4;    // waves per workgroup in the split-K kernels
+
+// One unit of token-parallel (split-K) attention: keys [kv_begin, kv_end) of
+// token `token` (row of the flat stream) belonging to request `req`.  When
+// `part` < 0 the range is the token's whole visible range and the kernel
+// writes the final output; otherwise it writes partial (m, l, o) at slot `part`.
+struct DecodeItem {
+  int32_t token;
+  int32_t req;
+  int32_t kv_begin;
+  int32_t kv_end;
+  int32_t part;
+  int32_t pad[3];
+};
+
+// Merge of the partials of one token: slots [first, first + count).
+struct MergeItem {
+  int32_t token;
+  int32_t first;
+  int32_t count;
+  int32_t pad;
+};
+
+// One workgroup of the MFMA extend kernel: columns [col0, col0 + kExtCols) of
+// request `req`, where column k is (token t = k / g, q head hg = k % g) of
+// kv head `kvh`; the request's new tokens start at stream row `tok0`, there
+// are `c` of them and the request holds `L` tokens in total.
+struct ExtendItem {
+  int32_t req;
+  int32_t kvh;
+  int32_t tok0;
+  int32_t c;
+  int32_t L;
+  int32_t col0;
+  int32_t pad[2];
+};
+
+struct DecodeArgs {
+  const void *q;          // [T][Hq][D]
+  void *out;              // [T][Hq][D]
+  const void *k_cache;
+  const void *v_cache;
+  const int32_t *block_table;
+  const DecodeItem *items;
+  float *part_ml;         // [slots][Hq][2]  (m in log2 units, l)
+  float *part_o;          // [slots][Hq][D]
+  int32_t n_items;
+  int32_t bt_stride;
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t num_q_heads;
+  int32_t g;              // q heads per kv head handled by this launch
+  int32_t h0;             // first q head (within each kv head's group) of this launch
+  int32_t g_total;        // num_q_heads / num_kv_heads
+  float scale_log2;       // softmax_scale * log2(e) (* k_scale for fp8 pools)
+  float v_scale;          // 1 for non-fp8 pools
+};
+
+struct MergeArgs {
+  void *out;
+  const float *part_ml;
+  const float *part_o;
+  const MergeItem *items;
+  int32_t n_items;
+  int32_t num_q_heads;
+};
+
+struct ExtendArgs {
+  const void *q;
+  void *out;
+  const void *k_cache;
+  const void *v_cache;
+  const int32_t *block_table;
+  const ExtendItem *items;
+  int32_t n_items;
+  int32_t bt_stride;
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t num_q_heads;
+  int32_t g;
+  int32_t causal;
+  float scale_log2;
+  float k_scale;
+  float v_scale;
+};
+
+constexpr int kExtCols = 128;        // columns per extend workgroup (4 waves x 32)
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_slot_mapping(const pa_batch &b, int64_t *slots, int max_c, hipStream_t s);
+hipError_t launch_write_kv(const pa_kv_pool &p, const void *key, const void *value,
+                           pa_dtype in_dtype, const int64_t *slots, int32_t num_tokens,
+                           hipStream_t s);
+hipError_t launch_decode(const pa_kv_pool &p, pa_dtype q_dtype, const DecodeArgs &a,
+                         int g_tmpl, hipStream_t s);
+hipError_t launch_merge(pa_dtype q_dtype, int head_dim, const MergeArgs &a, hipStream_t s);
+hipError_t launch_extend(const pa_kv_pool &p, const ExtendArgs &a, hipStream_t s);
+
+// Kernel timing hooks (no-ops unless profiling is enabled).
+void prof_begin(const char *name, hipStream_t s);
+void prof_end(hipStream_t s);
+
+}  // namespace pa

@@ -1,0 +1,176 @@
+"""Boundary tests that need no GPU: libpa.so loads and exports every symbol
+include/pa.h declares; the host-side calls (metadata, layout queries,
+workspace size) behave as documented; invalid arguments are rejected with the
+documented status before any work is enqueued."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from paged_kv_cache_pool_amd import binding
+    return binding
+
+
+def _declared():
+    src = open(HEADER, encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(B):
+    names = _declared()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(B.lib, n), n
+    assert sorted(B.EXPORTS) == names
+
+
+def test_status_strings(B):
+    for code, name in B.STATUS.items():
+        assert B.status_string(code) == name
+
+
+def test_prepare_metadata_page_examples(B):
+    qsl, sl = B.prepare_metadata([0, 0, 0], [1, 5, 1])
+    assert qsl.tolist() == [0, 1, 6, 7]
+    qsl, sl = B.prepare_metadata([1024, 512, 600], [1, 256, 3])
+    assert qsl.tolist() == [0, 1, 257, 260] and sl.tolist() == [1025, 768, 603]
+
+
+def test_prepare_metadata_matches_oracle(B, orc):
+    rng = np.random.default_rng(0)
+    for _ in range(20):
+        n = int(rng.integers(0, 30))
+        nc = rng.integers(0, 10000, n).astype(np.int32)
+        ns = rng.integers(0, 600, n).astype(np.int32)
+        qsl, sl = B.prepare_metadata(nc, ns)
+        assert (qsl == orc.query_start_loc(ns)).all()
+        assert (sl == orc.seq_lens(nc, ns)).all()
+    with pytest.raises(B.PaError) as e:
+        B.prepare_metadata([1, -1], [1, 1])
+    assert e.value.status == 1
+
+
+@pytest.mark.parametrize("kv", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_layout_offsets_match_logical_view(B, kv, D):
+    """pa_kv_elem_offset (the layout's definition) and the binding's logical view
+    agree, and the layout is a bijection onto the cache."""
+    nb, S, H = 3, 16, 2
+    spec = B.KVPool.spec(nb, S, H, D, kv)
+    nbytes = B.lib.pa_kv_cache_bytes(C.byref(spec))
+    itemsize = {"f32": 4, "bf16": 2, "fp8": 1}[kv]
+    n = nbytes // itemsize
+    assert n == nb * S * H * D
+    seen = np.zeros(n, dtype=bool)
+    for which in (0, 1):
+        seen[:] = False
+        for blk in range(nb):
+            for off in range(S):
+                for h in range(H):
+                    for d in range(0, D, 3):
+                        o = B.lib.pa_kv_elem_offset(C.byref(spec), which, blk, off, h, d)
+                        assert 0 <= o < n and not seen[o]
+                        seen[o] = True
+    # the logical view built by the binding reads element offsets consistently
+    import torch
+
+    class FakePool(B.KVPool):
+        pass
+    raw = np.arange(n, dtype=np.int64)
+    pool = FakePool(torch.from_numpy(raw.astype(np.float32).view(np.uint8) if kv == "f32" else np.zeros(1, np.uint8)),
+                    None, nb, S, H, D, kv)
+    if kv == "f32":
+        lk = pool.logical("k")
+        for blk, off, h, d in [(0, 0, 0, 0), (2, 15, 1, D - 1), (1, 7, 0, 33 % D)]:
+            assert lk[blk, off, h, d] == B.lib.pa_kv_elem_offset(C.byref(spec), 0, blk, off, h, d)
+    assert B.lib.pa_kv_elem_offset(C.byref(spec), 0, nb, 0, 0, 0) == -1
+    assert B.lib.pa_kv_elem_offset(C.byref(spec), 2, 0, 0, 0, 0) == -1
+
+
+def _pool(B, kv="bf16", D=128, S=16, H=8, nb=100):
+    p = B.KVPool.spec(nb, S, H, D, kv, 0.5, 0.5)
+    p.k_cache = 0x1000
+    p.v_cache = 0x2000
+    return p
+
+
+def _batch(B, qsl, sl, bt_stride=8):
+    qsl = np.asarray(qsl, np.int32)
+    sl = np.asarray(sl, np.int32)
+    b = B.PaBatch(sl.size, int(qsl[-1]), 0x3000, 0x4000, 0x5000, bt_stride,
+                  qsl.ctypes.data, sl.ctypes.data)
+    return b, (qsl, sl)
+
+
+def test_workspace_bytes(B):
+    p = _pool(B)
+    b, keep = _batch(B, [0, 1, 2, 40], [100, 3000, 64], bt_stride=200)
+    n = B.lib.pa_attention_workspace_bytes(C.byref(p), C.byref(b), 32)
+    assert n > 0 and n % 256 == 0
+    bad = B.PaBatch(b.num_seqs, b.num_tokens, 0, 0, 0, 200, 0, 0)
+    assert B.lib.pa_attention_workspace_bytes(C.byref(p), C.byref(bad), 32) == 0
+
+
+def _att(B, p, b, q_dtype=1, hq=32, ws=1 << 20, wsptr=0x10000, out=0x7000, q=0x6000, scale=0.088):
+    return B.lib.pa_attention(C.byref(p), C.byref(b), q, q_dtype, hq, scale, 1, out, wsptr, ws, None)
+
+
+def test_attention_rejects_bad_arguments(B):
+    p = _pool(B)
+    b, keep = _batch(B, [0, 1, 2], [10, 20])
+    assert _att(B, p, b, hq=12) == 1                       # Hq not a multiple of Hkv
+    assert _att(B, p, b, hq=8 * 17) == 2                   # g > 16
+    assert _att(B, p, b, q_dtype=0) == 2                   # f32 q with bf16 pool
+    assert _att(B, p, b, q_dtype=7) == 1
+    assert _att(B, p, b, scale=float("inf")) == 1
+    assert _att(B, p, b, wsptr=0) == 3                     # no workspace
+    assert _att(B, p, b, wsptr=0x10010) == 3               # misaligned workspace
+    assert _att(B, p, b, ws=16) == 3                       # too small
+    assert _att(B, p, b, q=0) == 1
+    b2, keep2 = _batch(B, [0, 2, 1], [10, 20])             # decreasing qsl
+    assert _att(B, p, b2) == 1
+    b3, keep3 = _batch(B, [1, 2, 3], [10, 20])             # qsl[0] != 0
+    assert _att(B, p, b3) == 1
+    b4, keep4 = _batch(B, [0, 5, 6], [4, 20])              # seq_len < new tokens
+    assert _att(B, p, b4) == 1
+    b5, keep5 = _batch(B, [0, 1, 2], [10, 20 * 16], bt_stride=8)  # too few block-table columns
+    assert _att(B, p, b5) == 1
+    p2 = _pool(B, S=32)
+    assert _att(B, p2, b) == 2                             # block size
+    p3 = _pool(B, D=96)
+    assert _att(B, p3, b) == 2                             # head dim
+    p4 = _pool(B, kv="fp8")
+    p4.k_scale = 0.0
+    assert _att(B, p4, b) == 1                             # fp8 scale
+    msg = B.lib.pa_last_error().decode()
+    assert "scale" in msg
+
+
+def test_write_and_slots_reject_bad_arguments(B):
+    p = _pool(B)
+    assert B.lib.pa_write_kv(C.byref(p), 0x1, 0x2, 1, 0x3, -1, None) == 1
+    assert B.lib.pa_write_kv(C.byref(p), None, 0x2, 1, 0x3, 4, None) == 1
+    assert B.lib.pa_write_kv(C.byref(p), 0x1, 0x2, 0, 0x3, 4, None) == 2   # f32 into bf16 pool
+    assert B.lib.pa_write_kv(C.byref(p), 0x1, 0x2, 2, 0x3, 4, None) == 1   # fp8 input
+    p.k_cache = 0
+    assert B.lib.pa_write_kv(C.byref(p), 0x1, 0x2, 1, 0x3, 4, None) == 1
+    b, keep = _batch(B, [0, 1, 2], [10, 20])
+    assert B.lib.pa_slot_mapping(C.byref(b), 32, 0x9000, None) == 2
+    assert B.lib.pa_slot_mapping(C.byref(b), 16, None, None) == 1
+    assert B.lib.pa_slot_mapping(None, 16, 0x9000, None) == 1
+
+
+def test_empty_calls_are_no_ops(B):
+    p = _pool(B)
+    assert B.lib.pa_write_kv(C.byref(p), None, None, 1, None, 0, None) == 0
+    b, keep = _batch(B, [0], [])
+    assert _att(B, p, b) == 0

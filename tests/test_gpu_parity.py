@@ -1,0 +1,285 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs.
+
+* slot derivation and the KV write: bit-exact (the pool is compared through
+  logical (block, offset, head, dim) indexing; unwritten slots must still
+  hold their canaries);
+* attention: max |O_gpu - O_oracle| <= 1e-5 for the fp32 workload and
+  <= 2e-2 for bf16 / fp8 pools (fp32 accumulation, bf16 output);
+* full-size workloads are checked on sampled query rows, which the oracle
+  computes one by one.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from paged_kv_cache_pool_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {W.F32: 1e-5, W.BF16: 2e-2, W.FP8: 2e-2}
+
+
+def say(*a):
+    print("[gpu-parity]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def R():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from paged_kv_cache_pool_amd import runner
+    return runner
+
+
+def _tol(w):
+    return TOL[w.kv_dtype]
+
+
+def _oracle_pool(w):
+    return O.build_pool(w)
+
+
+def _compare_pool(w, gpu_pool, orc_pool, blocks=None):
+    for which in ("k", "v"):
+        g = gpu_pool.logical(which)
+        o = orc_pool.k if which == "k" else orc_pool.v
+        if blocks is not None:
+            g, o = g[blocks], o[blocks]
+        gv = g.view(np.uint32) if g.dtype == np.float32 else g
+        ov = o.view(np.uint32) if o.dtype == np.float32 else o
+        bad = np.argwhere(gv != ov)
+        assert bad.size == 0, f"{which} pool differs at {bad[:5].tolist()} (of {len(bad)})"
+
+
+def _sample_tokens(w, n, seed=0):
+    rng = np.random.default_rng(seed)
+    T = w.num_tokens
+    if T <= n:
+        return np.arange(T, dtype=np.int32)
+    # always include the first and last rows of every request with > 1 row
+    qsl = O.query_start_loc(w.num_scheduled)
+    must = set()
+    for i in range(w.num_seqs):
+        if w.num_scheduled[i] > 1:
+            must |= {int(qsl[i]), int(qsl[i + 1]) - 1}
+    rest = rng.choice(T, size=max(0, n - len(must)), replace=False).tolist()
+    return np.array(sorted(must | set(rest)), dtype=np.int32)
+
+
+def _check_attention(w, step, tokens=None, tol=None):
+    tol = _tol(w) if tol is None else tol
+    ref = O.run_step(w, tokens=tokens).out
+    got = step.out_f64()
+    if tokens is not None:
+        got = got[tokens]
+    err = np.abs(got - ref)
+    say(w.name, "max_abs_err", float(err.max()), "mean", float(err.mean()), "max|O|", float(np.abs(ref).max()))
+    assert np.isfinite(got).all()
+    assert err.max() <= tol, (float(err.max()), np.unravel_index(err.argmax(), err.shape))
+
+
+# ------------------------------------------------------------ slots / write --
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 5])
+def test_slots_and_write_bit_exact(R, cfg):
+    say("slots+write config", cfg)
+    w = W.make(cfg)
+    step = R.GpuStep(w)
+    step.run()
+    torch.cuda.synchronize()
+    qsl = O.query_start_loc(w.num_scheduled)
+    sl = O.seq_lens(w.num_computed, w.num_scheduled)
+    want = O.slot_mapping(qsl, sl, w.block_table, w.block_size)
+    assert (step.slots.cpu().numpy() == want).all()
+    orc = _oracle_pool(w)
+    O.write_kv(orc, w.key, w.value, w.io_dtype, want)
+    used = np.unique(w.block_table[w.block_table >= 0])
+    rng = np.random.default_rng(cfg)
+    unused = np.setdiff1d(np.arange(w.num_blocks), used)
+    blocks = np.concatenate([used, rng.choice(unused, size=min(64, unused.size), replace=False)]) \
+        if unused.size else used
+    _compare_pool(w, step.pool, orc, np.sort(blocks))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_write_random_small_bit_exact(R, seed):
+    kv = [W.F32, W.BF16, W.FP8][seed % 3]
+    io = W.F32 if kv == W.F32 else W.BF16
+    D = [64, 128][(seed // 3) % 2]
+    say("write random", seed, kv, D)
+    w = W.random_small(seed, max_seqs=5, max_len=150, num_q_heads=4, num_kv_heads=2, head_dim=D,
+                       kv_dtype=kv, io_dtype=io, spare_blocks=5)
+    if kv == W.FP8:
+        w = W.build(w.name, seed, num_q_heads=4, num_kv_heads=2, head_dim=D, block_size=16,
+                    num_blocks=w.num_blocks, kv_dtype=W.FP8, io_dtype=W.BF16,
+                    num_computed=w.num_computed, num_scheduled=w.num_scheduled)
+    step = R.GpuStep(w)
+    step.run()
+    torch.cuda.synchronize()
+    orc = O.run_step(w).pool
+    _compare_pool(w, step.pool, orc)
+
+
+def test_write_negative_and_out_of_range_slots_skipped(R):
+    from paged_kv_cache_pool_amd import binding as B
+    say("write negative slots")
+    pool = B.KVPool.allocate(4, 16, 2, 64, "bf16", fill_byte=0xFF)
+    key = torch.arange(5 * 2 * 64, dtype=torch.float32, device="cuda").reshape(5, 2, 64).bfloat16()
+    val = -key
+    slots = torch.tensor([3, -1, 63, 64, 1 << 40], dtype=torch.int64, device="cuda")
+    B.write_kv(pool, key, val, slots)
+    torch.cuda.synchronize()
+    lk = pool.logical("k")
+    kb = key.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert (lk[0, 3] == kb[0]).all() and (lk[3, 15] == kb[2]).all()
+    mask = np.ones((4, 16), bool)
+    mask[0, 3] = mask[3, 15] = False
+    assert (lk[mask] == 0xFFFF).all()
+
+
+def test_fp8_encode_every_bf16(R):
+    """Every bf16 bit pattern through pa_write_kv into an fp8 pool (scale 1 and
+    a non-power-of-two scale) gives the oracle's code."""
+    from paged_kv_cache_pool_amd import binding as B
+    for scale in (1.0, 0.0137):
+        say("fp8 exhaustive scale", scale)
+        bits = np.arange(1 << 16, dtype=np.uint16)
+        T = (1 << 16) // 128
+        key = torch.from_numpy(bits.view(np.int16).reshape(T, 1, 128)).cuda().view(torch.bfloat16)
+        pool = B.KVPool.allocate(T // 16, 16, 1, 128, "fp8", scale, scale, fill_byte=0)
+        slots = torch.arange(T, dtype=torch.int64, device="cuda")
+        B.write_kv(pool, key, key, slots)
+        torch.cuda.synchronize()
+        got_k = pool.logical("k").reshape(-1)
+        got_v = pool.logical("v").reshape(-1)
+        x = (bits.astype(np.uint32) << 16).view(np.float32)
+        y = (x / np.float32(scale)).astype(np.float32)
+        want = O.e4m3_encode(y)
+        assert (got_k == want).all(), np.argwhere(got_k != want)[:5]
+        assert (got_v == want).all()
+
+
+# ------------------------------------------------------------- attention --
+
+def test_attention_tiny_f32_config(R):
+    say("attention config 1")
+    w = W.make(1)
+    step = R.GpuStep(w)
+    step.run()
+    torch.cuda.synchronize()
+    _check_attention(w, step)
+
+
+@pytest.mark.parametrize("cfg,n", [(2, 24), (3, 40), (5, 24)])
+def test_attention_full_size_sampled(R, cfg, n):
+    say("attention config", cfg)
+    w = W.make(cfg)
+    step = R.GpuStep(w)
+    step.run()
+    torch.cuda.synchronize()
+    _check_attention(w, step, tokens=_sample_tokens(w, n, seed=cfg))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_attention_random_small(R, seed):
+    kv = [W.F32, W.BF16, W.FP8][seed % 3]
+    io = W.F32 if kv == W.F32 else W.BF16
+    g = [1, 2, 4, 8][(seed // 3) % 4]
+    D = [64, 128][(seed // 12) % 2]
+    say("attention random", seed, kv, "g", g, "D", D)
+    w = W.random_small(seed, max_seqs=5, max_len=300, num_q_heads=2 * g, num_kv_heads=2,
+                       head_dim=D, kv_dtype=kv, io_dtype=io, spare_blocks=4)
+    if kv == W.FP8:
+        w = W.build(w.name, seed, num_q_heads=2 * g, num_kv_heads=2, head_dim=D, block_size=16,
+                    num_blocks=w.num_blocks, kv_dtype=W.FP8, io_dtype=W.BF16,
+                    num_computed=w.num_computed, num_scheduled=w.num_scheduled)
+    step = R.GpuStep(w)
+    step.run()
+    torch.cuda.synchronize()
+    _check_attention(w, step)
+
+
+def test_attention_long_and_split(R, monkeypatch):
+    """Several partitions per row (forced short partitions) and long rows."""
+    monkeypatch.setenv("PA_PARTITION_KEYS", "64")
+    say("attention forced 64-key partitions")
+    w = W.llama8b_decode(seed=3, num_seqs=6, lo=1, hi=700, num_blocks=400)
+    step = R.GpuStep(w)
+    step.run()
+    torch.cuda.synchronize()
+    _check_attention(w, step)
+
+
+def test_attention_zero_token_requests_and_noncausal(R):
+    say("attention c=0 requests + non-causal")
+    w = W.build("zeros", 5, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                num_blocks=60, kv_dtype=W.BF16, io_dtype=W.BF16,
+                num_computed=[10, 100, 0, 37, 64], num_scheduled=[0, 1, 3, 0, 5])
+    step = R.GpuStep(w)
+    step.run()
+    torch.cuda.synchronize()
+    _check_attention(w, step)
+    step_nc = R.GpuStep(w, causal=False)
+    step_nc.run()
+    torch.cuda.synchronize()
+    ref = O.run_step(w, causal=False).out
+    assert np.abs(step_nc.out_f64() - ref).max() <= 2e-2
+
+
+def test_one_hot_probe_bit_exact(R):
+    """All keys zero except one aligned with q and large: every other weight
+    underflows to 0 in fp32, so the output equals that key's value exactly.
+    Values encode their position, so any block/offset mistake in the attention
+    kernel shows as a wrong number."""
+    say("one-hot probe")
+    H, D = 2, 128
+    L = 16 * 9 + 5
+    w = W.build("probe", 0, num_q_heads=4, num_kv_heads=H, head_dim=D, block_size=16,
+                num_blocks=40, kv_dtype=W.BF16, io_dtype=W.BF16, num_computed=[L - 1],
+                num_scheduled=[1])
+    pos = np.arange(L - 1)
+    # value of position j, dim e: +j for even e, -j for odd e (exact in bf16, j < 256)
+    sign = np.where(np.arange(D) % 2 == 0, 1.0, -1.0)
+    vals = pos[:, None, None] * sign[None, None, :] * np.ones((1, H, 1))
+    w.history[0].value[:] = W.f32_to_bf16_bits(vals.astype(np.float32))
+    w.value[:] = W.f32_to_bf16_bits(((L - 1) * sign + np.zeros((1, H, D))).astype(np.float32))
+    q = np.ones((1, 4, D), np.float32)
+    w.query[:] = W.f32_to_bf16_bits(q)
+    w.key[:] = 0
+    for jstar in [0, 15, 16, 77, L - 2]:
+        w.history[0].key[:] = 0
+        w.history[0].key[jstar] = W.f32_to_bf16_bits(np.full((H, D), 16.0, np.float32))
+        step = R.GpuStep(w)
+        step.run()
+        torch.cuda.synchronize()
+        got = step.out.float().cpu().numpy()[0]
+        want = jstar * sign
+        assert (got == want[None, :]).all(), (jstar, got[0, :8], want[:8])
+
+
+def test_nan_canaries_never_read(R):
+    """Unwritten pool slots hold NaN and trailing block-table entries are -1:
+    outputs stay finite (covers partially filled last blocks)."""
+    say("nan canaries")
+    w = W.build("canary", 9, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                num_blocks=80, kv_dtype=W.BF16, io_dtype=W.BF16,
+                num_computed=[0, 16, 17, 30, 129], num_scheduled=[1, 1, 1, 2, 20])
+    w.block_table = np.concatenate([w.block_table, np.full((w.num_seqs, 3), -1, np.int32)], axis=1)
+    step = R.GpuStep(w)
+    step.run()
+    torch.cuda.synchronize()
+    assert np.isfinite(step.out_f64()).all()
+    _check_attention(w, step)
+
+
+def test_attention_long_context_config_sampled(R):
+    say("attention config 4 (long context, sampled rows)")
+    w = W.make(4)
+    step = R.GpuStep(w)
+    step.run()
+    torch.cuda.synchronize()
+    _check_attention(w, step, tokens=np.array([0, 3, 7], dtype=np.int32))
