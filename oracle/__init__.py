@@ -24,9 +24,10 @@ _LIB_PATH = os.environ.get("PA_ORACLE_LIB") or os.path.join(_HERE, "_build", "li
 F32, BF16, FP8 = 0, 1, 2
 _DT = {"f32": F32, "bf16": BF16, "fp8": FP8}
 _NP = {F32: np.float32, BF16: np.uint16, FP8: np.uint8}
-# Canary written into every pool element that no step has written: NaN in
-# each element type (fp32 quiet NaN, bf16 all-ones, E4M3FN S.1111.111).
-_CANARY = {F32: np.float32(np.nan), BF16: np.uint16(0xFFFF), FP8: np.uint8(0x7F)}
+# Canary written into every pool element that no step has written: the
+# all-ones bit pattern, a NaN in each element type (fp32, bf16, and E4M3FN
+# S.1111.111).
+_CANARY = {F32: np.uint32(0xFFFFFFFF).view(np.float32), BF16: np.uint16(0xFFFF), FP8: np.uint8(0xFF)}
 
 
 class _Pool(C.Structure):
