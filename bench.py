@@ -1,0 +1,198 @@
+"""Benchmark of one paged-attention step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config N] [--gpus 1]
+
+A step is the whole hot path on one batch: slot derivation (pa_slot_mapping),
+KV scatter (pa_write_kv) and attention (pa_attention: host plan + split-K
+decode + merge + MFMA extend), with every input already in HBM.  The default
+workload is the Llama-3-8B-shaped decode layer: 64 requests, 32 q / 8 kv
+heads, head_dim 128, block 16, bf16 KV, context U[512, 4096], 40k-block pool.
+
+Prints one JSON line: tokens/s (whole step), the dominant kernel's
+bandwidth against the HBM roofline (HIP events recorded around every launch
+of that kernel on its own stream during the timed steps), and the CPU oracle
+timed on this host on the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
+ELEM = {"f32": 4, "bf16": 2, "fp8": 1}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time for the oracle baseline (0 disables it)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (for counter calibration) and exit")
+    return ap.parse_args()
+
+
+def algorithmic_work(w, seq_lens, qsl, ext_min_rows=16, extend_on=True):
+    """Bytes the split-K decode kernel must move and flops the extend kernel
+    must do, per step, by the per-unit formulas in the design notes."""
+    b_kv, b_io = ELEM[w.kv_dtype], ELEM[w.io_dtype]
+    H, Hq, D, S = w.num_kv_heads, w.num_q_heads, w.head_dim, w.block_size
+    dec_bytes = 0
+    ext_flops = 0
+    ext_bytes = 0
+    for i in range(w.num_seqs):
+        c, L = int(qsl[i + 1] - qsl[i]), int(seq_lens[i])
+        if c == 0:
+            continue
+        use_ext = extend_on and c >= ext_min_rows and w.kv_dtype == "bf16" and D == 128
+        if use_ext:
+            ext_flops += 4 * Hq * D * sum(L - c + t + 1 for t in range(c))
+            ext_bytes += L * H * D * 2 * b_kv + c * Hq * D * 2 * b_io
+        else:
+            for t in range(c):
+                Lv = L - c + t + 1
+                dec_bytes += Lv * H * D * 2 * b_kv + Hq * D * b_io + -(-Lv // S) * 4
+    return dec_bytes, ext_flops, ext_bytes
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": a.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    from paged_kv_cache_pool_amd import binding as B
+    from paged_kv_cache_pool_amd import runner
+    from paged_kv_cache_pool_amd import workloads as W
+
+    if a.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n}), flush=True)
+        return
+
+    t0 = time.time()
+    w = W.make(a.config, a.seed)
+    print(f"[bench] workload {w.name}: generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+    step = runner.GpuStep(w, stream=stream)
+    print(f"[bench] device set-up done ({time.time() - t0:.1f}s)", file=sys.stderr, flush=True)
+
+    for _ in range(a.warmup):
+        step.run()
+    torch.cuda.synchronize()
+
+    # timed region: K steps back to back, bracketed by synchronisations, with
+    # HIP events around every kernel launch on the step's stream
+    B.profile_enable(True)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(a.steps):
+        step.run()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_instr = ev0.elapsed_time(ev1) / a.steps
+    kernels = {}
+    for name in ("k_slot_mapping", "k_write_kv", "k_decode", "k_merge", "k_extend"):
+        n, ms = B.profile_read(name)
+        if n:
+            kernels[name] = {"launches": n, "avg_us": 1000.0 * ms / n}
+    B.profile_enable(False)
+
+    # the same K steps without the per-kernel events (reported step time)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(a.steps):
+        step.run()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / a.steps
+
+    T = w.num_tokens
+    tokens_per_s = T / (ms_per_step / 1000.0)
+    qsl, sl = B.prepare_metadata(w.num_computed, w.num_scheduled)
+    ext_on = os.environ.get("PA_DISABLE_EXTEND", "0") in ("", "0")
+    dec_bytes, ext_flops, ext_bytes = algorithmic_work(
+        w, sl, qsl, int(os.environ.get("PA_EXTEND_MIN_ROWS", "16")), ext_on and "k_extend" in kernels)
+
+    if "k_decode" in kernels and (dec_bytes > 0):
+        dom = "k_decode"
+        achieved = dec_bytes / (kernels[dom]["avg_us"] * 1e-6) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": None, "algorithmic_bytes_per_launch": dec_bytes}
+    else:
+        dom = "k_extend"
+        achieved = ext_flops / (kernels[dom]["avg_us"] * 1e-6) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "algorithmic_flops_per_launch": ext_flops}
+
+    cpu = None
+    if a.cpu_seconds > 0:
+        import oracle as O
+        pool = O.build_pool(w)
+        reps, t_cpu = 0, 0.0
+        while t_cpu < a.cpu_seconds and reps < 50:
+            t1 = time.perf_counter()
+            O.run_step(w, pool=pool)
+            t_cpu += time.perf_counter() - t1
+            reps += 1
+        cpu = {"value": round(T * reps / t_cpu, 2), "unit": "tokens/s", "cores": O.num_threads(),
+               "kind": "oracle",
+               "sample": f"whole step of this workload ({T} tokens: slots, write, attention), "
+                         f"{reps} repetition(s), {t_cpu:.1f}s, fp64"}
+
+    out = {
+        "metric": "tokens/s per paged-attn step + decode KV GB/s (% of HBM peak), 1 MI355X",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.kv_dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "tokens_per_step": T,
+                   "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "block_size": w.block_size, "kv_dtype": w.kv_dtype,
+                   "num_blocks": w.num_blocks, "context_total": int(sl.sum()),
+                   "context_min": int(sl.min()), "context_max": int(sl.max()), "seed": a.seed},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels_us": {k: round(v["avg_us"], 2) for k, v in kernels.items()},
+        "ms_per_step_with_kernel_events": round(ms_instr, 5),
+        "decode_kv_gbps": roof["achieved"] if roof["unit"] == "GB/s" else None,
+    }
+    if ext_flops:
+        out["extend_tflops"] = round(ext_flops / (kernels["k_extend"]["avg_us"] * 1e-6) / 1e12, 1) \
+            if "k_extend" in kernels else None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
