@@ -225,9 +225,7 @@ static int extend_min_rows() {
 }
 
 static bool extend_supported(const pa_kv_pool &p, pa_dtype q_dtype) {
-  (void)p;
-  (void)q_dtype;
-  return false;
+  return q_dtype == PA_BF16 && p.kv_dtype == PA_BF16 && p.head_dim == 128;
 }
 
 static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dtype q_dtype,

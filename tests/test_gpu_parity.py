@@ -283,3 +283,58 @@ def test_attention_long_context_config_sampled(R):
     step.run()
     torch.cuda.synchronize()
     _check_attention(w, step, tokens=np.array([0, 3, 7], dtype=np.int32))
+
+
+# ------------------------------------------------------------ MFMA extend --
+
+@pytest.mark.parametrize("g", [1, 2, 4, 8])
+@pytest.mark.parametrize("c,hist", [(16, 0), (17, 5), (33, 64), (100, 37), (129, 300), (257, 16)])
+def test_extend_chunks(R, g, c, hist):
+    """Prefill chunks (c >= 16 rows go to the MFMA kernel) with ragged column
+    tiles, history before the chunk and a decode row in the same batch."""
+    say("extend g", g, "c", c, "hist", hist)
+    w = W.build(f"ext_{g}_{c}_{hist}", c + hist, num_q_heads=2 * g, num_kv_heads=2, head_dim=128,
+                block_size=16, num_blocks=-(-(c + hist) // 16) + 40, kv_dtype=W.BF16,
+                io_dtype=W.BF16, num_computed=[hist, 70], num_scheduled=[c, 1])
+    step = R.GpuStep(w)
+    step.run()
+    torch.cuda.synchronize()
+    _check_attention(w, step)
+
+
+def test_extend_noncausal(R):
+    say("extend non-causal")
+    w = W.build("ext_nc", 4, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                num_blocks=30, kv_dtype=W.BF16, io_dtype=W.BF16, num_computed=[50, 0],
+                num_scheduled=[70, 40])
+    step = R.GpuStep(w, causal=False)
+    step.run()
+    torch.cuda.synchronize()
+    ref = O.run_step(w, causal=False).out
+    err = np.abs(step.out_f64() - ref).max()
+    say("extend non-causal err", err)
+    assert err <= 2e-2
+
+
+def test_one_hot_probe_extend_bit_exact(R):
+    """The one-hot probe through the MFMA kernel: 40 new rows all select the
+    same history position; P = 1 and 0 are exact in bf16, so O = v exactly."""
+    say("one-hot probe (extend)")
+    H, D, hist, c = 2, 128, 16 * 7 + 3, 40
+    w = W.build("probe_ext", 1, num_q_heads=8, num_kv_heads=H, head_dim=D, block_size=16,
+                num_blocks=30, kv_dtype=W.BF16, io_dtype=W.BF16, num_computed=[hist],
+                num_scheduled=[c])
+    sign = np.where(np.arange(D) % 2 == 0, 1.0, -1.0)
+    vals = np.arange(hist)[:, None, None] * sign[None, None, :] * np.ones((1, H, 1))
+    w.history[0].value[:] = W.f32_to_bf16_bits(vals.astype(np.float32))
+    w.value[:] = W.f32_to_bf16_bits((200.0 * sign + np.zeros((c, H, D))).astype(np.float32))
+    w.query[:] = W.f32_to_bf16_bits(np.ones((c, 8, D), np.float32))
+    w.key[:] = 0
+    for jstar in [0, 31, 64, hist - 1]:
+        w.history[0].key[:] = 0
+        w.history[0].key[jstar] = W.f32_to_bf16_bits(np.full((H, D), 16.0, np.float32))
+        step = R.GpuStep(w)
+        step.run()
+        torch.cuda.synchronize()
+        got = step.out.float().cpu().numpy()
+        assert (got == (jstar * sign)[None, None, :]).all(), (jstar, got[0, 0, :6])
