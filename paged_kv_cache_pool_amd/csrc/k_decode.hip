@@ -268,9 +268,13 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
   }
 }
 
-// Merge of partitions: one wave per (token, q head).
+// Merge of partitions: one wave per (token, q head).  Every lane reads one
+// partition's (m, l) (64 per round), so the maximum and the weights come from
+// one wave reduction instead of a chain of dependent loads; the partial
+// outputs are then summed with the weights broadcast from LDS.
 template <int D, bool F32OUT>
 __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
+  __shared__ float wts[4][64];
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int unit = blockIdx.x * 4 + wave;
@@ -279,23 +283,45 @@ __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
   const int qh = unit - item_idx * a.num_q_heads;
   const MergeItem it = a.items[item_idx];
   const int first = uniform(it.first), count = uniform(it.count), token = uniform(it.token);
+  const float *ml = a.part_ml + ((int64_t)first * a.num_q_heads + qh) * 2;
+  const int64_t ml_stride = (int64_t)a.num_q_heads * 2;
+
   float m = -INFINITY;
-  for (int r = 0; r < count; ++r)
-    m = fmaxf(m, a.part_ml[((int64_t)(first + r) * a.num_q_heads + qh) * 2]);
+  for (int r0 = 0; r0 < count; r0 += 64)
+    if (r0 + lane < count) m = fmaxf(m, ml[(r0 + lane) * ml_stride]);
+  m = wave_max_dpp(m);
+
   constexpr int NE = D / 64;
   float acc[NE];
 #pragma unroll
   for (int i = 0; i < NE; ++i) acc[i] = 0.0f;
   float l = 0.0f;
-  for (int r = 0; r < count; ++r) {
-    const int64_t base = (int64_t)(first + r) * a.num_q_heads + qh;
-    const float mr = a.part_ml[base * 2], lr = a.part_ml[base * 2 + 1];
-    const float f = mr == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mr - m);
-    l = fmaf(f, lr, l);
-    const float *po = a.part_o + base * D;
+  for (int r0 = 0; r0 < count; r0 += 64) {
+    const int r = r0 + lane;
+    float wgt = 0.0f;
+    if (r < count) {
+      const float mr = ml[r * ml_stride];
+      wgt = mr == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mr - m);
+      l = fmaf(wgt, ml[r * ml_stride + 1], l);
+    }
+    wts[wave][lane] = wgt;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int n = min(64, count - r0);
+    const float *po = a.part_o + ((int64_t)(first + r0) * a.num_q_heads + qh) * D + lane;
+    const int64_t po_stride = (int64_t)a.num_q_heads * D;
+#pragma unroll 4
+    for (int k = 0; k < n; ++k) {
+      const float w = wts[wave][k];
 #pragma unroll
-    for (int i = 0; i < NE; ++i) acc[i] = fmaf(f, po[i * 64 + lane], acc[i]);
+      for (int i = 0; i < NE; ++i) acc[i] = fmaf(w, po[k * po_stride + i * 64], acc[i]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
+  l = wave_sum_dpp(l);
   const float inv = 1.0f / l;
 #pragma unroll
   for (int i = 0; i < NE; ++i) {

@@ -43,12 +43,12 @@ hipError_t launch_slot_mapping(const pa_batch &b, int64_t *slots, int max_c, hip
 }
 
 // ---------------------------------------------------------------------------
-// KV scatter.  A workgroup takes 16 consecutive tokens of one kv head.
-//  K: thread (chunk c, token n) copies / encodes the 16-byte pool chunk c of
-//     token n, so the 16 threads of a chunk write 256 contiguous bytes when
-//     the tokens' slots are consecutive within a block (prefill).
-//  V: the 16 rows are staged in LDS; thread (dim e, token n) writes one
-//     element of pool row e, token-fastest, so consecutive slots coalesce.
+// KV scatter.  One thread per (token, kv head, 16-byte pool chunk of K): it
+// reads the token's slot and the matching input elements of K and V once and
+// writes the K chunk (16 contiguous bytes) and the same dims of V (one
+// element per dim row of the dimension-major V tile).  Threads of one token
+// and head are consecutive, so input rows are read contiguously; a decode
+// step needs a single round trip per token.
 // IN / KV are the input and pool element kinds.
 // ---------------------------------------------------------------------------
 template <int IN, int KV, int D>
@@ -67,79 +67,59 @@ __global__ __launch_bounds__(256) void k_write_kv(const void *__restrict__ key,
   static_assert(IN != KV_FP8, "fp8 is a pool format only");
   static_assert(KV == KV_FP8 || IN == KV, "same-dtype copy or fp8 encode");
 
-  __shared__ float vstage[kBlock][D + 1];
-
-  const int h = blockIdx.y;
-  const int n0 = blockIdx.x * kBlock;
-  const int tid = threadIdx.x;
-
-  // ---- K ----
-  for (int w = tid; w < NCH * kBlock; w += 256) {
-    const int c = w / kBlock, nn = w % kBlock, n = n0 + nn;
-    if (n >= num_tokens) continue;
-    const int64_t slot = slots[n];
-    if (slot < 0 || slot >= capacity) continue;
-    const int64_t blk = slot / kBlock;
-    const int off = (int)(slot - blk * kBlock);
-    char *dst = (char *)kc + (blk * num_kv_heads + h) * (int64_t)TILE + (int64_t)c * (kBlock * 16) +
-                off * 16;
-    const char *src = (const char *)key + (((int64_t)n * num_kv_heads + h) * D + (int64_t)c * E) * IB;
-    if constexpr (KV != KV_FP8) {
-      *(uint4 *)dst = *(const uint4 *)src;
-    } else {
-      uint32_t out[4];
+  const int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)num_tokens * num_kv_heads * NCH;
+  if (w >= total) return;
+  const int c = (int)(w % NCH);
+  const int64_t th = w / NCH;               // token * num_kv_heads + head
+  const int h = (int)(th % num_kv_heads);
+  const int64_t n = th / num_kv_heads;
+  const int64_t slot = slots[n];
+  // input elements c*E .. c*E+E-1 of the token's K and V rows
+  const char *ks = (const char *)key + (th * D + (int64_t)c * E) * IB;
+  const char *vs = (const char *)value + (th * D + (int64_t)c * E) * IB;
+  constexpr int NV = E * IB / 16;           // 16-byte input vectors per chunk
+  uint4 kin[NV], vin[NV];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t word = 0;
+  for (int i = 0; i < NV; ++i) {
+    kin[i] = ((const uint4 *)ks)[i];
+    vin[i] = ((const uint4 *)vs)[i];
+  }
+  if (slot < 0 || slot >= capacity) return;  // padding token / out-of-range slot
+  const int64_t blk = slot / kBlock;
+  const int off = (int)(slot - blk * kBlock);
+  const int64_t tile = (blk * num_kv_heads + h) * (int64_t)TILE;
+  char *kdst = (char *)kc + tile + (int64_t)c * (kBlock * 16) + off * 16;
+  char *vdst = (char *)vc + tile + ((int64_t)c * E * kBlock + off) * PB;  // row c*E, column off
+  if constexpr (KV != KV_FP8) {
+    *(uint4 *)kdst = kin[0];
+    const uint32_t *vw = (const uint32_t *)vin;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int e = q * 4 + b;
-          float x;
-          if constexpr (IN == KV_BF16) x = __uint_as_float((uint32_t)((const uint16_t *)src)[e] << 16);
-          else x = ((const float *)src)[e];
-          word |= e4m3_encode(x / k_scale) << (8 * b);
-        }
-        out[q] = word;
-      }
-      *(uint4 *)dst = make_uint4(out[0], out[1], out[2], out[3]);
+    for (int e = 0; e < E; ++e) {
+      if constexpr (KV == KV_F32) ((uint32_t *)vdst)[e * kBlock] = vw[e];
+      else ((uint16_t *)vdst)[e * kBlock] = (uint16_t)(vw[e / 2] >> (16 * (e & 1)));
     }
-  }
-
-  // ---- V: stage the 16 rows as floats (exact for fp32 and bf16 inputs) ----
-  for (int w = tid; w < kBlock * D; w += 256) {
-    const int nn = w / D, e = w % D, n = n0 + nn;
-    float x = 0.0f;
-    if (n < num_tokens) {
-      const int64_t idx = ((int64_t)n * num_kv_heads + h) * D + e;
-      if constexpr (IN == KV_BF16) x = __uint_as_float((uint32_t)((const uint16_t *)value)[idx] << 16);
-      else x = ((const float *)value)[idx];
+  } else {
+    const uint32_t *kw = (const uint32_t *)kin, *vw = (const uint32_t *)vin;
+    auto elem = [](const uint32_t *words, int e) -> float {
+      if constexpr (IN == KV_BF16) return __uint_as_float((words[e / 2] >> (16 * (e & 1))) << 16);
+      else return __uint_as_float(words[e]);
+    };
+    uint32_t out[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      out[e / 4] |= e4m3_encode(elem(kw, e) / k_scale) << (8 * (e & 3));
+      ((uint8_t *)vdst)[e * kBlock] = (uint8_t)e4m3_encode(elem(vw, e) / v_scale);
     }
-    vstage[nn][e] = x;
-  }
-  __syncthreads();
-  for (int w = tid; w < kBlock * D; w += 256) {
-    const int e = w / kBlock, nn = w % kBlock, n = n0 + nn;
-    if (n >= num_tokens) continue;
-    const int64_t slot = slots[n];
-    if (slot < 0 || slot >= capacity) continue;
-    const int64_t blk = slot / kBlock;
-    const int off = (int)(slot - blk * kBlock);
-    const int64_t idx = ((blk * num_kv_heads + h) * D + e) * kBlock + off;  // element index
-    const float x = vstage[nn][e];
-    if constexpr (KV == KV_F32) {
-      ((float *)vc)[idx] = x;
-    } else if constexpr (KV == KV_BF16) {
-      ((uint16_t *)vc)[idx] = (uint16_t)(__float_as_uint(x) >> 16);  // exact: x came from bf16
-    } else {
-      ((uint8_t *)vc)[idx] = (uint8_t)e4m3_encode(x / v_scale);
-    }
+    *(uint4 *)kdst = make_uint4(out[0], out[1], out[2], out[3]);
   }
 }
 
 template <int IN, int KV>
 static hipError_t write_dispatch_d(const pa_kv_pool &p, const void *key, const void *value,
                                    const int64_t *slots, int32_t T, hipStream_t s) {
-  const dim3 grid((T + kBlock - 1) / kBlock, p.num_kv_heads);
+  const int64_t chunks = (int64_t)T * p.num_kv_heads * (p.head_dim * KvTraits<KV>::bytes / 16);
+  const dim3 grid((unsigned)((chunks + 255) / 256));
   const int64_t cap = (int64_t)p.num_blocks * p.block_size;
   prof_begin("k_write_kv", s);
   if (p.head_dim == 128)

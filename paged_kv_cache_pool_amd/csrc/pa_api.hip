@@ -435,14 +435,19 @@ pa_status pa_attention(const pa_kv_pool *pool, const pa_batch *batch, const void
     a.num_blocks = pool->num_blocks;
     a.num_kv_heads = pool->num_kv_heads;
     a.num_q_heads = num_q_heads;
-    a.g = g_total;
-    a.h0 = 0;
     a.g_total = g_total;
     a.scale_log2 = softmax_scale * log2e * kscale;
     a.v_scale = vscale;
-    const int g_tmpl = g_total <= 1 ? 1 : g_total <= 2 ? 2 : g_total <= 4 ? 4 : g_total <= 8 ? 8 : 16;
-    e = launch_decode(*pool, q_dtype, a, g_tmpl, s);
-    if (e != hipSuccess) return hip_fail(e, "k_decode launch");
+    // q heads per launch: the whole GQA group where the registers allow it,
+    // otherwise the group is covered by several launches (fp32 pools)
+    const int g_max = 16;
+    for (int h0 = 0; h0 < g_total; h0 += g_max) {
+      a.h0 = h0;
+      a.g = std::min(g_max, g_total - h0);
+      const int g_tmpl = a.g <= 1 ? 1 : a.g <= 2 ? 2 : a.g <= 4 ? 4 : a.g <= 8 ? 8 : 16;
+      e = launch_decode(*pool, q_dtype, a, g_tmpl, s);
+      if (e != hipSuccess) return hip_fail(e, "k_decode launch");
+    }
   }
   if (!plan.merge.empty()) {
     MergeArgs m{};

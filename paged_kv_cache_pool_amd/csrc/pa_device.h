@@ -89,4 +89,61 @@ __device__ __forceinline__ int readlane(int x, int lane) {
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load the compiler may neither hoist nor batch with its neighbours
+// (used for LDS data that is re-read every step instead of kept in registers).
+__device__ __forceinline__ uint4 load16_volatile(const void *p) {
+  const u32x4_t v = *(const volatile u32x4_t *)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+}  // namespace pa
+
+namespace pa {
+
+// DPP lane movements (gfx9 encodings).
+constexpr int kDppQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppRowHalfMirror = 0x141; // lane i of 8 <- lane 7 - i
+constexpr int kDppRowMirror = 0x140;     // lane i of 16 <- lane 15 - i
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// All 16 lanes of each row end with the row's max / sum (butterfly over the
+// row: lane ^ 1, lane ^ 2, the other quad, the other half-row).
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, dpp_f32<kDppQuadSwap1>(x));
+  x = fmaxf(x, dpp_f32<kDppQuadSwap2>(x));
+  x = fmaxf(x, dpp_f32<kDppRowHalfMirror>(x));
+  x = fmaxf(x, dpp_f32<kDppRowMirror>(x));
+  return x;
+}
+
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp_f32<kDppQuadSwap1>(x);
+  x += dpp_f32<kDppQuadSwap2>(x);
+  x += dpp_f32<kDppRowHalfMirror>(x);
+  x += dpp_f32<kDppRowMirror>(x);
+  return x;
+}
+
+__device__ __forceinline__ float lane_f32(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+// Wave-wide max / sum, result uniform (row results combined through readlane).
+__device__ __forceinline__ float wave_max_dpp(float x) {
+  x = row_max16(x);
+  return fmaxf(fmaxf(lane_f32(x, 0), lane_f32(x, 16)), fmaxf(lane_f32(x, 32), lane_f32(x, 48)));
+}
+
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+  x = row_sum16(x);
+  return (lane_f32(x, 0) + lane_f32(x, 16)) + (lane_f32(x, 32) + lane_f32(x, 48));
+}
+
 }  // namespace pa

@@ -69,6 +69,7 @@ struct DecodeArgs {
   int32_t g_total;        // num_q_heads / num_kv_heads
   float scale_log2;       // softmax_scale * log2(e) (* k_scale for fp8 pools)
   float v_scale;          // 1 for non-fp8 pools
+  int32_t zero;           // always 0 (used to keep per-step loads inside the loop)
 };
 
 struct MergeArgs {
