@@ -165,7 +165,8 @@ size_t pa_attention_workspace_bytes(const pa_kv_pool *pool, const pa_batch *batc
  *   s_j = softmax_scale * (query[n][h] . K_j[h / g]),  g = num_q_heads / num_kv_heads;
  *   output[n][h] = sum_j softmax(s)_j * V_j[h / g],
  * with K_j / V_j read from the pool through block_table (FP8 pools are
- * dequantised with k_scale / v_scale).  Accumulation is fp32; the output is
+ * dequantised with k_scale / v_scale).  softmax_scale must be finite and
+ * positive (normally 1/sqrt(head_dim)).  Accumulation is fp32; the output is
  * rounded to q_dtype.  Supported: q_dtype F32 with an F32 pool; q_dtype
  * BF16 with a BF16 or FP8 pool; num_q_heads a multiple of num_kv_heads with
  * g <= 16.

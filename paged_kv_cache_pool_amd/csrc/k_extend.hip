@@ -30,7 +30,9 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kExtD = 128;
 constexpr int kTileKeys = 64;
 constexpr int kKPitch = kExtD * 2 + 16;        // bytes per key row of the K tile in LDS
-constexpr int kVPitch = kTileKeys * 2 + 16;    // bytes per dim row of the V tile in LDS
+// bytes per dim row of the V tile in LDS: 136 = 34 banks, so the 16 rows read
+// together by an 8-byte LDS read land on 16 distinct bank pairs
+constexpr int kVPitch = kTileKeys * 2 + 8;
 constexpr int kKBytes = kTileKeys * kKPitch;   // 17408
 constexpr int kVBytes = kExtD * kVPitch;       // 18432
 constexpr int kBufBytes = kKBytes + kVBytes;
@@ -64,6 +66,10 @@ __global__ __launch_bounds__(256, 2) void k_extend(const ExtendArgs a) {
   const int t = col / g, hg = col - t * g;
   const int nvis = a.causal ? hist + t + 1 : L;  // visible keys of this column
   const int hsel = lane >> 5;                    // which 8-element k group the lane feeds
+  // visible keys of the wave's first column (columns are token-major, so the
+  // smallest); tiles below it need no causal mask
+  const int wave_first_col = min(col0 + wave * 32, ncols - 1);
+  const int wave_min_nvis = a.causal ? hist + wave_first_col / g + 1 : L;
 
   // Q^T operand: 8 k-steps of 16 dims; lane holds dims 16ks + 8 hsel .. +8
   const uint16_t *qrow = (const uint16_t *)a.q + ((int64_t)(tok0 + t) * a.num_q_heads + kvh * g + hg) * kExtD;
@@ -120,7 +126,9 @@ __global__ __launch_bounds__(256, 2) void k_extend(const ExtendArgs a) {
       const int kc = w >> 4, kk = w & 15;        // K: chunk, key in block
       *(uint4 *)(kb + (b * kBlock + kk) * kKPitch + kc * 16) = kst[r];
       const int vd = w >> 1, vh = w & 1;         // V: dim, key half
-      *(uint4 *)(vb + vd * kVPitch + (b * kBlock + vh * 8) * 2) = vst[r];
+      uint2 *vdst = (uint2 *)(vb + vd * kVPitch + (b * kBlock + vh * 8) * 2);  // 8-byte aligned rows
+      vdst[0] = make_uint2(vst[r].x, vst[r].y);
+      vdst[1] = make_uint2(vst[r].z, vst[r].w);
     }
   };
 
@@ -157,37 +165,53 @@ __global__ __launch_bounds__(256, 2) void k_extend(const ExtendArgs a) {
         }
       }
       // ---- online softmax over this tile (column = lane & 31) ----
+      // Scores stay unscaled until the exponent (scale > 0 commutes with max);
+      // keys past a column's causal limit are masked only on tiles that cross
+      // some column's limit.  The reference max m_ref is raised only when a
+      // column's maximum exceeds it by more than 2^8 (decided for the whole
+      // wave), so O and l are rescaled rarely; exp2(s*c - m_ref) <= 2^8 stays
+      // well inside bf16 and fp32, and O / l is unchanged by the choice of
+      // reference.
+      const bool crosses = kbase + kTileKeys > wave_min_nvis;
       float mt_max = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kbase + mt * 32 + 8 * (r >> 2) + 4 * hsel + (r & 3);
-          const float s = key < nvis ? sacc[mt][r] * a.scale_log2 : -INFINITY;
-          sacc[mt][r] = s;
-          mt_max = fmaxf(mt_max, s);
+          float sv = sacc[mt][r];
+          if (crosses) {
+            const int key = kbase + mt * 32 + 8 * (r >> 2) + 4 * hsel + (r & 3);
+            sv = key < nvis ? sv : -INFINITY;
+            sacc[mt][r] = sv;
+          }
+          mt_max = fmaxf(mt_max, sv);
         }
       mt_max = fmaxf(mt_max, __shfl_xor(mt_max, 32, 64));
-      const float m_new = fmaxf(m_run, mt_max);
-      const bool any = m_new != -INFINITY;
-      const float alpha = any ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+      const float cand = mt_max * a.scale_log2;      // this tile's max, log2 units
+      const bool raise = cand > m_run + 8.0f;
+      if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform: rescale
+        const float m_new = raise ? cand : m_run;
+        const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int md = 0; md < 4; ++md)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[md][r] *= alpha;
+        m_run = m_new;
+      }
+      const float neg_m = m_run == -INFINITY ? 0.0f : -m_run;  // fully masked column: p = 0
       float psum = 0.0f;
       uint32_t pp[2][8];                          // P^T as bf16 pairs, [mt][r/2]
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const float p0 = any ? __builtin_amdgcn_exp2f(sacc[mt][r] - m_new) : 0.0f;
-          const float p1 = any ? __builtin_amdgcn_exp2f(sacc[mt][r + 1] - m_new) : 0.0f;
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[mt][r], a.scale_log2, neg_m));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[mt][r + 1], a.scale_log2, neg_m));
           psum += p0 + p1;
           pp[mt][r >> 1] = pack_bf16x2(p0, p1);
         }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int md = 0; md < 4; ++md)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[md][r] *= alpha;
+      l_run += psum;
       // ---- O^T += V^T . P^T ----
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {

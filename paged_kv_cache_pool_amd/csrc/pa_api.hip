@@ -132,6 +132,42 @@ static pa_status upload(void *dst, const void *src, size_t bytes, hipStream_t s)
   return PA_OK;
 }
 
+// ------------------------------------------------------------- side stream --
+// Prefill rows (MFMA) and decode rows (HBM-bound) of one step are
+// independent; with PA_OVERLAP=1 the extend kernel runs on a second stream,
+// forked from and joined back to the caller's stream with events, so the two
+// kernels overlap on the GPU while the caller still sees one ordered stream.
+// Off by default: measured on the mixed 2048-token step it is slower than
+// running the two kernels one after the other (each slows the other more than
+// the overlap gains).  One side stream and event pair per device, created on
+// first use, default priority.
+
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+
+static std::mutex g_side_mu;
+static std::vector<SideStream> g_side;
+
+static pa_status side_stream(SideStream **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  if ((int)g_side.size() <= dev) g_side.resize(dev + 1);
+  SideStream &ss = g_side[dev];
+  if (!ss.stream) {
+    if ((e = hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking)) != hipSuccess)
+      return hip_fail(e, "side stream");
+    if ((e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess)
+      return hip_fail(e, "side stream events");
+  }
+  *out = &ss;
+  return PA_OK;
+}
+
 // ---------------------------------------------------------------- checks ---
 
 static int elem_bytes(pa_dtype d) { return d == PA_F32 ? 4 : d == PA_BF16 ? 2 : 1; }
@@ -276,12 +312,31 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
       plan.n_slots += nparts;
     }
   }
-  // longest extend tiles first (their key range grows with the column offset)
-  std::stable_sort(plan.ext.begin(), plan.ext.end(), [g](const ExtendItem &x, const ExtendItem &y) {
-    const int64_t kx = (int64_t)x.L - x.c + std::min<int64_t>(x.c, (x.col0 + kExtCols + g - 1) / g);
-    const int64_t ky = (int64_t)y.L - y.c + std::min<int64_t>(y.c, (y.col0 + kExtCols + g - 1) / g);
-    return kx > ky;
-  });
+  // Extend tiles: workgroup b runs on XCD b % 8 (round-robin dispatch), and
+  // all tiles of one (request, kv head) read the same K/V, so each (request,
+  // kv head) is pinned to one XCD, whose L2 then serves the repeats.  Within
+  // an XCD the longest tiles (key range grows with the column offset) go
+  // first.
+  if (!plan.ext.empty()) {
+    constexpr int kXcds = 8;
+    auto keys_of = [g](const ExtendItem &x) {
+      return (int64_t)x.L - x.c + std::min<int64_t>(x.c, (x.col0 + kExtCols + g - 1) / g);
+    };
+    std::vector<std::vector<ExtendItem>> q(kXcds);
+    for (const ExtendItem &x : plan.ext) q[(x.req * Hkv + x.kvh) % kXcds].push_back(x);
+    for (auto &v : q)
+      std::stable_sort(v.begin(), v.end(), [&](const ExtendItem &x, const ExtendItem &y) { return keys_of(x) > keys_of(y); });
+    plan.ext.clear();
+    std::vector<size_t> pos(kXcds, 0);
+    for (bool more = true; more;) {
+      more = false;
+      for (int x = 0; x < kXcds; ++x)
+        if (pos[x] < q[x].size()) {
+          plan.ext.push_back(q[x][pos[x]++]);
+          more = true;
+        }
+    }
+  }
 
   size_t off = 0;
   plan.off_dec = off;
@@ -392,7 +447,8 @@ pa_status pa_attention(const pa_kv_pool *pool, const pa_batch *batch, const void
   pa_status st = check_attention_args(pool, batch, q_dtype, num_q_heads, true);
   if (st != PA_OK) return st;
   if (batch->num_tokens > 0 && (!query || !output)) return fail(PA_ERR_INVALID_ARG, "NULL query/output");
-  if (!std::isfinite(softmax_scale)) return fail(PA_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0f))
+    return fail(PA_ERR_INVALID_ARG, "softmax_scale must be finite and positive");
   if (batch->num_tokens == 0) return PA_OK;
   hipStream_t s = (hipStream_t)stream;
   if (env_flag("PA_VALIDATE") && (st = validate_block_table(batch, pool->num_blocks, s)) != PA_OK) return st;
@@ -420,6 +476,37 @@ pa_status pa_attention(const pa_kv_pool *pool, const pa_batch *batch, const void
   const float vscale = pool->kv_dtype == PA_FP8_E4M3 ? pool->v_scale : 1.0f;
 
   hipError_t e = hipSuccess;
+  // the extend kernel goes to the side stream when decode work runs beside it
+  hipStream_t xs = s;
+  SideStream *side = nullptr;
+  const bool fork = !plan.ext.empty() && !plan.dec.empty() && env_flag("PA_OVERLAP");
+  if (fork) {
+    if ((st = side_stream(&side)) != PA_OK) return st;
+    if ((e = hipEventRecord(side->fork, s)) != hipSuccess) return hip_fail(e, "fork record");
+    if ((e = hipStreamWaitEvent(side->stream, side->fork, 0)) != hipSuccess) return hip_fail(e, "fork wait");
+    xs = side->stream;
+  }
+  if (!plan.ext.empty()) {
+    ExtendArgs x{};
+    x.q = query;
+    x.out = output;
+    x.k_cache = pool->k_cache;
+    x.v_cache = pool->v_cache;
+    x.block_table = batch->block_table;
+    x.items = (const ExtendItem *)(ws + plan.off_ext);
+    x.n_items = (int32_t)plan.ext.size();
+    x.bt_stride = batch->bt_stride;
+    x.num_blocks = pool->num_blocks;
+    x.num_kv_heads = pool->num_kv_heads;
+    x.num_q_heads = num_q_heads;
+    x.g = g_total;
+    x.causal = causal ? 1 : 0;
+    x.scale_log2 = softmax_scale * log2e * kscale;
+    x.k_scale = kscale;
+    x.v_scale = vscale;
+    e = launch_extend(*pool, x, xs);
+    if (e != hipSuccess) return hip_fail(e, "k_extend launch");
+  }
   if (!plan.dec.empty()) {
     DecodeArgs a{};
     a.q = query;
@@ -460,26 +547,9 @@ pa_status pa_attention(const pa_kv_pool *pool, const pa_batch *batch, const void
     e = launch_merge(q_dtype, pool->head_dim, m, s);
     if (e != hipSuccess) return hip_fail(e, "k_merge launch");
   }
-  if (!plan.ext.empty()) {
-    ExtendArgs x{};
-    x.q = query;
-    x.out = output;
-    x.k_cache = pool->k_cache;
-    x.v_cache = pool->v_cache;
-    x.block_table = batch->block_table;
-    x.items = (const ExtendItem *)(ws + plan.off_ext);
-    x.n_items = (int32_t)plan.ext.size();
-    x.bt_stride = batch->bt_stride;
-    x.num_blocks = pool->num_blocks;
-    x.num_kv_heads = pool->num_kv_heads;
-    x.num_q_heads = num_q_heads;
-    x.g = g_total;
-    x.causal = causal ? 1 : 0;
-    x.scale_log2 = softmax_scale * log2e * kscale;
-    x.k_scale = kscale;
-    x.v_scale = vscale;
-    e = launch_extend(*pool, x, s);
-    if (e != hipSuccess) return hip_fail(e, "k_extend launch");
+  if (fork) {
+    if ((e = hipEventRecord(side->join, xs)) != hipSuccess) return hip_fail(e, "join record");
+    if ((e = hipStreamWaitEvent(s, side->join, 0)) != hipSuccess) return hip_fail(e, "join wait");
   }
   return PA_OK;
 }

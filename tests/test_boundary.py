@@ -132,6 +132,8 @@ def test_attention_rejects_bad_arguments(B):
     assert _att(B, p, b, q_dtype=0) == 2                   # f32 q with bf16 pool
     assert _att(B, p, b, q_dtype=7) == 1
     assert _att(B, p, b, scale=float("inf")) == 1
+    assert _att(B, p, b, scale=0.0) == 1
+    assert _att(B, p, b, scale=-0.1) == 1
     assert _att(B, p, b, wsptr=0) == 3                     # no workspace
     assert _att(B, p, b, wsptr=0x10010) == 3               # misaligned workspace
     assert _att(B, p, b, ws=16) == 3                       # too small
