@@ -5,20 +5,35 @@
 // third walk-through path): every new token t of a request with seq_len L and
 // c new tokens attends causally over keys 0 .. L - c + t, read from the paged
 // pool through the block table (earlier chunks' history included), with a
-// softmax stabilised by the running maximum.
+// softmax stabilised by a running maximum.
 //
-// Work decomposition (gfx950): a workgroup (4 waves) owns 128 "columns" of one
-// (request, kv head); column k is query row (token k / g, head k % g), so the
-// GQA heads that share a kv head share every K/V tile.  The workgroup walks
-// 64-key tiles; each tile is gathered from 4 pool blocks into LDS (K as
-// [key][dim], V as [dim][key] -- the V tile is already dimension-major in the
-// pool, so no transpose is needed), double-buffered so the next tile's loads
-// overlap this tile's math.  Each wave owns 32 columns and computes
-//   S^T (64 keys x 32 cols) = K (64 x 128) . Q^T (128 x 32)
+// Work decomposition (gfx950).  A workgroup of 8 waves owns 256 "columns"
+// of one (request, kv head); column k is query row (token k / g, head k % g),
+// so the GQA heads that share a kv head share every K/V tile.  It walks
+// 64-key tiles.  Each tile is copied from 4 pool blocks straight into LDS
+// with the direct global->LDS load (no staging registers) into a 4-stage
+// ring, so up to three tiles are in flight while one is computed.  Each wave
+// owns 32 columns and computes
+//   S^T (64 keys x 32 cols)   = K (64 x 128) . Q^T (128 x 32)
 //   O^T (128 dims x 32 cols) += V^T (128 x 64) . P^T (64 x 32)
-// with v_mfma_f32_32x32x16_bf16.  Keeping the column index on the lane makes
-// the online softmax a per-lane affair (one exchange with lane^32 for the
-// max).  P is rounded to bf16 for the second product.
+// on v_mfma_f32_32x32x16_bf16; two waves share each SIMD, so one wave's
+// softmax overlaps the other's matrix work.  The column index stays on the
+// lane, so the online softmax needs one exchange with lane^32.  P is rounded
+// to bf16 for the second product.
+//
+// LDS layouts (per stage: K 16 KB + V^T 16 KB):
+//  K:   row r holds key swap_bits23(r) of the tile; its 16-byte chunk c sits
+//       in slot c ^ (r & 7).  The row permutation makes the MFMA output rows
+//       of one lane the keys 8*hsel .. 8*hsel+7 of each 16-key group, so the
+//       V operand below is one 16-byte read; the XOR spreads the rows read
+//       together over distinct banks.
+//  V^T: [tile block b][dim d][16 keys], 32 bytes per (b, d); the 16-byte
+//       half h (keys 8h .. 8h+7) sits at position h ^ ((d >> 2) & 1), so
+//       eight consecutive dims read together cover all banks.  Each block's
+//       part is a permutation of the pool's (block, head) V tile, so one
+//       1 KB copy instruction reads 1 KB of one pool tile.
+// The copy writes lane i's 16 bytes at base + 16 i, so each lane's source
+// address is chosen to produce these layouts.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -27,19 +42,58 @@ namespace pa {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kExtD = 128;
-constexpr int kTileKeys = 64;
-constexpr int kKPitch = kExtD * 2 + 16;        // bytes per key row of the K tile in LDS
-// bytes per dim row of the V tile in LDS: 136 = 34 banks, so the 16 rows read
-// together by an 8-byte LDS read land on 16 distinct bank pairs
-constexpr int kVPitch = kTileKeys * 2 + 8;
-constexpr int kKBytes = kTileKeys * kKPitch;   // 17408
-constexpr int kVBytes = kExtD * kVPitch;       // 18432
-constexpr int kBufBytes = kKBytes + kVBytes;
+constexpr int kXD = 128;                        // head dim
+constexpr int kXT = 64;                         // keys per tile
+constexpr int kXStages = 4;
+constexpr int kXKBytes = kXT * kXD * 2;         // 16 KB
+constexpr int kXStage = 2 * kXKBytes;           // K + V^T
+constexpr int kXLds = kXStages * kXStage;       // 128 KB
+constexpr int kXTileB = kXD * kBlock * 2;       // pool bytes of one (block, head) tile
+static_assert(kExtCols == 256, "8 waves x 32 columns");
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+// byte offset of (dim d, tile key k) in the LDS V^T tile
+__device__ __forceinline__ int vt_offset(int d, int k) {
+  return (k >> 4) * 4096 + d * 32 + ((((k >> 3) & 1) ^ ((d >> 2) & 1)) * 16) + (k & 7) * 2;
+}
 
-__global__ __launch_bounds__(256, 2) void k_extend(const ExtendArgs a) {
+// 16 bytes per lane from base + off (global) to LDS at lds_base + 16 * lane;
+// base and lds_base are wave-uniform.  Written as inline asm so that the
+// compiler does not see an LDS write and does not drain every copy in flight
+// before the next LDS read: completion is handled explicitly (s_waitcnt
+// vmcnt + barrier) by the caller.  m0 (the LDS base of the copy) is saved and
+// restored; one wait state separates the m0 write from the copy (gfx9 hazard).
+__device__ __forceinline__ void copy16_to_lds(const char *base, uint32_t off, char *lds_base) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds_base;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(off), "s"(base)
+      : "memory");
+}
+
+// Uniform load through the scalar data path (read-only data).
+__device__ __forceinline__ int32_t load_uniform(const int32_t *p) {
+  return *(const __attribute__((address_space(4))) int32_t *)p;
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding; expcnt left free).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | (((N >> 4) & 3) << 14));
+}
+
+// Workgroup barrier that leaves outstanding vector loads in flight (the
+// compiler's __syncthreads waits for every copy first).
+__device__ __forceinline__ void barrier_keep_loads() { asm volatile("s_barrier" ::: "memory"); }
+
+__global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -49,87 +103,76 @@ __global__ __launch_bounds__(256, 2) void k_extend(const ExtendArgs a) {
   const int c = uniform(item.c), L = uniform(item.L), col0 = uniform(item.col0);
   const int g = a.g;
   const int ncols = c * g;
-  const int hist = L - c;                       // tokens before this step's first new token
+  const int hist = L - c;                        // tokens before this step's first new token
+  const int hsel = lane >> 5;                    // which 8-element k group the lane feeds
 
-  // key range of the workgroup and of this wave
+  // key range of the workgroup and of this wave (columns are token-major)
   const int last_col_wg = min(ncols, col0 + kExtCols) - 1;
   const int kend_wg = a.causal ? hist + last_col_wg / g + 1 : L;
-  const int last_col_w = min(ncols, col0 + wave * 32 + 32) - 1;
-  const bool wave_active = col0 + wave * 32 < ncols;
-  const int kend_w = a.causal ? hist + last_col_w / g + 1 : L;
-  const int n_tiles = (kend_wg + kTileKeys - 1) / kTileKeys;
+  const int n_tiles = (kend_wg + kXT - 1) / kXT;
+  const int blk_last = (kend_wg - 1) / kBlock;   // last logical block read
+  const int wcol0 = col0 + wave * 32;
+  const bool wave_active = wcol0 < ncols;
+  const int kend_w = a.causal ? hist + (min(ncols, wcol0 + 32) - 1) / g + 1 : L;
+  const int wave_min_nvis = a.causal ? hist + min(wcol0, ncols - 1) / g + 1 : L;
 
   // this lane's column (clamped to a valid one; invalid columns are not stored)
-  const int col_raw = col0 + wave * 32 + (lane & 31);
+  const int col_raw = wcol0 + (lane & 31);
   const bool col_ok = col_raw < ncols;
   const int col = col_ok ? col_raw : ncols - 1;
   const int t = col / g, hg = col - t * g;
-  const int nvis = a.causal ? hist + t + 1 : L;  // visible keys of this column
-  const int hsel = lane >> 5;                    // which 8-element k group the lane feeds
-  // visible keys of the wave's first column (columns are token-major, so the
-  // smallest); tiles below it need no causal mask
-  const int wave_first_col = min(col0 + wave * 32, ncols - 1);
-  const int wave_min_nvis = a.causal ? hist + wave_first_col / g + 1 : L;
+  const int nvis = a.causal ? hist + t + 1 : L;
 
-  // Q^T operand: 8 k-steps of 16 dims; lane holds dims 16ks + 8 hsel .. +8
-  const uint16_t *qrow = (const uint16_t *)a.q + ((int64_t)(tok0 + t) * a.num_q_heads + kvh * g + hg) * kExtD;
+  // Q^T operand: the lane holds dims 16 ks + 8 hsel .. +8 of its column
+  const uint16_t *qrow = (const uint16_t *)a.q + ((int64_t)(tok0 + t) * a.num_q_heads + kvh * g + hg) * kXD;
   bf16x8_t qop[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) qop[ks] = as_bf16x8(*(const uint4 *)(qrow + ks * 16 + hsel * 8));
+  // Wait for Q here: the compiler does not count the copies issued below, so
+  // a later wait for Q would be vmcnt(0) and drain the copy ring.
+  asm volatile("" ::"v"(qop[0]), "v"(qop[1]), "v"(qop[2]), "v"(qop[3]), "v"(qop[4]), "v"(qop[5]),
+               "v"(qop[6]), "v"(qop[7]));
 
   const int32_t *btrow = a.block_table + (int64_t)req * a.bt_stride;
-  const char *kpool = (const char *)a.k_cache;
-  const char *vpool = (const char *)a.v_cache;
-  constexpr int TILE = kExtD * kBlock * 2;       // bytes per (block, head) tile
+  const char *kpool = (const char *)a.k_cache + (int64_t)kvh * kXTileB;
+  const char *vpool = (const char *)a.v_cache + (int64_t)kvh * kXTileB;
+  const int64_t bstride = (int64_t)a.num_kv_heads * kXTileB;
 
-  // ---- staging: thread owns 4 K pieces and 4 V pieces (16 B each) per tile ----
-  uint4 kst[4], vst[4];
-  auto load_tile = [&](int kt) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int p = tid + 256 * r;               // piece index 0..1023
-      const int b = p >> 8;                      // block within the tile
-      const int kpos_blk = kt * kTileKeys + b * kBlock;
-      int phys = -1;
-      if (kpos_blk < kend_wg) phys = btrow[kpos_blk / kBlock];
-      if (phys >= a.num_blocks) phys = -1;
-      const int w = p & 255;
-      if (phys >= 0) {
-        const int64_t tile_off = ((int64_t)phys * a.num_kv_heads + kvh) * TILE;
-        kst[r] = *(const uint4 *)(kpool + tile_off + w * 16);     // chunk w/16, key w%16
-        uint4 v = *(const uint4 *)(vpool + tile_off + w * 16);    // dim w/2, keys 8(w%2)..+8
-        const int key0 = kpos_blk + (w & 1) * 8;
-        if (key0 + 8 > kend_wg) {                  // unwritten slots may hold anything
-          uint32_t vw[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t lo = (key0 + 2 * q < kend_wg) ? (vw[q] & 0xffffu) : 0u;
-            const uint32_t hi = (key0 + 2 * q + 1 < kend_wg) ? (vw[q] & 0xffff0000u) : 0u;
-            vw[q] = lo | hi;
-          }
-          v = make_uint4(vw[0], vw[1], vw[2], vw[3]);
-        }
-        vst[r] = v;
-      } else {
-        kst[r] = make_uint4(0, 0, 0, 0);
-        vst[r] = make_uint4(0, 0, 0, 0);
-      }
-    }
+  // Block id of logical block b (uniform).  Blocks past the range repeat the
+  // last one and ids outside the pool read block 0: both in bounds, and every
+  // key taken from them is masked (K) or zeroed (V) below.
+  auto blk_id = [&](int b) -> int {
+    const int v = load_uniform(btrow + min(b, blk_last));
+    return (v >= 0 && v < a.num_blocks) ? v : 0;
   };
-  auto store_tile = [&](int buf) {
-    char *kb = smem + buf * kBufBytes;
-    char *vb = kb + kKBytes;
+  // This wave's copy share: tile block w / 2, and within it K rows
+  // 8 w + 4 u .. +3 and V^T dims 32 (2 w + u) % 128 .. +31 for u = 0, 1, each
+  // instruction moving 1 KB of LDS.  Per-lane source offsets within the pool
+  // tile of a (block, head):
+  uint32_t koff[2], voff[2];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int p = tid + 256 * r;
-      const int b = p >> 8, w = p & 255;
-      const int kc = w >> 4, kk = w & 15;        // K: chunk, key in block
-      *(uint4 *)(kb + (b * kBlock + kk) * kKPitch + kc * 16) = kst[r];
-      const int vd = w >> 1, vh = w & 1;         // V: dim, key half
-      uint2 *vdst = (uint2 *)(vb + vd * kVPitch + (b * kBlock + vh * 8) * 2);  // 8-byte aligned rows
-      vdst[0] = make_uint2(vst[r].x, vst[r].y);
-      vdst[1] = make_uint2(vst[r].z, vst[r].w);
+  for (int u = 0; u < 2; ++u) {
+    const int I = wave * 2 + u;
+    const int rho = 4 * I + (lane >> 4);
+    const int chunk = (lane & 15) ^ (rho & 7);
+    koff[u] = chunk * 256 + (swap23(rho) & 15) * 16;
+    const int d = 32 * (I & 3) + (lane >> 1);
+    const int half = (lane & 1) ^ ((d >> 2) & 1);
+    voff[u] = d * 32 + half * 16;
+  }
+  const int my_blk = wave >> 1;
+  int next_id = blk_id(my_blk);                  // block id for the next tile to issue
+  auto issue = [&](int kt) {
+    char *kst = smem + (kt % kXStages) * kXStage + wave * 2048;
+    char *vst = kst + kXKBytes;
+    const char *ksrc = kpool + (int64_t)next_id * bstride;
+    const char *vsrc = vpool + (int64_t)next_id * bstride;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      copy16_to_lds(ksrc, koff[u], kst + u * 1024);
+      copy16_to_lds(vsrc, voff[u], vst + u * 1024);
     }
+    next_id = blk_id((kt + 1) * 4 + my_blk);
   };
 
   f32x16_t oacc[4];
@@ -139,101 +182,114 @@ __global__ __launch_bounds__(256, 2) void k_extend(const ExtendArgs a) {
     for (int r = 0; r < 16; ++r) oacc[md][r] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  // prologue: tiles 0 .. kXStages - 2 in flight
+  int issued = 0;
+  for (; issued < kXStages - 1 && issued < n_tiles; ++issued) issue(issued);
 
   for (int kt = 0; kt < n_tiles; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < n_tiles) load_tile(kt + 1);     // global loads in flight during the math
+    // This wave's copies of tile kt have landed once at most 4 per later
+    // issued tile are outstanding; the barrier then makes every wave's
+    // copies visible and guarantees that stage (kt - 1) % 4, refilled
+    // below, is no longer read.
+    const int later = issued - kt - 1;
+    if (later >= 2) wait_vm_lgkm0<8>();
+    else if (later == 1) wait_vm_lgkm0<4>();
+    else wait_vm_lgkm0<0>();
+    barrier_keep_loads();
+    if (issued < n_tiles) issue(issued++);
+    const int st = kt % kXStages;
+    const char *kb = smem + st * kXStage;
+    char *vb = smem + st * kXStage + kXKBytes;
+    const int kbase = kt * kXT;
+    if (kbase + kXT > kend_wg) {
+      // Last tile: keys past the range may hold anything (unwritten slots,
+      // stand-in blocks); zero their V so that 0 * v stays 0.  No copy is
+      // outstanding any more, so the full barrier costs nothing.
+      const int kv = kend_wg - kbase;
+      for (int e = tid; e < kXD * kXT; e += 512) {
+        const int d = e >> 6, k = e & 63;
+        if (k >= kv) *(uint16_t *)(vb + vt_offset(d, k)) = 0;
+      }
+      __syncthreads();
+    }
+    if (!wave_active || kbase >= kend_w) continue;
 
-    const int kbase = kt * kTileKeys;
-    if (wave_active && kbase < kend_w) {
-      const char *kb = smem + buf * kBufBytes;
-      const char *vb = kb + kKBytes;
-      // ---- S^T = K . Q^T ----
-      f32x16_t sacc[2];
+    // ---- S^T = K . Q^T ----
+    f32x16_t sacc[2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+    for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.0f;
-        const char *krow = kb + (mt * 32 + (lane & 31)) * kKPitch + hsel * 16;
+      for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.0f;
+      const int rho = mt * 32 + (lane & 31);
+      const char *krow = kb + rho * 256;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const bf16x8_t aop = as_bf16x8(*(const uint4 *)(krow + ks * 32));
-          sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, qop[ks], sacc[mt], 0, 0, 0);
-        }
-      }
-      // ---- online softmax over this tile (column = lane & 31) ----
-      // Scores stay unscaled until the exponent (scale > 0 commutes with max);
-      // keys past a column's causal limit are masked only on tiles that cross
-      // some column's limit.  The reference max m_ref is raised only when a
-      // column's maximum exceeds it by more than 2^8 (decided for the whole
-      // wave), so O and l are rescaled rarely; exp2(s*c - m_ref) <= 2^8 stays
-      // well inside bf16 and fp32, and O / l is unchanged by the choice of
-      // reference.
-      const bool crosses = kbase + kTileKeys > wave_min_nvis;
-      float mt_max = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float sv = sacc[mt][r];
-          if (crosses) {
-            const int key = kbase + mt * 32 + 8 * (r >> 2) + 4 * hsel + (r & 3);
-            sv = key < nvis ? sv : -INFINITY;
-            sacc[mt][r] = sv;
-          }
-          mt_max = fmaxf(mt_max, sv);
-        }
-      mt_max = fmaxf(mt_max, __shfl_xor(mt_max, 32, 64));
-      const float cand = mt_max * a.scale_log2;      // this tile's max, log2 units
-      const bool raise = cand > m_run + 8.0f;
-      if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform: rescale
-        const float m_new = raise ? cand : m_run;
-        const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int md = 0; md < 4; ++md)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[md][r] *= alpha;
-        m_run = m_new;
-      }
-      const float neg_m = m_run == -INFINITY ? 0.0f : -m_run;  // fully masked column: p = 0
-      float psum = 0.0f;
-      uint32_t pp[2][8];                          // P^T as bf16 pairs, [mt][r/2]
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[mt][r], a.scale_log2, neg_m));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[mt][r + 1], a.scale_log2, neg_m));
-          psum += p0 + p1;
-          pp[mt][r >> 1] = pack_bf16x2(p0, p1);
-        }
-      l_run += psum;
-      // ---- O^T += V^T . P^T ----
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int mt = ks >> 1, half = ks & 1;
-        const uint4 pb = make_uint4(pp[mt][half * 4 + 0], pp[mt][half * 4 + 1], pp[mt][half * 4 + 2],
-                                    pp[mt][half * 4 + 3]);
-        const bf16x8_t bop = as_bf16x8(pb);
-#pragma unroll
-        for (int md = 0; md < 4; ++md) {
-          const char *vrow = vb + (md * 32 + (lane & 31)) * kVPitch + (ks * 16 + 4 * hsel) * 2;
-          const uint2 lo = *(const uint2 *)vrow;          // keys 16ks + 4h + 0..3
-          const uint2 hi = *(const uint2 *)(vrow + 16);   // keys 16ks + 8 + 4h + 0..3
-          const bf16x8_t aop = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-          oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, oacc[md], 0, 0, 0);
-        }
+      for (int ks = 0; ks < 8; ++ks) {
+        const int chunk = 2 * ks + hsel;
+        const bf16x8_t aop = as_bf16x8(*(const uint4 *)(krow + ((chunk ^ (rho & 7)) * 16)));
+        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, qop[ks], sacc[mt], 0, 0, 0);
       }
     }
-    if (kt + 1 < n_tiles) {
-      // buf ^ 1 was last read in the previous iteration, which every wave
-      // finished before that iteration's closing barrier
-      store_tile(buf ^ 1);
-      __syncthreads();
+
+    // ---- online softmax (column = lane % 32) ----
+    // Scores stay unscaled until the exponent (scale > 0 commutes with max);
+    // the causal mask is applied only on tiles that cross some column's limit.
+    // The reference max is raised only when a column's maximum exceeds it by
+    // more than 2^8 (decided for the whole wave), so O and l are rescaled
+    // rarely; exp2(s * c - m_ref) <= 2^8 stays well inside bf16 and fp32, and
+    // O / l does not depend on the reference.
+    const bool crosses = kbase + kXT > wave_min_nvis;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float sv = sacc[mt][r];
+        if (crosses) {
+          const int key = kbase + swap23(mt * 32 + 8 * (r >> 2) + 4 * hsel + (r & 3));
+          sv = key < nvis ? sv : -INFINITY;
+          sacc[mt][r] = sv;
+        }
+        mx = fmaxf(mx, sv);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float cand = mx * a.scale_log2;
+    const bool raise = cand > m_run + 8.0f;
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      const float m_new = raise ? cand : m_run;
+      const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int md = 0; md < 4; ++md)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[md][r] *= alpha;
+      m_run = m_new;
+    }
+    const float neg_m = m_run == -INFINITY ? 0.0f : -m_run;  // fully masked column: p = 0
+    float psum = 0.0f;
+    uint32_t pp[2][8];                           // P^T as bf16 pairs [mt][r / 2]
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[mt][r], a.scale_log2, neg_m));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[mt][r + 1], a.scale_log2, neg_m));
+        psum += p0 + p1;
+        pp[mt][r >> 1] = pack_bf16x2(p0, p1);
+      }
+    l_run += psum;
+
+    // ---- O^T += V^T . P^T (k-step ks covers keys 16 ks .. 16 ks + 15) ----
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int mt = ks >> 1, half = ks & 1;
+      const bf16x8_t bop = as_bf16x8(make_uint4(pp[mt][half * 4 + 0], pp[mt][half * 4 + 1],
+                                                pp[mt][half * 4 + 2], pp[mt][half * 4 + 3]));
+#pragma unroll
+      for (int md = 0; md < 4; ++md) {                // keys 16 ks + 8 hsel .. +8 of dim d
+        const int d = md * 32 + (lane & 31);
+        const bf16x8_t aop = as_bf16x8(*(const uint4 *)(vb + vt_offset(d, 16 * ks + 8 * hsel)));
+        oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, oacc[md], 0, 0, 0);
+      }
     }
   }
 
@@ -241,7 +297,7 @@ __global__ __launch_bounds__(256, 2) void k_extend(const ExtendArgs a) {
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (!col_ok) return;
   const float inv = 1.0f / l_tot;
-  uint16_t *orow = (uint16_t *)a.out + ((int64_t)(tok0 + t) * a.num_q_heads + kvh * g + hg) * kExtD;
+  uint16_t *orow = (uint16_t *)a.out + ((int64_t)(tok0 + t) * a.num_q_heads + kvh * g + hg) * kXD;
 #pragma unroll
   for (int md = 0; md < 4; ++md)
 #pragma unroll
@@ -255,16 +311,15 @@ __global__ __launch_bounds__(256, 2) void k_extend(const ExtendArgs a) {
 
 hipError_t launch_extend(const pa_kv_pool &p, const ExtendArgs &a, hipStream_t s) {
   if (a.n_items == 0) return hipSuccess;
-  if (p.kv_dtype != PA_BF16 || p.head_dim != kExtD) return hipErrorNotSupported;
+  if (p.kv_dtype != PA_BF16 || p.head_dim != kXD) return hipErrorNotSupported;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)k_extend, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       2 * kBufBytes);
+    hipError_t e = hipFuncSetAttribute((const void *)k_extend, hipFuncAttributeMaxDynamicSharedMemorySize, kXLds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   prof_begin("k_extend", s);
-  hipLaunchKernelGGL(k_extend, dim3(a.n_items), dim3(256), 2 * kBufBytes, s, a);
+  hipLaunchKernelGGL(k_extend, dim3(a.n_items), dim3(512), kXLds, s, a);
   prof_end(s);
   return hipGetLastError();
 }
