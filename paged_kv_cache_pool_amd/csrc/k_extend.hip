@@ -23,15 +23,17 @@
 //
 // LDS layouts (per stage: K 16 KB + V^T 16 KB):
 //  K:   row r holds key swap_bits23(r) of the tile; its 16-byte chunk c sits
-//       in slot c ^ (r & 7).  The row permutation makes the MFMA output rows
+//       in slot c ^ (r & 15).  The row permutation makes the MFMA output rows
 //       of one lane the keys 8*hsel .. 8*hsel+7 of each 16-key group, so the
-//       V operand below is one 16-byte read; the XOR spreads the rows read
-//       together over distinct banks.
+//       V operand below is one 16-byte read.
 //  V^T: [tile block b][dim d][16 keys], 32 bytes per (b, d); the 16-byte
-//       half h (keys 8h .. 8h+7) sits at position h ^ ((d >> 2) & 1), so
-//       eight consecutive dims read together cover all banks.  Each block's
-//       part is a permutation of the pool's (block, head) V tile, so one
-//       1 KB copy instruction reads 1 KB of one pool tile.
+//       half h (keys 8h .. 8h+7) sits at position h ^ ((d >> 2) ^ (d >> 3)) & 1.
+//       Each block's part is a permutation of the pool's (block, head) V
+//       tile, so one 1 KB copy instruction reads 1 KB of one pool tile.
+// A 16-byte LDS read is served 16 lanes at a time over 64 four-byte banks;
+// both swizzles put the 16 rows that one pass reads on distinct banks (on
+// gfx950 a conflict-free read of 1 KB takes about 5 clocks, a two-way
+// conflicted one 8).
 // The copy writes lane i's 16 bytes at base + 16 i, so each lane's source
 // address is chosen to produce these layouts.
 #include "pa_device.h"
@@ -49,13 +51,14 @@ constexpr int kXKBytes = kXT * kXD * 2;         // 16 KB
 constexpr int kXStage = 2 * kXKBytes;           // K + V^T
 constexpr int kXLds = kXStages * kXStage;       // 128 KB
 constexpr int kXTileB = kXD * kBlock * 2;       // pool bytes of one (block, head) tile
-static_assert(kExtCols == 256, "8 waves x 32 columns");
+static_assert(kExtCols == 128, "4 column blocks of 32, each split over two waves");
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
-// byte offset of (dim d, tile key k) in the LDS V^T tile
+// half-row swizzle of dim d in the LDS V^T tile, and byte offset of (dim d, tile key k)
+__device__ __forceinline__ int vt_swz(int d) { return ((d >> 2) ^ (d >> 3)) & 1; }
 __device__ __forceinline__ int vt_offset(int d, int k) {
-  return (k >> 4) * 4096 + d * 32 + ((((k >> 3) & 1) ^ ((d >> 2) & 1)) * 16) + (k & 7) * 2;
+  return (k >> 4) * 4096 + d * 32 + ((((k >> 3) & 1) ^ vt_swz(d)) * 16) + (k & 7) * 2;
 }
 
 // 16 bytes per lane from base + off (global) to LDS at lds_base + 16 * lane;
@@ -111,7 +114,9 @@ __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
   const int kend_wg = a.causal ? hist + last_col_wg / g + 1 : L;
   const int n_tiles = (kend_wg + kXT - 1) / kXT;
   const int blk_last = (kend_wg - 1) / kBlock;   // last logical block read
-  const int wcol0 = col0 + wave * 32;
+  const int grp = wave >> 2;                     // key-split group: even (0) or odd (1) tiles
+  const int cw = wave & 3;                       // column block within the workgroup
+  const int wcol0 = col0 + cw * 32;
   const bool wave_active = wcol0 < ncols;
   const int kend_w = a.causal ? hist + (min(ncols, wcol0 + 32) - 1) / g + 1 : L;
   const int wave_min_nvis = a.causal ? hist + min(wcol0, ncols - 1) / g + 1 : L;
@@ -154,10 +159,10 @@ __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
   for (int u = 0; u < 2; ++u) {
     const int I = wave * 2 + u;
     const int rho = 4 * I + (lane >> 4);
-    const int chunk = (lane & 15) ^ (rho & 7);
+    const int chunk = (lane & 15) ^ (rho & 15);
     koff[u] = chunk * 256 + (swap23(rho) & 15) * 16;
     const int d = 32 * (I & 3) + (lane >> 1);
-    const int half = (lane & 1) ^ ((d >> 2) & 1);
+    const int half = (lane & 1) ^ vt_swz(d);
     voff[u] = d * 32 + half * 16;
   }
   const int my_blk = wave >> 1;
@@ -182,75 +187,56 @@ __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
     for (int r = 0; r < 16; ++r) oacc[md][r] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
-  // prologue: tiles 0 .. kXStages - 2 in flight
-  int issued = 0;
-  for (; issued < kXStages - 1 && issued < n_tiles; ++issued) issue(issued);
-
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    // This wave's copies of tile kt have landed once at most 4 per later
-    // issued tile are outstanding; the barrier then makes every wave's
-    // copies visible and guarantees that stage (kt - 1) % 4, refilled
-    // below, is no longer read.
-    const int later = issued - kt - 1;
-    if (later >= 2) wait_vm_lgkm0<8>();
-    else if (later == 1) wait_vm_lgkm0<4>();
-    else wait_vm_lgkm0<0>();
-    barrier_keep_loads();
-    if (issued < n_tiles) issue(issued++);
-    const int st = kt % kXStages;
-    const char *kb = smem + st * kXStage;
-    char *vb = smem + st * kXStage + kXKBytes;
-    const int kbase = kt * kXT;
-    if (kbase + kXT > kend_wg) {
-      // Last tile: keys past the range may hold anything (unwritten slots,
-      // stand-in blocks); zero their V so that 0 * v stays 0.  No copy is
-      // outstanding any more, so the full barrier costs nothing.
-      const int kv = kend_wg - kbase;
-      for (int e = tid; e < kXD * kXT; e += 512) {
-        const int d = e >> 6, k = e & 63;
-        if (k >= kv) *(uint16_t *)(vb + vt_offset(d, k)) = 0;
-      }
-      __syncthreads();
-    }
-    if (!wave_active || kbase >= kend_w) continue;
-
-    // ---- S^T = K . Q^T ----
+  // One 64-key tile for this wave's 32 columns: S^T = K . Q^T, online
+  // softmax, O^T += V^T . P^T.  `mask` (wave-uniform) applies the causal
+  // limit of each column; it is set only on tiles that cross some column's
+  // limit (the last one or two of a wave).
+  auto tile = [&](const char *kb, const char *vb, int kbase, bool mask) __attribute__((always_inline)) {
     f32x16_t sacc[2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.0f;
-      const int rho = mt * 32 + (lane & 31);
-      const char *krow = kb + rho * 256;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {             // the two chains alternate
+        const int rho = mt * 32 + (lane & 31);
         const int chunk = 2 * ks + hsel;
-        const bf16x8_t aop = as_bf16x8(*(const uint4 *)(krow + ((chunk ^ (rho & 7)) * 16)));
+        const bf16x8_t aop = as_bf16x8(*(const uint4 *)(kb + rho * 256 + ((chunk ^ (rho & 15)) * 16)));
         sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, qop[ks], sacc[mt], 0, 0, 0);
       }
+    // Schedule: four LDS operand reads ahead, then alternate one MFMA and
+    // one read, so each read has about four MFMAs (~128 clocks) to land.
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 
-    // ---- online softmax (column = lane % 32) ----
-    // Scores stay unscaled until the exponent (scale > 0 commutes with max);
-    // the causal mask is applied only on tiles that cross some column's limit.
-    // The reference max is raised only when a column's maximum exceeds it by
-    // more than 2^8 (decided for the whole wave), so O and l are rescaled
-    // rarely; exp2(s * c - m_ref) <= 2^8 stays well inside bf16 and fp32, and
-    // O / l does not depend on the reference.
-    const bool crosses = kbase + kXT > wave_min_nvis;
+    // Online softmax (column = lane % 32).  Scores stay unscaled until the
+    // exponent (scale > 0 commutes with max).  The reference max is raised
+    // only when a column's maximum exceeds it by more than 2^8 (decided for
+    // the whole wave), so O and l are rescaled rarely; exp2(s * c - m_ref) <=
+    // 2^8 stays well inside bf16 and fp32, and O / l does not depend on the
+    // reference.
+    if (mask) {
+      const int lim = nvis - kbase;              // keys of this tile the column sees
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = swap23(mt * 32 + 8 * (r >> 2) + 4 * hsel + (r & 3));
+          sacc[mt][r] = key < lim ? sacc[mt][r] : -INFINITY;
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float sv = sacc[mt][r];
-        if (crosses) {
-          const int key = kbase + swap23(mt * 32 + 8 * (r >> 2) + 4 * hsel + (r & 3));
-          sv = key < nvis ? sv : -INFINITY;
-          sacc[mt][r] = sv;
-        }
-        mx = fmaxf(mx, sv);
-      }
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float cand = mx * a.scale_log2;
     const bool raise = cand > m_run + 8.0f;
@@ -278,7 +264,7 @@ __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
       }
     l_run += psum;
 
-    // ---- O^T += V^T . P^T (k-step ks covers keys 16 ks .. 16 ks + 15) ----
+    // O^T += V^T . P^T (k-step ks covers keys 16 ks .. 16 ks + 15)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int mt = ks >> 1, half = ks & 1;
@@ -291,21 +277,88 @@ __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
         oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, oacc[md], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+  };
+
+  // Tiles go in pairs (2p, 2p + 1): group 0 computes the even tile, group 1
+  // the odd one, for the same columns.  The ring holds two pairs: while pair
+  // p is computed, pair p + 1 is in flight.
+  const int n_pairs = (n_tiles + 1) / 2;
+  auto issue_pair = [&](int p) {
+    issue(2 * p);
+    if (2 * p + 1 < n_tiles) issue(2 * p + 1);
+  };
+  issue_pair(0);
+  for (int p = 0; p < n_pairs; ++p) {
+    // Only pair p's copies are outstanding: wait for them, then the barrier
+    // makes every wave's copies visible and guarantees that the stages of
+    // pair p - 1, refilled below, are no longer read.
+    wait_vm_lgkm0<0>();
+    barrier_keep_loads();
+    if (p + 1 < n_pairs) issue_pair(p + 1);
+    if (2 * p + 2 >= n_tiles) {
+      // Last pair: keys past the range may hold anything (unwritten slots,
+      // stand-in blocks); zero their V so that 0 * v stays 0.
+      const int tl = n_tiles - 1;
+      char *vb = smem + (tl % kXStages) * kXStage + kXKBytes;
+      const int kv = kend_wg - tl * kXT;
+      for (int e = tid; e < kXD * kXT; e += 512) {
+        const int d = e >> 6, k = e & 63;
+        if (k >= kv) *(uint16_t *)(vb + vt_offset(d, k)) = 0;
+      }
+      __syncthreads();
+    }
+    const int kt = 2 * p + grp;
+    const int kbase = kt * kXT;
+    if (kt >= n_tiles || !wave_active || kbase >= kend_w) continue;
+    const char *kb = smem + (kt % kXStages) * kXStage;
+    tile(kb, kb + kXKBytes, kbase, kbase + kXT > wave_min_nvis);
   }
 
-  if (!wave_active) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (!col_ok) return;
-  const float inv = 1.0f / l_tot;
+  // Merge the odd-tile partial (m, l, O) of each column into the even-tile
+  // one through LDS (the ring is free once every wave has passed the
+  // barrier).  Both are relative to their own reference maxima m_g:
+  //   O = O_0 2^(m_0 - m) + O_1 2^(m_1 - m),  l likewise,  m = max(m_0, m_1);
+  // m_0 is finite (tile 0, key 0 is visible to every column), m_1 may be
+  // -inf when the odd tiles hold no visible key.
+  const float l_half = l_run + __shfl_xor(l_run, 32, 64);
+  __syncthreads();
+  float *xo = (float *)smem;                     // [cw][md * 16 + r][lane]
+  float *xm = xo + 4 * 64 * 64;                  // [cw][lane]
+  float *xl = xm + 4 * 64;
+  if (grp == 1 && wave_active) {
+#pragma unroll
+    for (int md = 0; md < 4; ++md)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xo[(cw * 64 + md * 16 + r) * 64 + lane] = oacc[md][r];
+    xm[cw * 64 + lane] = m_run;
+    xl[cw * 64 + lane] = l_half;
+  }
+  __syncthreads();
+  if (grp == 1 || !wave_active || !col_ok) return;
+  const float m1 = xm[cw * 64 + lane];
+  const float m = fmaxf(m_run, m1);
+  const float a0 = __builtin_amdgcn_exp2f(m_run - m);
+  const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
+  const float inv = 1.0f / (l_half * a0 + xl[cw * 64 + lane] * a1);
+  const float s0 = a0 * inv, s1 = a1 * inv;
   uint16_t *orow = (uint16_t *)a.out + ((int64_t)(tok0 + t) * a.num_q_heads + kvh * g + hg) * kXD;
 #pragma unroll
   for (int md = 0; md < 4; ++md)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int dim = md * 32 + 8 * q + 4 * hsel;  // rows r = 4q .. 4q+3
-      const uint32_t w0 = pack_bf16x2(oacc[md][4 * q] * inv, oacc[md][4 * q + 1] * inv);
-      const uint32_t w1 = pack_bf16x2(oacc[md][4 * q + 2] * inv, oacc[md][4 * q + 3] * inv);
-      *(uint2 *)(orow + dim) = make_uint2(w0, w1);
+      float o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[i] = oacc[md][4 * q + i] * s0 + xo[(cw * 64 + md * 16 + 4 * q + i) * 64 + lane] * s1;
+      *(uint2 *)(orow + dim) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
     }
 }
 

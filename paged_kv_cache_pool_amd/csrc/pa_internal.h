@@ -100,7 +100,7 @@ struct ExtendArgs {
   float v_scale;
 };
 
-constexpr int kExtCols = 256;        // columns per extend workgroup (8 waves x 32)
+constexpr int kExtCols = 128;        // columns per extend workgroup (4 x 32, keys split over 2 waves)
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_slot_mapping(const pa_batch &b, int64_t *slots, int max_c, hipStream_t s);
