@@ -40,7 +40,123 @@ def parse():
                     help="target CPU time for the oracle baseline (0 disables it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for counter calibration) and exit")
+    ap.add_argument("--traffic-ingest", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
+                    help="turn four rocprofv3 --pmc output folders (FETCH_SIZE and WRITE_SIZE of "
+                         "this workload, then of --copy-calibration) into the traffic record of "
+                         "the dominant kernel under profiles/, and exit")
+    ap.add_argument("--kernel", default="k_decode", help="kernel for --traffic-ingest")
     return ap.parse_args()
+
+
+# Sources whose change invalidates a kernel's measured traffic.
+KERNEL_SOURCES = {
+    "k_decode": ["k_decode.hip", "pa_device.h", "pa_internal.h", "pa_api.hip"],
+    "k_extend": ["k_extend.hip", "pa_device.h", "pa_internal.h", "pa_api.hip"],
+}
+COPY_BYTES = 1 << 30
+
+
+def source_hash(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "paged_kv_cache_pool_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record_path(kernel, workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
+
+
+def _counter_per_dispatch(folder, counter, name_part):
+    """Mean of `counter` over the dispatches whose kernel name contains name_part."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {folder}")
+    vals = []
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+                    vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"{counter} for '{name_part}' not found under {folder}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def _largest_dispatch(folder, counter):
+    """Counter value of the dispatch reading/writing the most (the 1 GiB copy)."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    best = []
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    best.append(float(r["Counter_Value"]))
+    best.sort()
+    top = [v for v in best if v >= 0.5 * best[-1]]
+    return sum(top) / len(top)
+
+
+def traffic_ingest(a):
+    """Write the traffic record: KiB per dispatch from FETCH_SIZE / WRITE_SIZE,
+    each scaled by (bytes a plain 1 GiB copy moves) / (bytes the same counter
+    reports for it)."""
+    from paged_kv_cache_pool_amd import workloads as W
+    fetch_dir, write_dir, cal_fetch_dir, cal_write_dir = a.traffic_ingest
+    fetch_kib, n_f = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", a.kernel)
+    write_kib, n_w = _counter_per_dispatch(write_dir, "WRITE_SIZE", a.kernel)
+    cal_fetch = COPY_BYTES / (1024.0 * _largest_dispatch(cal_fetch_dir, "FETCH_SIZE"))
+    cal_write = COPY_BYTES / (1024.0 * _largest_dispatch(cal_write_dir, "WRITE_SIZE"))
+    read_b = fetch_kib * 1024.0 * cal_fetch
+    write_b = write_kib * 1024.0 * cal_write
+    w = W.make(a.config, a.seed)
+    rec = {"kernel": a.kernel, "workload": w.name, "source_sha": source_hash(a.kernel),
+           "fetch_kib_per_dispatch": round(fetch_kib, 1), "write_kib_per_dispatch": round(write_kib, 1),
+           "dispatches": [n_f, n_w], "copy_factor_fetch": round(cal_fetch, 4),
+           "copy_factor_write": round(cal_write, 4), "hbm_bytes_read": round(read_b),
+           "hbm_bytes_written": round(write_b), "hbm_bytes": round(read_b + write_b)}
+    cmd = f"python bench.py --config {a.config} --steps 5 --warmup 2 --cpu-seconds 0"
+    text = [f"# HBM traffic of {a.kernel}, workload {w.name}", "",
+            "Counters (one pass each, on the GPU box, from the repository root):", "",
+            "```",
+            f"rocprofv3 --pmc FETCH_SIZE -d <fetch> -o run --output-format csv -- {cmd}",
+            f"rocprofv3 --pmc WRITE_SIZE -d <write> -o run --output-format csv -- {cmd}",
+            "rocprofv3 --pmc FETCH_SIZE -d <cal_fetch> -o run --output-format csv -- python bench.py --copy-calibration",
+            "rocprofv3 --pmc WRITE_SIZE -d <cal_write> -o run --output-format csv -- python bench.py --copy-calibration",
+            f"python bench.py --config {a.config} --kernel {a.kernel} --traffic-ingest <fetch> <write> <cal_fetch> <cal_write>",
+            "```", "",
+            f"FETCH_SIZE {fetch_kib:.1f} KiB and WRITE_SIZE {write_kib:.1f} KiB per dispatch "
+            f"(mean of {n_f} / {n_w} dispatches).  A plain copy of {COPY_BYTES} bytes reads "
+            f"{cal_fetch:.3f}x and writes {cal_write:.3f}x what the counters report, so the "
+            f"kernel moves {read_b / 1e6:.1f} MB read + {write_b / 1e6:.1f} MB written per launch.",
+            "bench.py reports this as roofline.traffic while the kernel's sources hash to "
+            "source_sha below.", "", "```json", json.dumps(rec), "```", ""]
+    path = traffic_record_path(a.kernel, w.name)
+    with open(path, "w") as fh:
+        fh.write("\n".join(text))
+    print(json.dumps(rec), flush=True)
+
+
+def load_traffic(kernel, workload):
+    """Measured HBM bytes per launch, or None when absent or taken on other sources."""
+    path = traffic_record_path(kernel, workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        body = fh.read()
+    try:
+        rec = json.loads(body.split("```json", 1)[1].split("```", 1)[0])
+    except (IndexError, ValueError):
+        return None
+    if rec.get("source_sha") != source_hash(kernel):
+        return None
+    return rec["hbm_bytes"]
 
 
 def algorithmic_work(w, seq_lens, qsl, ext_min_rows=16, extend_on=True):
@@ -68,6 +184,9 @@ def algorithmic_work(w, seq_lens, qsl, ext_min_rows=16, extend_on=True):
 
 def main():
     a = parse()
+    if a.traffic_ingest:
+        traffic_ingest(a)
+        return
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": a.gpus}), flush=True)
@@ -140,13 +259,13 @@ def main():
         achieved = dec_bytes / (kernels[dom]["avg_us"] * 1e-6) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": None, "algorithmic_bytes_per_launch": dec_bytes}
+                "traffic": load_traffic(dom, w.name), "algorithmic_bytes_per_launch": dec_bytes}
     else:
         dom = "k_extend"
         achieved = ext_flops / (kernels[dom]["avg_us"] * 1e-6) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": load_traffic(dom, w.name),
                 "algorithmic_flops_per_launch": ext_flops}
 
     cpu = None
