@@ -273,7 +273,7 @@ def main():
         import oracle as O
         pool = O.build_pool(w)
         reps, t_cpu = 0, 0.0
-        while t_cpu < a.cpu_seconds and reps < 50:
+        while t_cpu < a.cpu_seconds and reps < 1000:
             t1 = time.perf_counter()
             O.run_step(w, pool=pool)
             t_cpu += time.perf_counter() - t1
