@@ -45,6 +45,9 @@ def parse():
                          "this workload, then of --copy-calibration) into the traffic record of "
                          "the dominant kernel under profiles/, and exit")
     ap.add_argument("--kernel", default="k_decode", help="kernel for --traffic-ingest")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time steps that start with cold caches (a 1 GiB scratch read "
+                         "before each step, outside the timed events)")
     return ap.parse_args()
 
 
@@ -182,6 +185,22 @@ def algorithmic_work(w, seq_lens, qsl, ext_min_rows=16, extend_on=True):
     return dec_bytes, ext_flops, ext_bytes
 
 
+def unique_kv_bytes(w, seq_lens, qsl):
+    """K+V bytes of the distinct pool slots the decode rows read (a block shared
+    by several requests counts once): what HBM must deliver at least once."""
+    b_kv = ELEM[w.kv_dtype]
+    S = w.block_size
+    seen = {}
+    for i in range(w.num_seqs):
+        c, L = int(qsl[i + 1] - qsl[i]), int(seq_lens[i])
+        if c == 0:
+            continue
+        for b in range(-(-L // S)):
+            blk = int(w.block_table[i, b])
+            seen[blk] = max(seen.get(blk, 0), min(S, L - b * S))
+    return sum(seen.values()) * w.num_kv_heads * w.head_dim * 2 * b_kv
+
+
 def main():
     a = parse()
     if a.traffic_ingest:
@@ -238,14 +257,39 @@ def main():
             kernels[name] = {"launches": n, "avg_us": 1000.0 * ms / n}
     B.profile_enable(False)
 
-    # the same K steps without the per-kernel events (reported step time)
+    # the same K steps without the per-kernel events (reported step time);
+    # an event after every step gives the per-step spread
     torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(a.steps):
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
+    evs[0].record(stream)
+    for k in range(a.steps):
         step.run()
-    ev1.record(stream)
+        evs[k + 1].record(stream)
     torch.cuda.synchronize()
-    ms_per_step = ev0.elapsed_time(ev1) / a.steps
+    ms_per_step = evs[0].elapsed_time(evs[-1]) / a.steps
+    per_step = np.array([evs[k].elapsed_time(evs[k + 1]) for k in range(a.steps)])
+    spread = {"p10": round(float(np.percentile(per_step, 10)), 5),
+              "p50": round(float(np.percentile(per_step, 50)), 5),
+              "p90": round(float(np.percentile(per_step, 90)), 5)}
+    cold = None
+    if a.cold:
+        # each step starts after a 1 GiB read, so L2 and the 256 MB Infinity
+        # Cache hold none of its inputs (clean lines: no write-back is left
+        # for the step to pay); only the step is between its events
+        scratch = torch.ones(1 << 27, dtype=torch.int64, device="cuda")
+        times = []
+        for _ in range(a.steps):
+            scratch.max()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step.run()
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        cold = {"p10": round(float(np.percentile(times, 10)), 5),
+                "p50": round(float(np.percentile(times, 50)), 5),
+                "p90": round(float(np.percentile(times, 90)), 5)}
+        del scratch
 
     T = w.num_tokens
     tokens_per_s = T / (ms_per_step / 1000.0)
@@ -305,8 +349,16 @@ def main():
         "cpu_baseline": cpu,
         "kernels_us": {k: round(v["avg_us"], 2) for k, v in kernels.items()},
         "ms_per_step_with_kernel_events": round(ms_instr, 5),
+        "ms_per_step_spread": spread,
         "decode_kv_gbps": roof["achieved"] if roof["unit"] == "GB/s" else None,
     }
+    if cold is not None:
+        out["ms_per_step_cold"] = cold
+    if roof["unit"] == "GB/s":
+        uniq = unique_kv_bytes(w, sl, qsl)
+        out["decode_kv_bytes_logical"] = dec_bytes
+        out["decode_kv_bytes_unique"] = uniq
+        out["decode_kv_gbps_unique"] = round(uniq / (kernels["k_decode"]["avg_us"] * 1e-6) / 1e9, 1)
     if ext_flops:
         out["extend_tflops"] = round(ext_flops / (kernels["k_extend"]["avg_us"] * 1e-6) / 1e12, 1) \
             if "k_extend" in kernels else None
