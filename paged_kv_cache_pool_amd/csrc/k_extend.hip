@@ -123,20 +123,18 @@ __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
 
   // this lane's column (clamped to a valid one; invalid columns are not stored)
   const int col_raw = wcol0 + (lane & 31);
-  const bool col_ok = col_raw < ncols;
-  const int col = col_ok ? col_raw : ncols - 1;
-  const int t = col / g, hg = col - t * g;
+  const int col = min(col_raw, ncols - 1);
+  const int t = col / g;
   const int nvis = a.causal ? hist + t + 1 : L;
 
-  // Q^T operand: the lane holds dims 16 ks + 8 hsel .. +8 of its column
-  const uint16_t *qrow = (const uint16_t *)a.q + ((int64_t)(tok0 + t) * a.num_q_heads + kvh * g + hg) * kXD;
-  bf16x8_t qop[8];
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) qop[ks] = as_bf16x8(*(const uint4 *)(qrow + ks * 16 + hsel * 8));
-  // Wait for Q here: the compiler does not count the copies issued below, so
-  // a later wait for Q would be vmcnt(0) and drain the copy ring.
-  asm volatile("" ::"v"(qop[0]), "v"(qop[1]), "v"(qop[2]), "v"(qop[3]), "v"(qop[4]), "v"(qop[5]),
-               "v"(qop[6]), "v"(qop[7]));
+  // Output row (in units of head_dim elements) of workgroup column cc, clamped
+  // to a valid column.
+  auto out_row = [&](int cc) -> int64_t {
+    const int cg = min(col0 + cc, ncols - 1);
+    const int tt = cg / g;
+    return (int64_t)(tok0 + tt) * a.num_q_heads + kvh * g + (cg - tt * g);
+  };
+  bf16x8_t qop[8];                               // Q^T operand: dims 16 ks + 8 hsel .. +8 of the lane's column
 
   const int32_t *btrow = a.block_table + (int64_t)req * a.bt_stride;
   const char *kpool = (const char *)a.k_cache + (int64_t)kvh * kXTileB;
@@ -294,13 +292,37 @@ __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
     issue(2 * p);
     if (2 * p + 1 < n_tiles) issue(2 * p + 1);
   };
+  // Q of the workgroup's 128 columns is copied into stage 3 (free until pair
+  // 1 is issued) together with pair 0: row cc (256 bytes) holds column cc's
+  // 16-byte chunk c in slot c ^ (cc & 15), so the operand reads below are
+  // conflict-free.  Instruction u of wave w moves columns 4 (4 w + u) .. +3.
+  char *qst = smem + 3 * kXStage;
+  {
+    const char *qsrc = (const char *)a.q + (int64_t)out_row(0) * (kXD * 2);
+    const int64_t row0 = out_row(0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int J = wave * 4 + u;
+      const int cc = 4 * J + (lane >> 4);
+      const int chunk = (lane & 15) ^ (cc & 15);
+      copy16_to_lds(qsrc, (uint32_t)((out_row(cc) - row0) * (kXD * 2) + chunk * 16), qst + J * 1024);
+    }
+  }
   issue_pair(0);
   for (int p = 0; p < n_pairs; ++p) {
-    // Only pair p's copies are outstanding: wait for them, then the barrier
-    // makes every wave's copies visible and guarantees that the stages of
-    // pair p - 1, refilled below, are no longer read.
+    // Only pair p's copies (and, for p = 0, Q's) are outstanding: wait for
+    // them, then the barrier makes every wave's copies visible and
+    // guarantees that the stages of pair p - 1, refilled below, are no
+    // longer read.
     wait_vm_lgkm0<0>();
     barrier_keep_loads();
+    if (p == 0) {
+      const int cc = cw * 32 + (lane & 31);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        qop[ks] = as_bf16x8(*(const uint4 *)(qst + cc * 256 + (((2 * ks + hsel) ^ (cc & 15)) * 16)));
+      __syncthreads();                           // every wave has Q before stage 3 is refilled
+    }
     if (p + 1 < n_pairs) issue_pair(p + 1);
     if (2 * p + 2 >= n_tiles) {
       // Last pair: keys past the range may hold anything (unwritten slots,
@@ -341,25 +363,41 @@ __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
     xl[cw * 64 + lane] = l_half;
   }
   __syncthreads();
-  if (grp == 1 || !wave_active || !col_ok) return;
-  const float m1 = xm[cw * 64 + lane];
-  const float m = fmaxf(m_run, m1);
-  const float a0 = __builtin_amdgcn_exp2f(m_run - m);
-  const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
-  const float inv = 1.0f / (l_half * a0 + xl[cw * 64 + lane] * a1);
-  const float s0 = a0 * inv, s1 = a1 * inv;
-  uint16_t *orow = (uint16_t *)a.out + ((int64_t)(tok0 + t) * a.num_q_heads + kvh * g + hg) * kXD;
+  // The merged bf16 outputs are staged as [column][dims] rows (pitch 272
+  // bytes, so the 8-byte writes of 32 columns spread over the banks) and
+  // then written out as whole 256-byte rows.
+  constexpr int kOutPitch = kXD * 2 + 16;
+  char *ost = smem + 80 * 1024;
+  if (grp == 0 && wave_active) {
+    const float m1 = xm[cw * 64 + lane];
+    const float m = fmaxf(m_run, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m_run - m);
+    const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
+    const float inv = 1.0f / (l_half * a0 + xl[cw * 64 + lane] * a1);
+    const float s0 = a0 * inv, s1 = a1 * inv;
+    char *orow = ost + (cw * 32 + (lane & 31)) * kOutPitch;
 #pragma unroll
-  for (int md = 0; md < 4; ++md)
+    for (int md = 0; md < 4; ++md)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int dim = md * 32 + 8 * q + 4 * hsel;  // rows r = 4q .. 4q+3
-      float o[4];
+      for (int q = 0; q < 4; ++q) {
+        const int dim = md * 32 + 8 * q + 4 * hsel;  // rows r = 4q .. 4q+3
+        float o[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        o[i] = oacc[md][4 * q + i] * s0 + xo[(cw * 64 + md * 16 + 4 * q + i) * 64 + lane] * s1;
-      *(uint2 *)(orow + dim) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-    }
+        for (int i = 0; i < 4; ++i)
+          o[i] = oacc[md][4 * q + i] * s0 + xo[(cw * 64 + md * 16 + 4 * q + i) * 64 + lane] * s1;
+        *(uint2 *)(orow + dim * 2) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+      }
+  }
+  __syncthreads();
+  const int ncols_wg = min(kExtCols, ncols - col0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int piece = tid + 512 * i;             // column piece / 16, 16-byte chunk piece % 16
+    const int cc = piece >> 4, chunk = piece & 15;
+    if (cc < ncols_wg)
+      *(uint4 *)((char *)a.out + out_row(cc) * (kXD * 2) + chunk * 16) =
+          *(const uint4 *)(ost + cc * kOutPitch + chunk * 16);
+  }
 }
 
 hipError_t launch_extend(const pa_kv_pool &p, const ExtendArgs &a, hipStream_t s) {
