@@ -7,19 +7,24 @@
 // pool through the block table (earlier chunks' history included), with a
 // softmax stabilised by a running maximum.
 //
-// Work decomposition (gfx950).  A workgroup of 8 waves owns 256 "columns"
-// of one (request, kv head); column k is query row (token k / g, head k % g),
-// so the GQA heads that share a kv head share every K/V tile.  It walks
-// 64-key tiles.  Each tile is copied from 4 pool blocks straight into LDS
-// with the direct global->LDS load (no staging registers) into a 4-stage
-// ring, so up to three tiles are in flight while one is computed.  Each wave
-// owns 32 columns and computes
+// Work decomposition (gfx950).  A workgroup of 8 waves owns 128 "columns" of
+// one (request, kv head); column k is query row (token k / g, head k % g), so
+// the GQA heads that share a kv head share every K/V tile.  The keys are cut
+// into 64-key tiles (four pool blocks) taken in pairs: waves 0-3 compute the
+// even tile of each pair and waves 4-7 the odd one, for the same 4 x 32
+// columns, and the two partial (m, l, O) of a column are merged in LDS at the
+// end, so that the longest items of a causal chunk are half as long.  Each
+// wave computes, for its 32 columns,
 //   S^T (64 keys x 32 cols)   = K (64 x 128) . Q^T (128 x 32)
 //   O^T (128 dims x 32 cols) += V^T (128 x 64) . P^T (64 x 32)
-// on v_mfma_f32_32x32x16_bf16; two waves share each SIMD, so one wave's
-// softmax overlaps the other's matrix work.  The column index stays on the
-// lane, so the online softmax needs one exchange with lane^32.  P is rounded
-// to bf16 for the second product.
+// on v_mfma_f32_32x32x16_bf16.  The column index stays on the lane, so the
+// online softmax needs one exchange with lane^32.  P is rounded to bf16 for
+// the second product.
+//
+// Data movement.  Tiles are copied from the pool straight into LDS with the
+// direct global->LDS load (no staging registers) into a ring of two pairs
+// (128 KB): one pair is computed while the next is in flight.  Q of the 128
+// columns rides the first pair's copies.
 //
 // LDS layouts (per stage: K 16 KB + V^T 16 KB):
 //  K:   row r holds key swap_bits23(r) of the tile; its 16-byte chunk c sits
