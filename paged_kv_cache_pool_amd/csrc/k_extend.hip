@@ -41,6 +41,9 @@
 // conflicted one 8).
 // The copy writes lane i's 16 bytes at base + 16 i, so each lane's source
 // address is chosen to produce these layouts.
+#include <mutex>
+#include <vector>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -408,11 +411,21 @@ __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
 hipError_t launch_extend(const pa_kv_pool &p, const ExtendArgs &a, hipStream_t s) {
   if (a.n_items == 0) return hipSuccess;
   if (p.kv_dtype != PA_BF16 || p.head_dim != kXD) return hipErrorNotSupported;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)k_extend, hipFuncAttributeMaxDynamicSharedMemorySize, kXLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
+  // The LDS size above the default limit is a per-device attribute of the
+  // kernel: set it once for each device the library launches on.
+  static std::mutex mu;
+  static std::vector<char> attr_set;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    if ((int)attr_set.size() <= dev) attr_set.resize(dev + 1, 0);
+    if (!attr_set[dev]) {
+      e = hipFuncSetAttribute((const void *)k_extend, hipFuncAttributeMaxDynamicSharedMemorySize, kXLds);
+      if (e != hipSuccess) return e;
+      attr_set[dev] = 1;
+    }
   }
   prof_begin("k_extend", s);
   hipLaunchKernelGGL(k_extend, dim3(a.n_items), dim3(512), kXLds, s, a);

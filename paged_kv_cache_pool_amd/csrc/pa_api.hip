@@ -90,7 +90,8 @@ static void prof_reset_locked() {
 // The plan of a step (work lists) is built on the host and uploaded into the
 // caller's workspace.  Uploads go through pinned buffers so they are truly
 // asynchronous; a buffer is reused only after the copy that last read it has
-// completed (checked with an event).
+// completed (checked with an event).  One ring per device (events belong to
+// the device they were created on).
 
 struct StageSlot {
   void *host = nullptr;
@@ -100,14 +101,21 @@ struct StageSlot {
 };
 
 static std::mutex g_stage_mu;
-static std::vector<StageSlot> g_stage(8);
-static unsigned g_stage_next = 0;
+static std::vector<std::vector<StageSlot>> g_stage;   // per device: 8 slots
+static std::vector<unsigned> g_stage_next;
 
 static pa_status upload(void *dst, const void *src, size_t bytes, hipStream_t s) {
   if (bytes == 0) return PA_OK;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   std::lock_guard<std::mutex> lk(g_stage_mu);
-  StageSlot &slot = g_stage[g_stage_next++ % g_stage.size()];
-  hipError_t e;
+  if ((int)g_stage.size() <= dev) {
+    g_stage.resize(dev + 1);
+    g_stage_next.resize(dev + 1, 0);
+  }
+  if (g_stage[dev].empty()) g_stage[dev].resize(8);
+  StageSlot &slot = g_stage[dev][g_stage_next[dev]++ % g_stage[dev].size()];
   if (slot.pending) {
     if ((e = hipEventSynchronize(slot.done)) != hipSuccess) return hip_fail(e, "staging wait");
     slot.pending = false;

@@ -285,6 +285,25 @@ def test_attention_long_context_config_sampled(R):
     _check_attention(w, step, tokens=np.array([0, 3, 7], dtype=np.int32))
 
 
+def test_page_mixed_batch(R):
+    """The mixed batch the source-map page walks through ("vLLM 源码完全拆解（十六）",
+    fourth walk-through path): one decode row, a 256-token chunk and a 3-token
+    chunk, with 1024, 512 and 600 tokens already computed, so seq_lens =
+    [1025, 768, 603] and query_start_loc = [0, 1, 257, 260].  Every row of
+    the three paths (decode, MFMA extend, short chunk through the split-K
+    kernel) is compared with the oracle."""
+    say("page mixed batch")
+    w = W.build("page_mixed", 3, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                num_blocks=200, kv_dtype=W.BF16, io_dtype=W.BF16, num_computed=[1024, 512, 600],
+                num_scheduled=[1, 256, 3])
+    assert O.query_start_loc(w.num_scheduled).tolist() == [0, 1, 257, 260]
+    assert O.seq_lens(w.num_computed, w.num_scheduled).tolist() == [1025, 768, 603]
+    step = R.GpuStep(w)
+    step.run()
+    torch.cuda.synchronize()
+    _check_attention(w, step)
+
+
 # ------------------------------------------------------------ MFMA extend --
 
 @pytest.mark.parametrize("g", [1, 2, 4, 8])
