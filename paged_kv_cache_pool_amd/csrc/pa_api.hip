@@ -87,14 +87,17 @@ static void prof_reset_locked() {
 }
 
 // ------------------------------------------------------ pinned staging ring --
-// The plan of a step (work lists) is built on the host and uploaded into the
-// caller's workspace.  Uploads go through pinned buffers so they are truly
-// asynchronous; a buffer is reused only after the copy that last read it has
-// completed (checked with an event).  One ring per device (events belong to
-// the device they were created on).
+// The plan of a step (work lists) is built on the host.  It is written into
+// a pinned, device-mapped host buffer that the kernels read directly (one
+// small read per wave or workgroup), so no copy is queued between the
+// caller's previous kernel and ours.  A buffer is reused only after the last
+// kernel that reads it has completed (checked with an event).  With
+// PA_PLAN_UPLOAD=1 the plan is instead copied into the caller's workspace.
+// One ring per device (events belong to the device they were created on).
 
 struct StageSlot {
   void *host = nullptr;
+  void *dev = nullptr;                           // device address of `host`
   size_t cap = 0;
   hipEvent_t done = nullptr;
   bool pending = false;
@@ -104,8 +107,9 @@ static std::mutex g_stage_mu;
 static std::vector<std::vector<StageSlot>> g_stage;   // per device: 8 slots
 static std::vector<unsigned> g_stage_next;
 
-static pa_status upload(void *dst, const void *src, size_t bytes, hipStream_t s) {
-  if (bytes == 0) return PA_OK;
+// A free slot of at least `bytes`; the caller fills slot->host, launches the
+// kernels that read slot->dev, then calls stage_release.
+static pa_status stage_acquire(size_t bytes, StageSlot **out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -124,21 +128,38 @@ static pa_status upload(void *dst, const void *src, size_t bytes, hipStream_t s)
     return hip_fail(e, "staging event");
   if (slot.cap < bytes) {
     if (slot.host) hipHostFree(slot.host);
-    slot.host = nullptr;
-    size_t cap = std::max<size_t>(bytes, 64 << 10);
-    if ((e = hipHostMalloc(&slot.host, cap, hipHostMallocDefault)) != hipSuccess) {
-      slot.cap = 0;
+    slot.host = slot.dev = nullptr;
+    slot.cap = 0;
+    const size_t cap = std::max<size_t>(bytes, 64 << 10);
+    if ((e = hipHostMalloc(&slot.host, cap, hipHostMallocMapped | hipHostMallocCoherent)) != hipSuccess) {
+      slot.host = nullptr;
       return hip_fail(e, "staging buffer");
     }
+    if ((e = hipHostGetDevicePointer(&slot.dev, slot.host, 0)) != hipSuccess) return hip_fail(e, "staging map");
     slot.cap = cap;
   }
-  memcpy(slot.host, src, bytes);
-  if ((e = hipMemcpyAsync(dst, slot.host, bytes, hipMemcpyHostToDevice, s)) != hipSuccess)
-    return hip_fail(e, "plan upload");
-  if ((e = hipEventRecord(slot.done, s)) != hipSuccess) return hip_fail(e, "staging record");
-  slot.pending = true;
+  *out = &slot;
   return PA_OK;
 }
+
+// Marks the slot busy until the work queued on `s` so far has completed
+// (recorded when the guard leaves scope, i.e. after every launch of the call,
+// on every return path).
+struct StageGuard {
+  StageSlot *slot = nullptr;
+  hipStream_t s = nullptr;
+  ~StageGuard() {
+    if (!slot) return;
+    std::lock_guard<std::mutex> lk(g_stage_mu);
+    if (hipEventRecord(slot->done, s) == hipSuccess) {
+      slot->pending = true;
+    } else {
+      // the event could not be queued: wait for the stream instead, so the
+      // buffer is not reused while kernels may still read it
+      (void)hipStreamSynchronize(s);
+    }
+  }
+};
 
 // ------------------------------------------------------------- side stream --
 // Prefill rows (MFMA) and decode rows (HBM-bound) of one step are
@@ -468,14 +489,27 @@ pa_status pa_attention(const pa_kv_pool *pool, const pa_batch *batch, const void
   if (workspace_bytes < plan.bytes)
     return fail(PA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, plan.bytes);
 
-  // upload the work lists (one contiguous copy)
+  // the work lists: written into a staging slot that the kernels read
+  // directly, or (PA_PLAN_UPLOAD=1) copied into the workspace
   const size_t plan_bytes = plan.off_ml;
+  StageSlot *slot = nullptr;
+  StageGuard guard;
+  const char *items = (const char *)workspace;
   if (plan_bytes) {
-    std::vector<char> host(plan_bytes, 0);
-    if (!plan.dec.empty()) memcpy(host.data() + plan.off_dec, plan.dec.data(), plan.dec.size() * sizeof(DecodeItem));
-    if (!plan.merge.empty()) memcpy(host.data() + plan.off_merge, plan.merge.data(), plan.merge.size() * sizeof(MergeItem));
-    if (!plan.ext.empty()) memcpy(host.data() + plan.off_ext, plan.ext.data(), plan.ext.size() * sizeof(ExtendItem));
-    if ((st = upload(workspace, host.data(), plan_bytes, s)) != PA_OK) return st;
+    if ((st = stage_acquire(plan_bytes, &slot)) != PA_OK) return st;
+    guard.slot = slot;
+    guard.s = s;
+    char *host = (char *)slot->host;
+    memset(host, 0, plan_bytes);
+    if (!plan.dec.empty()) memcpy(host + plan.off_dec, plan.dec.data(), plan.dec.size() * sizeof(DecodeItem));
+    if (!plan.merge.empty()) memcpy(host + plan.off_merge, plan.merge.data(), plan.merge.size() * sizeof(MergeItem));
+    if (!plan.ext.empty()) memcpy(host + plan.off_ext, plan.ext.data(), plan.ext.size() * sizeof(ExtendItem));
+    if (env_flag("PA_PLAN_UPLOAD")) {
+      hipError_t ce = hipMemcpyAsync(workspace, host, plan_bytes, hipMemcpyHostToDevice, s);
+      if (ce != hipSuccess) return hip_fail(ce, "plan upload");
+    } else {
+      items = (const char *)slot->dev;
+    }
   }
   char *ws = (char *)workspace;
   const int g_total = num_q_heads / pool->num_kv_heads;
@@ -501,7 +535,7 @@ pa_status pa_attention(const pa_kv_pool *pool, const pa_batch *batch, const void
     x.k_cache = pool->k_cache;
     x.v_cache = pool->v_cache;
     x.block_table = batch->block_table;
-    x.items = (const ExtendItem *)(ws + plan.off_ext);
+    x.items = (const ExtendItem *)(items + plan.off_ext);
     x.n_items = (int32_t)plan.ext.size();
     x.bt_stride = batch->bt_stride;
     x.num_blocks = pool->num_blocks;
@@ -522,7 +556,7 @@ pa_status pa_attention(const pa_kv_pool *pool, const pa_batch *batch, const void
     a.k_cache = pool->k_cache;
     a.v_cache = pool->v_cache;
     a.block_table = batch->block_table;
-    a.items = (const DecodeItem *)(ws + plan.off_dec);
+    a.items = (const DecodeItem *)(items + plan.off_dec);
     a.part_ml = (float *)(ws + plan.off_ml);
     a.part_o = (float *)(ws + plan.off_o);
     a.n_items = (int32_t)plan.dec.size();
@@ -549,7 +583,7 @@ pa_status pa_attention(const pa_kv_pool *pool, const pa_batch *batch, const void
     m.out = output;
     m.part_ml = (const float *)(ws + plan.off_ml);
     m.part_o = (const float *)(ws + plan.off_o);
-    m.items = (const MergeItem *)(ws + plan.off_merge);
+    m.items = (const MergeItem *)(items + plan.off_merge);
     m.n_items = (int32_t)plan.merge.size();
     m.num_q_heads = num_q_heads;
     e = launch_merge(q_dtype, pool->head_dim, m, s);
