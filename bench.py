@@ -174,7 +174,7 @@ def algorithmic_work(w, seq_lens, qsl, ext_min_rows=16, extend_on=True):
         c, L = int(qsl[i + 1] - qsl[i]), int(seq_lens[i])
         if c == 0:
             continue
-        use_ext = extend_on and c >= ext_min_rows and w.kv_dtype == "bf16" and D == 128
+        use_ext = extend_on and c >= ext_min_rows and w.kv_dtype in ("bf16", "fp8") and D == 128
         if use_ext:
             ext_flops += 4 * Hq * D * sum(L - c + t + 1 for t in range(c))
             ext_bytes += L * H * D * 2 * b_kv + c * Hq * D * 2 * b_io

@@ -55,10 +55,20 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kXD = 128;                        // head dim
 constexpr int kXT = 64;                         // keys per tile
 constexpr int kXStages = 4;
-constexpr int kXKBytes = kXT * kXD * 2;         // 16 KB
-constexpr int kXStage = 2 * kXKBytes;           // K + V^T
-constexpr int kXLds = kXStages * kXStage;       // 128 KB
-constexpr int kXTileB = kXD * kBlock * 2;       // pool bytes of one (block, head) tile
+constexpr int kXLds = 128 * 1024;               // ring (<= 128 KB), Q, epilogue staging
+
+// Per pool dtype (bf16, fp8): bytes of a K row and of the K / V^T halves of a
+// stage in LDS, and pool bytes of one (block, head) tile.
+template <int KV>
+struct XLayout {
+  static constexpr int PB = KvTraits<KV>::bytes;
+  static constexpr int kRow = kXD * PB;         // 256 / 128
+  static constexpr int kKBytes = kXT * kRow;    // 16 KB / 8 KB
+  static constexpr int kStage = 2 * kKBytes;    // K + V^T
+  static constexpr int kTileB = kXD * kBlock * PB;
+  static constexpr int kCopies = kKBytes / 8 / 1024;  // 1 KB copies per wave per half of a tile
+};
+static_assert(kXStages * XLayout<KV_BF16>::kStage <= kXLds, "ring fits");
 static_assert(kExtCols == 128, "4 column blocks of 32, each split over two waves");
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -67,6 +77,19 @@ __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1)
 __device__ __forceinline__ int vt_swz(int d) { return ((d >> 2) ^ (d >> 3)) & 1; }
 __device__ __forceinline__ int vt_offset(int d, int k) {
   return (k >> 4) * 4096 + d * 32 + ((((k >> 3) & 1) ^ vt_swz(d)) * 16) + (k & 7) * 2;
+}
+// fp8 V^T tile: [tile block b][dim d][16 keys], one byte per key (the pool's
+// own block tile layout).
+__device__ __forceinline__ int vt8_offset(int d, int k) { return (k >> 4) * 2048 + d * 16 + (k & 15); }
+
+// 8 E4M3 codes -> 8 bf16 values (exact: every E4M3 value is a bf16 value).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint2 u) {
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.x, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.x, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.y, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.y, 1.0f, true);
+  return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 // 16 bytes per lane from base + off (global) to LDS at lds_base + 16 * lane;
@@ -104,7 +127,9 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 // compiler's __syncthreads waits for every copy first).
 __device__ __forceinline__ void barrier_keep_loads() { asm volatile("s_barrier" ::: "memory"); }
 
+template <int KV>
 __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
+  using X = XLayout<KV>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -145,9 +170,9 @@ __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
   bf16x8_t qop[8];                               // Q^T operand: dims 16 ks + 8 hsel .. +8 of the lane's column
 
   const int32_t *btrow = a.block_table + (int64_t)req * a.bt_stride;
-  const char *kpool = (const char *)a.k_cache + (int64_t)kvh * kXTileB;
-  const char *vpool = (const char *)a.v_cache + (int64_t)kvh * kXTileB;
-  const int64_t bstride = (int64_t)a.num_kv_heads * kXTileB;
+  const char *kpool = (const char *)a.k_cache + (int64_t)kvh * X::kTileB;
+  const char *vpool = (const char *)a.v_cache + (int64_t)kvh * X::kTileB;
+  const int64_t bstride = (int64_t)a.num_kv_heads * X::kTileB;
 
   // Block id of logical block b (uniform).  Blocks past the range repeat the
   // last one and ids outside the pool read block 0: both in bounds, and every
@@ -156,30 +181,39 @@ __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
     const int v = load_uniform(btrow + min(b, blk_last));
     return (v >= 0 && v < a.num_blocks) ? v : 0;
   };
-  // This wave's copy share: tile block w / 2, and within it K rows
-  // 8 w + 4 u .. +3 and V^T dims 32 (2 w + u) % 128 .. +31 for u = 0, 1, each
-  // instruction moving 1 KB of LDS.  Per-lane source offsets within the pool
-  // tile of a (block, head):
-  uint32_t koff[2], voff[2];
+  // This wave's copy share of a tile, all from tile block w / 2, each
+  // instruction moving 1 KB of LDS.  bf16: K rows 8 w + 4 u .. +3 and V^T
+  // dims 32 (2 w + u) % 128 .. +31 for u = 0, 1.  fp8 (K rows of 128 bytes,
+  // chunk c of row r in slot c ^ ((r >> 1) & 7); the V^T block tile is the
+  // pool's own): K rows 8 w .. 8 w + 7 and V^T dims 64 (w % 2) .. +63.
+  // Per-lane source offsets within the pool tile of a (block, head):
+  uint32_t koff[X::kCopies], voff[X::kCopies];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int I = wave * 2 + u;
-    const int rho = 4 * I + (lane >> 4);
-    const int chunk = (lane & 15) ^ (rho & 15);
-    koff[u] = chunk * 256 + (swap23(rho) & 15) * 16;
-    const int d = 32 * (I & 3) + (lane >> 1);
-    const int half = (lane & 1) ^ vt_swz(d);
-    voff[u] = d * 32 + half * 16;
+  for (int u = 0; u < X::kCopies; ++u) {
+    if constexpr (KV == KV_BF16) {
+      const int I = wave * 2 + u;
+      const int rho = 4 * I + (lane >> 4);
+      const int chunk = (lane & 15) ^ (rho & 15);
+      koff[u] = chunk * 256 + (swap23(rho) & 15) * 16;
+      const int d = 32 * (I & 3) + (lane >> 1);
+      const int half = (lane & 1) ^ vt_swz(d);
+      voff[u] = d * 32 + half * 16;
+    } else {
+      const int rho = 8 * wave + (lane >> 3);
+      const int chunk = (lane & 7) ^ ((rho >> 1) & 7);
+      koff[u] = chunk * 256 + (swap23(rho) & 15) * 16;
+      voff[u] = (wave & 1) * 1024 + lane * 16;
+    }
   }
   const int my_blk = wave >> 1;
   int next_id = blk_id(my_blk);                  // block id for the next tile to issue
   auto issue = [&](int kt) {
-    char *kst = smem + (kt % kXStages) * kXStage + wave * 2048;
-    char *vst = kst + kXKBytes;
+    char *kst = smem + (kt % kXStages) * X::kStage + wave * (X::kCopies * 1024);
+    char *vst = kst + X::kKBytes;
     const char *ksrc = kpool + (int64_t)next_id * bstride;
     const char *vsrc = vpool + (int64_t)next_id * bstride;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < X::kCopies; ++u) {
       copy16_to_lds(ksrc, koff[u], kst + u * 1024);
       copy16_to_lds(vsrc, voff[u], vst + u * 1024);
     }
@@ -209,7 +243,11 @@ __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
       for (int mt = 0; mt < 2; ++mt) {             // the two chains alternate
         const int rho = mt * 32 + (lane & 31);
         const int chunk = 2 * ks + hsel;
-        const bf16x8_t aop = as_bf16x8(*(const uint4 *)(kb + rho * 256 + ((chunk ^ (rho & 15)) * 16)));
+        bf16x8_t aop;
+        if constexpr (KV == KV_BF16)
+          aop = as_bf16x8(*(const uint4 *)(kb + rho * 256 + ((chunk ^ (rho & 15)) * 16)));
+        else
+          aop = fp8x8_to_bf16x8(*(const uint2 *)(kb + rho * 128 + ((ks ^ ((rho >> 1) & 7)) * 16) + hsel * 8));
         sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, qop[ks], sacc[mt], 0, 0, 0);
       }
     // Schedule: four LDS operand reads ahead, then alternate one MFMA and
@@ -279,7 +317,11 @@ __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
 #pragma unroll
       for (int md = 0; md < 4; ++md) {                // keys 16 ks + 8 hsel .. +8 of dim d
         const int d = md * 32 + (lane & 31);
-        const bf16x8_t aop = as_bf16x8(*(const uint4 *)(vb + vt_offset(d, 16 * ks + 8 * hsel)));
+        bf16x8_t aop;
+        if constexpr (KV == KV_BF16)
+          aop = as_bf16x8(*(const uint4 *)(vb + vt_offset(d, 16 * ks + 8 * hsel)));
+        else
+          aop = fp8x8_to_bf16x8(*(const uint2 *)(vb + vt8_offset(d, 16 * ks + 8 * hsel)));
         oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, oacc[md], 0, 0, 0);
       }
     }
@@ -304,7 +346,7 @@ __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
   // 1 is issued) together with pair 0: row cc (256 bytes) holds column cc's
   // 16-byte chunk c in slot c ^ (cc & 15), so the operand reads below are
   // conflict-free.  Instruction u of wave w moves columns 4 (4 w + u) .. +3.
-  char *qst = smem + 3 * kXStage;
+  char *qst = smem + kXLds - 32 * 1024;
   {
     const char *qsrc = (const char *)a.q + (int64_t)out_row(0) * (kXD * 2);
     const int64_t row0 = out_row(0);
@@ -336,19 +378,22 @@ __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
       // Last pair: keys past the range may hold anything (unwritten slots,
       // stand-in blocks); zero their V so that 0 * v stays 0.
       const int tl = n_tiles - 1;
-      char *vb = smem + (tl % kXStages) * kXStage + kXKBytes;
+      char *vb = smem + (tl % kXStages) * X::kStage + X::kKBytes;
       const int kv = kend_wg - tl * kXT;
       for (int e = tid; e < kXD * kXT; e += 512) {
         const int d = e >> 6, k = e & 63;
-        if (k >= kv) *(uint16_t *)(vb + vt_offset(d, k)) = 0;
+        if (k >= kv) {
+          if constexpr (KV == KV_BF16) *(uint16_t *)(vb + vt_offset(d, k)) = 0;
+          else *(uint8_t *)(vb + vt8_offset(d, k)) = 0;
+        }
       }
       __syncthreads();
     }
     const int kt = 2 * p + grp;
     const int kbase = kt * kXT;
     if (kt >= n_tiles || !wave_active || kbase >= kend_w) continue;
-    const char *kb = smem + (kt % kXStages) * kXStage;
-    tile(kb, kb + kXKBytes, kbase, kbase + kXT > wave_min_nvis);
+    const char *kb = smem + (kt % kXStages) * X::kStage;
+    tile(kb, kb + X::kKBytes, kbase, kbase + kXT > wave_min_nvis);
   }
 
   // Merge the odd-tile partial (m, l, O) of each column into the even-tile
@@ -381,7 +426,7 @@ __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
     const float m = fmaxf(m_run, m1);
     const float a0 = __builtin_amdgcn_exp2f(m_run - m);
     const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
-    const float inv = 1.0f / (l_half * a0 + xl[cw * 64 + lane] * a1);
+    const float inv = a.v_scale / (l_half * a0 + xl[cw * 64 + lane] * a1);
     const float s0 = a0 * inv, s1 = a1 * inv;
     char *orow = ost + (cw * 32 + (lane & 31)) * kOutPitch;
 #pragma unroll
@@ -408,29 +453,41 @@ __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
   }
 }
 
-hipError_t launch_extend(const pa_kv_pool &p, const ExtendArgs &a, hipStream_t s) {
-  if (a.n_items == 0) return hipSuccess;
-  if (p.kv_dtype != PA_BF16 || p.head_dim != kXD) return hipErrorNotSupported;
-  // The LDS size above the default limit is a per-device attribute of the
-  // kernel: set it once for each device the library launches on.
+// The LDS size above the default limit is a per-device attribute of each
+// kernel: set it once for each (kernel, device) the library launches on.
+template <int KV>
+static hipError_t set_lds_attr() {
   static std::mutex mu;
-  static std::vector<char> attr_set;
+  static std::vector<char> done;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  {
-    std::lock_guard<std::mutex> lk(mu);
-    if ((int)attr_set.size() <= dev) attr_set.resize(dev + 1, 0);
-    if (!attr_set[dev]) {
-      e = hipFuncSetAttribute((const void *)k_extend, hipFuncAttributeMaxDynamicSharedMemorySize, kXLds);
-      if (e != hipSuccess) return e;
-      attr_set[dev] = 1;
-    }
+  std::lock_guard<std::mutex> lk(mu);
+  if ((int)done.size() <= dev) done.resize(dev + 1, 0);
+  if (!done[dev]) {
+    e = hipFuncSetAttribute((const void *)k_extend<KV>, hipFuncAttributeMaxDynamicSharedMemorySize, kXLds);
+    if (e != hipSuccess) return e;
+    done[dev] = 1;
   }
+  return hipSuccess;
+}
+
+template <int KV>
+static hipError_t launch_extend_t(const ExtendArgs &a, hipStream_t s) {
+  hipError_t e = set_lds_attr<KV>();
+  if (e != hipSuccess) return e;
   prof_begin("k_extend", s);
-  hipLaunchKernelGGL(k_extend, dim3(a.n_items), dim3(512), kXLds, s, a);
+  hipLaunchKernelGGL(k_extend<KV>, dim3(a.n_items), dim3(512), kXLds, s, a);
   prof_end(s);
   return hipGetLastError();
+}
+
+hipError_t launch_extend(const pa_kv_pool &p, const ExtendArgs &a, hipStream_t s) {
+  if (a.n_items == 0) return hipSuccess;
+  if (p.head_dim != kXD) return hipErrorNotSupported;
+  if (p.kv_dtype == PA_BF16) return launch_extend_t<KV_BF16>(a, s);
+  if (p.kv_dtype == PA_FP8_E4M3) return launch_extend_t<KV_FP8>(a, s);
+  return hipErrorNotSupported;
 }
 
 }  // namespace pa

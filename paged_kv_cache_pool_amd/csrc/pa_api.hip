@@ -283,14 +283,15 @@ struct Plan {
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Smallest number of prefill rows for which a request goes to the MFMA
-// extend kernel (bf16 pools); shorter ones use the split-K kernel.
+// extend kernel (bf16 or fp8 pools with bf16 q, head_dim 128); shorter ones use
+// the split-K kernel.
 static int extend_min_rows() {
   const char *v = getenv("PA_EXTEND_MIN_ROWS");
   return v ? atoi(v) : 16;
 }
 
 static bool extend_supported(const pa_kv_pool &p, pa_dtype q_dtype) {
-  return q_dtype == PA_BF16 && p.kv_dtype == PA_BF16 && p.head_dim == 128;
+  return q_dtype == PA_BF16 && (p.kv_dtype == PA_BF16 || p.kv_dtype == PA_FP8_E4M3) && p.head_dim == 128;
 }
 
 static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dtype q_dtype,

@@ -321,6 +321,22 @@ def test_extend_chunks(R, g, c, hist):
     _check_attention(w, step)
 
 
+@pytest.mark.parametrize("g", [1, 4, 8])
+@pytest.mark.parametrize("c,hist", [(16, 0), (100, 37), (129, 300), (257, 16)])
+def test_extend_chunks_fp8(R, g, c, hist):
+    """Prefill chunks over an fp8 pool (per-tensor scales) through the MFMA
+    kernel: the codes are widened to bf16 exactly in LDS, scores take
+    k_scale and the output v_scale."""
+    say("extend fp8 g", g, "c", c, "hist", hist)
+    w = W.build(f"ext8_{g}_{c}_{hist}", c + hist + 1, num_q_heads=2 * g, num_kv_heads=2, head_dim=128,
+                block_size=16, num_blocks=-(-(c + hist) // 16) + 40, kv_dtype=W.FP8,
+                io_dtype=W.BF16, num_computed=[hist, 70], num_scheduled=[c, 1])
+    step = R.GpuStep(w)
+    step.run()
+    torch.cuda.synchronize()
+    _check_attention(w, step)
+
+
 def test_extend_noncausal(R):
     say("extend non-causal")
     w = W.build("ext_nc", 4, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
