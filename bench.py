@@ -162,14 +162,36 @@ def load_traffic(kernel, workload):
     return rec["hbm_bytes"]
 
 
-def algorithmic_work(w, seq_lens, qsl, ext_min_rows=16, extend_on=True):
-    """Bytes the split-K decode kernel must move and flops the extend kernel
-    must do, per step, by the per-unit formulas in the design notes."""
+def cascade_prefix(w, seq_lens, qsl, ext_min_rows=16, extend_on=True, hint=True):
+    """Keys of the shared prefix that the library's cascade pass takes over
+    from the split-K rows (0 when it does not apply): the same rule as the
+    library's plan."""
+    P = w.shared_prefix_blocks * w.block_size if hint else 0
+    mfma_ok = w.kv_dtype in ("bf16", "fp8") and w.head_dim == 128 and w.io_dtype == "bf16"
+    if P == 0 or not mfma_ok or os.environ.get("PA_DISABLE_CASCADE", "0") not in ("", "0"):
+        return 0
+    rows = 0
+    for i in range(w.num_seqs):
+        c, L = int(qsl[i + 1] - qsl[i]), int(seq_lens[i])
+        if c == 0 or (extend_on and c >= ext_min_rows and mfma_ok):
+            continue
+        if L - c < P:
+            return 0
+        rows += c
+    return P if rows else 0
+
+
+def algorithmic_work(w, seq_lens, qsl, ext_min_rows=16, extend_on=True, prefix=0):
+    """Bytes the split-K decode kernel must move, flops the extend kernel must
+    do and flops of the shared-prefix pass, per step, by the per-unit formulas
+    in the design notes.  With a shared prefix of `prefix` keys taken over by
+    the cascade pass, the split-K rows' bytes count their own keys only."""
     b_kv, b_io = ELEM[w.kv_dtype], ELEM[w.io_dtype]
     H, Hq, D, S = w.num_kv_heads, w.num_q_heads, w.head_dim, w.block_size
     dec_bytes = 0
     ext_flops = 0
     ext_bytes = 0
+    pre_flops = 0
     for i in range(w.num_seqs):
         c, L = int(qsl[i + 1] - qsl[i]), int(seq_lens[i])
         if c == 0:
@@ -181,13 +203,15 @@ def algorithmic_work(w, seq_lens, qsl, ext_min_rows=16, extend_on=True):
         else:
             for t in range(c):
                 Lv = L - c + t + 1
-                dec_bytes += Lv * H * D * 2 * b_kv + Hq * D * b_io + -(-Lv // S) * 4
-    return dec_bytes, ext_flops, ext_bytes
+                dec_bytes += (Lv - prefix) * H * D * 2 * b_kv + Hq * D * b_io + (-(-Lv // S) - prefix // S) * 4
+                pre_flops += 4 * Hq * D * prefix
+    return dec_bytes, ext_flops, ext_bytes, pre_flops
 
 
-def unique_kv_bytes(w, seq_lens, qsl):
+def unique_kv_bytes(w, seq_lens, qsl, prefix=0):
     """K+V bytes of the distinct pool slots the decode rows read (a block shared
-    by several requests counts once): what HBM must deliver at least once."""
+    by several requests counts once; keys before `prefix` are the cascade
+    pass's): what HBM must deliver at least once."""
     b_kv = ELEM[w.kv_dtype]
     S = w.block_size
     seen = {}
@@ -195,7 +219,7 @@ def unique_kv_bytes(w, seq_lens, qsl):
         c, L = int(qsl[i + 1] - qsl[i]), int(seq_lens[i])
         if c == 0:
             continue
-        for b in range(-(-L // S)):
+        for b in range(prefix // S, -(-L // S)):
             blk = int(w.block_table[i, b])
             seen[blk] = max(seen.get(blk, 0), min(S, L - b * S))
     return sum(seen.values()) * w.num_kv_heads * w.head_dim * 2 * b_kv
@@ -251,7 +275,7 @@ def main():
     torch.cuda.synchronize()
     ms_instr = ev0.elapsed_time(ev1) / a.steps
     kernels = {}
-    for name in ("k_slot_mapping", "k_write_kv", "k_decode", "k_merge", "k_extend"):
+    for name in ("k_slot_mapping", "k_write_kv", "k_prefix", "k_decode", "k_merge", "k_extend"):
         n, ms = B.profile_read(name)
         if n:
             kernels[name] = {"launches": n, "avg_us": 1000.0 * ms / n}
@@ -295,8 +319,10 @@ def main():
     tokens_per_s = T / (ms_per_step / 1000.0)
     qsl, sl = B.prepare_metadata(w.num_computed, w.num_scheduled)
     ext_on = os.environ.get("PA_DISABLE_EXTEND", "0") in ("", "0")
-    dec_bytes, ext_flops, ext_bytes = algorithmic_work(
-        w, sl, qsl, int(os.environ.get("PA_EXTEND_MIN_ROWS", "16")), ext_on and "k_extend" in kernels)
+    ext_min = int(os.environ.get("PA_EXTEND_MIN_ROWS", "16"))
+    prefix = cascade_prefix(w, sl, qsl, ext_min, ext_on, hint=step.batch.num_common_prefix_blocks > 0)
+    dec_bytes, ext_flops, ext_bytes, pre_flops = algorithmic_work(
+        w, sl, qsl, ext_min, ext_on and "k_extend" in kernels, prefix)
 
     if "k_decode" in kernels and (dec_bytes > 0):
         dom = "k_decode"
@@ -355,10 +381,13 @@ def main():
     if cold is not None:
         out["ms_per_step_cold"] = cold
     if roof["unit"] == "GB/s":
-        uniq = unique_kv_bytes(w, sl, qsl)
+        uniq = unique_kv_bytes(w, sl, qsl, prefix)
         out["decode_kv_bytes_logical"] = dec_bytes
         out["decode_kv_bytes_unique"] = uniq
         out["decode_kv_gbps_unique"] = round(uniq / (kernels["k_decode"]["avg_us"] * 1e-6) / 1e9, 1)
+    if pre_flops and "k_prefix" in kernels:
+        out["prefix_keys"] = prefix
+        out["prefix_tflops"] = round(pre_flops / (kernels["k_prefix"]["avg_us"] * 1e-6) / 1e12, 1)
     if ext_flops:
         out["extend_tflops"] = round(ext_flops / (kernels["k_extend"]["avg_us"] * 1e-6) / 1e12, 1) \
             if "k_extend" in kernels else None

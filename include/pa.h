@@ -114,7 +114,22 @@ typedef struct pa_batch {
   int32_t bt_stride;                    /* elements between block_table rows   */
   const int32_t *query_start_loc_host;  /* host   [N + 1], same values         */
   const int32_t *seq_lens_host;         /* host   [N],     same values         */
+  int32_t num_common_prefix_blocks;     /* shared-prefix hint, see below (0: none) */
 } pa_batch;
+
+/* num_common_prefix_blocks ([P1] common prefix of all requests, the
+ * num_common_prefix_blocks the scheduler reports; cascade attention): n > 0
+ * states that the first n block-table entries of every request that has new
+ * tokens are the same n physical blocks, and that these blocks lie wholly in
+ * every such request's history (16 * n <= seq_lens[i] - c_i).  The library
+ * may then compute the rows' attention over those 16 * n keys once for all
+ * rows that share them and combine it with the rest by the partition rule of
+ * [P5] third walk-through path; the result equals the one without the hint
+ * up to rounding.  The hint is ignored (no error) where it cannot be used: a
+ * request violating the history condition, rows the library handles with
+ * its prefill kernel, or pool / query types without that path.  A hint whose
+ * blocks are not actually shared gives wrong results; with PA_VALIDATE set,
+ * pa_attention checks the block tables and returns PA_ERR_VALIDATION. */
 
 /* ---------------------------------------------------------------------- */
 

@@ -47,7 +47,8 @@ class PaBatch(C.Structure):
     _fields_ = [("num_seqs", C.c_int32), ("num_tokens", C.c_int32),
                 ("query_start_loc", C.c_void_p), ("seq_lens", C.c_void_p),
                 ("block_table", C.c_void_p), ("bt_stride", C.c_int32),
-                ("query_start_loc_host", C.c_void_p), ("seq_lens_host", C.c_void_p)]
+                ("query_start_loc_host", C.c_void_p), ("seq_lens_host", C.c_void_p),
+                ("num_common_prefix_blocks", C.c_int32)]
 
 
 def _load():
@@ -168,15 +169,16 @@ class Batch:
     block_table: torch.Tensor       # int32 device [N, W]
     qsl_host: np.ndarray            # int32 [N+1]
     seq_lens_host: np.ndarray       # int32 [N]
+    num_common_prefix_blocks: int = 0   # shared-prefix hint (pa.h)
 
     @classmethod
     def from_host(cls, qsl: np.ndarray, seq_lens: np.ndarray, block_table: np.ndarray,
-                  device="cuda") -> "Batch":
+                  device="cuda", num_common_prefix_blocks: int = 0) -> "Batch":
         qsl = np.ascontiguousarray(qsl, dtype=np.int32)
         sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
         bt = np.ascontiguousarray(block_table, dtype=np.int32)
         return cls(torch.from_numpy(qsl).to(device), torch.from_numpy(sl).to(device),
-                   torch.from_numpy(bt).to(device), qsl, sl)
+                   torch.from_numpy(bt).to(device), qsl, sl, int(num_common_prefix_blocks))
 
     @property
     def num_seqs(self) -> int:
@@ -190,7 +192,8 @@ class Batch:
         bt = self.block_table
         return PaBatch(self.num_seqs, self.num_tokens, self.query_start_loc.data_ptr(),
                        self.seq_lens.data_ptr(), bt.data_ptr(), bt.stride(0) if bt.dim() == 2 else 0,
-                       self.qsl_host.ctypes.data, self.seq_lens_host.ctypes.data)
+                       self.qsl_host.ctypes.data, self.seq_lens_host.ctypes.data,
+                       self.num_common_prefix_blocks)
 
 
 # ---------------------------------------------------------------- calls ----

@@ -127,49 +127,71 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 // compiler's __syncthreads waits for every copy first).
 __device__ __forceinline__ void barrier_keep_loads() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int KV>
+// PREFIX = false: a prefill chunk of one request (columns = its new tokens x
+// GQA heads, causal or not), written to the output.  PREFIX = true: the
+// shared-prefix (cascade) pass: columns = the prefix rows (rows of every
+// request that shares the common prefix) x GQA heads, keys = one chunk of the
+// common prefix, all visible; written as partial (m, l, o) for the merge.
+template <int KV, bool PREFIX>
 __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
   using X = XLayout<KV>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
-  const ExtendItem item = a.items[blockIdx.x];
-  const int req = uniform(item.req), kvh = uniform(item.kvh), tok0 = uniform(item.tok0);
-  const int c = uniform(item.c), L = uniform(item.L), col0 = uniform(item.col0);
   const int g = a.g;
-  const int ncols = c * g;
-  const int hist = L - c;                        // tokens before this step's first new token
   const int hsel = lane >> 5;                    // which 8-element k group the lane feeds
+  int kvh, col0, ncols, kspan, kc = 0, hist = 0, tok0 = 0;
+  const int32_t *btrow;
+  if constexpr (PREFIX) {
+    const PrefixItem it = a.pitems[blockIdx.x];
+    kvh = uniform(it.kvh);
+    col0 = uniform(it.col0);
+    kc = uniform(it.kc);
+    const int key0 = uniform(it.key0), key1 = uniform(it.key1);
+    ncols = a.prefix_cols;
+    kspan = key1 - key0;                         // keys are counted from key0 (a multiple of 64)
+    btrow = a.prefix_bt + key0 / kBlock;
+  } else {
+    const ExtendItem item = a.items[blockIdx.x];
+    const int req = uniform(item.req), c = uniform(item.c), L = uniform(item.L);
+    kvh = uniform(item.kvh);
+    tok0 = uniform(item.tok0);
+    col0 = uniform(item.col0);
+    ncols = c * g;
+    hist = L - c;                                // tokens before this step's first new token
+    kspan = L;
+    btrow = a.block_table + (int64_t)req * a.bt_stride;
+  }
+  const bool causal = !PREFIX && a.causal;
 
   // key range of the workgroup and of this wave (columns are token-major)
   const int last_col_wg = min(ncols, col0 + kExtCols) - 1;
-  const int kend_wg = a.causal ? hist + last_col_wg / g + 1 : L;
+  const int kend_wg = causal ? hist + last_col_wg / g + 1 : kspan;
   const int n_tiles = (kend_wg + kXT - 1) / kXT;
   const int blk_last = (kend_wg - 1) / kBlock;   // last logical block read
   const int grp = wave >> 2;                     // key-split group: even (0) or odd (1) tiles
   const int cw = wave & 3;                       // column block within the workgroup
   const int wcol0 = col0 + cw * 32;
   const bool wave_active = wcol0 < ncols;
-  const int kend_w = a.causal ? hist + (min(ncols, wcol0 + 32) - 1) / g + 1 : L;
-  const int wave_min_nvis = a.causal ? hist + min(wcol0, ncols - 1) / g + 1 : L;
+  const int kend_w = causal ? hist + (min(ncols, wcol0 + 32) - 1) / g + 1 : kspan;
+  const int wave_min_nvis = causal ? hist + min(wcol0, ncols - 1) / g + 1 : kspan;
 
   // this lane's column (clamped to a valid one; invalid columns are not stored)
   const int col_raw = wcol0 + (lane & 31);
   const int col = min(col_raw, ncols - 1);
-  const int t = col / g;
-  const int nvis = a.causal ? hist + t + 1 : L;
+  const int nvis = causal ? hist + col / g + 1 : kspan;
 
-  // Output row (in units of head_dim elements) of workgroup column cc, clamped
-  // to a valid column.
+  // q / output row (in units of head_dim elements) of workgroup column cc,
+  // clamped to a valid column; increasing in cc.
   auto out_row = [&](int cc) -> int64_t {
     const int cg = min(col0 + cc, ncols - 1);
     const int tt = cg / g;
-    return (int64_t)(tok0 + tt) * a.num_q_heads + kvh * g + (cg - tt * g);
+    if constexpr (PREFIX) return (int64_t)a.row_token[tt] * a.num_q_heads + kvh * g + (cg - tt * g);
+    else return (int64_t)(tok0 + tt) * a.num_q_heads + kvh * g + (cg - tt * g);
   };
   bf16x8_t qop[8];                               // Q^T operand: dims 16 ks + 8 hsel .. +8 of the lane's column
 
-  const int32_t *btrow = a.block_table + (int64_t)req * a.bt_stride;
   const char *kpool = (const char *)a.k_cache + (int64_t)kvh * X::kTileB;
   const char *vpool = (const char *)a.v_cache + (int64_t)kvh * X::kTileB;
   const int64_t bstride = (int64_t)a.num_kv_heads * X::kTileB;
@@ -342,8 +364,9 @@ __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
     issue(2 * p);
     if (2 * p + 1 < n_tiles) issue(2 * p + 1);
   };
-  // Q of the workgroup's 128 columns is copied into stage 3 (free until pair
-  // 1 is issued) together with pair 0: row cc (256 bytes) holds column cc's
+  // Q of the workgroup's 128 columns is copied into the last 32 KB of LDS
+  // (for bf16 pools stage 3, not refilled before pair 1 is issued) together
+  // with pair 0: row cc (256 bytes) holds column cc's
   // 16-byte chunk c in slot c ^ (cc & 15), so the operand reads below are
   // conflict-free.  Instruction u of wave w moves columns 4 (4 w + u) .. +3.
   char *qst = smem + kXLds - 32 * 1024;
@@ -421,6 +444,38 @@ __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
   // then written out as whole 256-byte rows.
   constexpr int kOutPitch = kXD * 2 + 16;
   char *ost = smem + 80 * 1024;
+  if constexpr (PREFIX) {
+    // partial (m, l, o) of this key chunk: o unnormalised, relative to m (log2
+    // units), v_scale applied -- the split-K kernel's format
+    if (grp == 0 && wave_active && col_raw < ncols) {
+      const float m1 = xm[cw * 64 + lane];
+      const float m = fmaxf(m_run, m1);
+      const float a0 = __builtin_amdgcn_exp2f(m_run - m);
+      const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
+      const int r = col / g;
+      const int head = kvh * g + (col - r * g);
+      const int64_t slot = (int64_t)a.row_slot0[r] + kc;
+      float *po = a.part_o + (slot * a.num_q_heads + head) * kXD;
+      const float s0 = a0 * a.v_scale, s1 = a1 * a.v_scale;
+#pragma unroll
+      for (int md = 0; md < 4; ++md)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int dim = md * 32 + 8 * q + 4 * hsel;  // rows r = 4q .. 4q+3
+          float o[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            o[i] = oacc[md][4 * q + i] * s0 + xo[(cw * 64 + md * 16 + 4 * q + i) * 64 + lane] * s1;
+          *(float4 *)(po + dim) = make_float4(o[0], o[1], o[2], o[3]);
+        }
+      if (hsel == 0) {
+        float *pml = a.part_ml + (slot * a.num_q_heads + head) * 2;
+        pml[0] = m;
+        pml[1] = l_half * a0 + xl[cw * 64 + lane] * a1;
+      }
+    }
+    return;
+  }
   if (grp == 0 && wave_active) {
     const float m1 = xm[cw * 64 + lane];
     const float m = fmaxf(m_run, m1);
@@ -455,7 +510,7 @@ __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
 
 // The LDS size above the default limit is a per-device attribute of each
 // kernel: set it once for each (kernel, device) the library launches on.
-template <int KV>
+template <int KV, bool PREFIX>
 static hipError_t set_lds_attr() {
   static std::mutex mu;
   static std::vector<char> done;
@@ -465,19 +520,19 @@ static hipError_t set_lds_attr() {
   std::lock_guard<std::mutex> lk(mu);
   if ((int)done.size() <= dev) done.resize(dev + 1, 0);
   if (!done[dev]) {
-    e = hipFuncSetAttribute((const void *)k_extend<KV>, hipFuncAttributeMaxDynamicSharedMemorySize, kXLds);
+    e = hipFuncSetAttribute((const void *)k_extend<KV, PREFIX>, hipFuncAttributeMaxDynamicSharedMemorySize, kXLds);
     if (e != hipSuccess) return e;
     done[dev] = 1;
   }
   return hipSuccess;
 }
 
-template <int KV>
-static hipError_t launch_extend_t(const ExtendArgs &a, hipStream_t s) {
-  hipError_t e = set_lds_attr<KV>();
+template <int KV, bool PREFIX>
+static hipError_t launch_t(int n, const ExtendArgs &a, hipStream_t s) {
+  hipError_t e = set_lds_attr<KV, PREFIX>();
   if (e != hipSuccess) return e;
-  prof_begin("k_extend", s);
-  hipLaunchKernelGGL(k_extend<KV>, dim3(a.n_items), dim3(512), kXLds, s, a);
+  prof_begin(PREFIX ? "k_prefix" : "k_extend", s);
+  hipLaunchKernelGGL((k_extend<KV, PREFIX>), dim3(n), dim3(512), kXLds, s, a);
   prof_end(s);
   return hipGetLastError();
 }
@@ -485,8 +540,17 @@ static hipError_t launch_extend_t(const ExtendArgs &a, hipStream_t s) {
 hipError_t launch_extend(const pa_kv_pool &p, const ExtendArgs &a, hipStream_t s) {
   if (a.n_items == 0) return hipSuccess;
   if (p.head_dim != kXD) return hipErrorNotSupported;
-  if (p.kv_dtype == PA_BF16) return launch_extend_t<KV_BF16>(a, s);
-  if (p.kv_dtype == PA_FP8_E4M3) return launch_extend_t<KV_FP8>(a, s);
+  if (p.kv_dtype == PA_BF16) return launch_t<KV_BF16, false>(a.n_items, a, s);
+  if (p.kv_dtype == PA_FP8_E4M3) return launch_t<KV_FP8, false>(a.n_items, a, s);
+  return hipErrorNotSupported;
+}
+
+// The shared-prefix pass: a.n_items prefix items (a.pitems).
+hipError_t launch_prefix(const pa_kv_pool &p, const ExtendArgs &a, hipStream_t s) {
+  if (a.n_items == 0) return hipSuccess;
+  if (p.head_dim != kXD) return hipErrorNotSupported;
+  if (p.kv_dtype == PA_BF16) return launch_t<KV_BF16, true>(a.n_items, a, s);
+  if (p.kv_dtype == PA_FP8_E4M3) return launch_t<KV_FP8, true>(a.n_items, a, s);
   return hipErrorNotSupported;
 }
 

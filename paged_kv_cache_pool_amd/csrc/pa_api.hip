@@ -232,6 +232,7 @@ static pa_status check_batch(const pa_batch *b, bool need_dev) {
       (!b->query_start_loc || !b->seq_lens || !b->block_table))
     return fail(PA_ERR_INVALID_ARG, "batch device arrays are NULL");
   if (b->bt_stride < 0) return fail(PA_ERR_INVALID_ARG, "negative bt_stride");
+  if (b->num_common_prefix_blocks < 0) return fail(PA_ERR_INVALID_ARG, "negative num_common_prefix_blocks");
   const int32_t *q = b->query_start_loc_host, *L = b->seq_lens_host;
   if (q[0] != 0) return fail(PA_ERR_INVALID_ARG, "query_start_loc[0] = %d, expected 0", q[0]);
   for (int32_t i = 0; i < b->num_seqs; ++i) {
@@ -262,6 +263,20 @@ static pa_status validate_block_table(const pa_batch *b, int32_t num_blocks, hip
         return fail(PA_ERR_VALIDATION, "block_table[%d][%lld] = %d outside [0, %d)", i, (long long)j, blk, num_blocks);
     }
   }
+  // the shared-prefix hint: the same leading blocks in every row with new tokens
+  const int32_t np = b->num_common_prefix_blocks;
+  int32_t first = -1;
+  for (int32_t i = 0; i < b->num_seqs && np > 0; ++i) {
+    if (b->query_start_loc_host[i + 1] == b->query_start_loc_host[i]) continue;
+    if (np > b->bt_stride) return fail(PA_ERR_VALIDATION, "num_common_prefix_blocks %d > bt_stride", np);
+    if (first < 0) {
+      first = i;
+      continue;
+    }
+    for (int32_t j = 0; j < np; ++j)
+      if (bt[(size_t)i * b->bt_stride + j] != bt[(size_t)first * b->bt_stride + j])
+        return fail(PA_ERR_VALIDATION, "block_table[%d][%d] differs from request %d inside the common prefix", i, j, first);
+  }
   return PA_OK;
 }
 
@@ -275,9 +290,14 @@ struct Plan {
   std::vector<DecodeItem> dec;
   std::vector<MergeItem> merge;
   std::vector<ExtendItem> ext;
+  // shared-prefix (cascade) pass
+  std::vector<PrefixItem> pre;
+  std::vector<int32_t> row_token, row_slot0;
+  int32_t prefix_req = -1;                       // request whose block-table row supplies the prefix
   int32_t n_slots = 0;
   int32_t part_len = 0;
-  size_t off_dec = 0, off_merge = 0, off_ext = 0, off_ml = 0, off_o = 0, bytes = 0;
+  size_t off_dec = 0, off_merge = 0, off_ext = 0, off_pre = 0, off_rtok = 0, off_rslot = 0;
+  size_t off_ml = 0, off_o = 0, bytes = 0;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -301,20 +321,51 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
   const bool ext_ok = extend_supported(p, q_dtype) && env_flag("PA_DISABLE_EXTEND") == false;
   const int ext_min = extend_min_rows();
 
+  // Shared prefix (cascade): the split-K rows' first P keys are the same
+  // blocks for every request; their attention over them is computed once per
+  // kv head by the MFMA prefix pass and merged with the rest.  Used when
+  // every split-K request holds the prefix wholly in its history.
+  const int32_t P = b.num_common_prefix_blocks * kBlock;
+  bool cascade = P > 0 && extend_supported(p, q_dtype) && !env_flag("PA_DISABLE_CASCADE") &&
+                 (int64_t)b.num_tokens * Hq * p.head_dim * 2 < ((int64_t)1 << 32);
+  int32_t prefix_rows = 0;
+  for (int32_t i = 0; i < b.num_seqs && cascade; ++i) {
+    const int32_t c = q[i + 1] - q[i];
+    if (c == 0 || (ext_ok && c >= ext_min)) continue;
+    if (L[i] - c < P) cascade = false;
+    if (plan.prefix_req < 0) plan.prefix_req = i;
+    prefix_rows += c;
+  }
+  if (prefix_rows == 0) cascade = false;
+  if (!cascade) plan.prefix_req = -1;
+  const int32_t kstart = cascade ? P : 0;        // first key of the split-K rows' own work
+
   // total key work of the split-K rows, to size partitions so that the whole
   // launch has about 16 waves per compute unit
   int64_t key_work = 0;
   for (int32_t i = 0; i < b.num_seqs; ++i) {
     const int32_t c = q[i + 1] - q[i];
     if (c == 0 || (ext_ok && c >= ext_min)) continue;
-    for (int32_t t = 0; t < c; ++t) key_work += causal ? (L[i] - c + t + 1) : L[i];
+    for (int32_t t = 0; t < c; ++t) key_work += (causal ? (L[i] - c + t + 1) : L[i]) - kstart;
   }
   const int64_t target_waves = 256 * 16;
   int64_t part = (key_work * Hkv + target_waves - 1) / target_waves;
   part = ((part + kKeysPerIter - 1) / kKeysPerIter) * kKeysPerIter;
-  part = std::max<int64_t>(part, 256);
+  part = std::max<int64_t>(part, 64);
   if (const char *v = getenv("PA_PARTITION_KEYS")) part = std::max(64, atoi(v) / 64 * 64);
   plan.part_len = (int32_t)part;
+
+  // prefix chunks: about one workgroup per compute unit over kv heads x
+  // column blocks x chunks (a workgroup costs several microseconds to start
+  // and finish, so one round of longer chunks beats two of shorter ones)
+  int32_t n_kc = 0, kc_len = 0;
+  if (cascade) {
+    const int64_t ncb = ((int64_t)prefix_rows * g + kExtCols - 1) / kExtCols;
+    const int64_t max_kc = (P + 63) / 64;
+    n_kc = (int32_t)std::min<int64_t>(max_kc, std::max<int64_t>(1, 256 / (Hkv * ncb)));
+    kc_len = (int32_t)(((P + n_kc - 1) / n_kc + 63) / 64 * 64);
+    n_kc = (P + kc_len - 1) / kc_len;
+  }
 
   for (int32_t i = 0; i < b.num_seqs; ++i) {
     const int32_t c = q[i + 1] - q[i];
@@ -329,6 +380,19 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
     for (int32_t t = 0; t < c; ++t) {
       const int32_t tok = q[i] + t;
       const int32_t nvis = causal ? (L[i] - c + t + 1) : L[i];
+      if (cascade) {
+        // slots: the prefix chunks, then the partitions of keys [P, nvis)
+        const int32_t nparts = (int32_t)((nvis - P + part - 1) / part);
+        plan.row_token.push_back(tok);
+        plan.row_slot0.push_back(plan.n_slots);
+        plan.merge.push_back(MergeItem{tok, plan.n_slots, n_kc + nparts, 0});
+        for (int32_t r = 0; r < nparts; ++r) {
+          const int32_t b0 = (int32_t)(P + r * part), b1 = (int32_t)std::min<int64_t>(nvis, P + (r + 1) * part);
+          plan.dec.push_back(DecodeItem{tok, i, b0, b1, plan.n_slots + n_kc + r, {0, 0, 0}});
+        }
+        plan.n_slots += n_kc + nparts;
+        continue;
+      }
       const int32_t nparts = (int32_t)((nvis + part - 1) / part);
       if (nparts <= 1) {
         plan.dec.push_back(DecodeItem{tok, i, 0, nvis, -1, {0, 0, 0}});
@@ -368,6 +432,27 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
     }
   }
 
+  // Prefix items: all chunks of one kv head read the same blocks, so each kv
+  // head is pinned to one XCD (workgroup b runs on XCD b % 8).
+  if (cascade) {
+    constexpr int kXcds = 8;
+    std::vector<std::vector<PrefixItem>> qx(kXcds);
+    const int32_t cols = prefix_rows * g;
+    for (int kvh = 0; kvh < Hkv; ++kvh)
+      for (int32_t c0 = 0; c0 < cols; c0 += kExtCols)
+        for (int32_t kc = 0; kc < n_kc; ++kc)
+          qx[kvh % kXcds].push_back(PrefixItem{kvh, c0, kc * kc_len, std::min(P, (kc + 1) * kc_len), kc, {0, 0, 0}});
+    std::vector<size_t> pos(kXcds, 0);
+    for (bool more = true; more;) {
+      more = false;
+      for (int x = 0; x < kXcds; ++x)
+        if (pos[x] < qx[x].size()) {
+          plan.pre.push_back(qx[x][pos[x]++]);
+          more = true;
+        }
+    }
+  }
+
   size_t off = 0;
   plan.off_dec = off;
   off = align256(off + plan.dec.size() * sizeof(DecodeItem));
@@ -375,6 +460,12 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
   off = align256(off + plan.merge.size() * sizeof(MergeItem));
   plan.off_ext = off;
   off = align256(off + plan.ext.size() * sizeof(ExtendItem));
+  plan.off_pre = off;
+  off = align256(off + plan.pre.size() * sizeof(PrefixItem));
+  plan.off_rtok = off;
+  off = align256(off + plan.row_token.size() * sizeof(int32_t));
+  plan.off_rslot = off;
+  off = align256(off + plan.row_slot0.size() * sizeof(int32_t));
   plan.off_ml = off;
   off = align256(off + (size_t)plan.n_slots * Hq * 2 * sizeof(float));
   plan.off_o = off;
@@ -505,6 +596,11 @@ pa_status pa_attention(const pa_kv_pool *pool, const pa_batch *batch, const void
     if (!plan.dec.empty()) memcpy(host + plan.off_dec, plan.dec.data(), plan.dec.size() * sizeof(DecodeItem));
     if (!plan.merge.empty()) memcpy(host + plan.off_merge, plan.merge.data(), plan.merge.size() * sizeof(MergeItem));
     if (!plan.ext.empty()) memcpy(host + plan.off_ext, plan.ext.data(), plan.ext.size() * sizeof(ExtendItem));
+    if (!plan.pre.empty()) {
+      memcpy(host + plan.off_pre, plan.pre.data(), plan.pre.size() * sizeof(PrefixItem));
+      memcpy(host + plan.off_rtok, plan.row_token.data(), plan.row_token.size() * sizeof(int32_t));
+      memcpy(host + plan.off_rslot, plan.row_slot0.data(), plan.row_slot0.size() * sizeof(int32_t));
+    }
     if (env_flag("PA_PLAN_UPLOAD")) {
       hipError_t ce = hipMemcpyAsync(workspace, host, plan_bytes, hipMemcpyHostToDevice, s);
       if (ce != hipSuccess) return hip_fail(ce, "plan upload");
@@ -549,6 +645,30 @@ pa_status pa_attention(const pa_kv_pool *pool, const pa_batch *batch, const void
     x.v_scale = vscale;
     e = launch_extend(*pool, x, xs);
     if (e != hipSuccess) return hip_fail(e, "k_extend launch");
+  }
+  if (!plan.pre.empty()) {
+    ExtendArgs x{};
+    x.q = query;
+    x.k_cache = pool->k_cache;
+    x.v_cache = pool->v_cache;
+    x.pitems = (const PrefixItem *)(items + plan.off_pre);
+    x.row_token = (const int32_t *)(items + plan.off_rtok);
+    x.row_slot0 = (const int32_t *)(items + plan.off_rslot);
+    x.prefix_bt = batch->block_table + (int64_t)plan.prefix_req * batch->bt_stride;
+    x.part_ml = (float *)(ws + plan.off_ml);
+    x.part_o = (float *)(ws + plan.off_o);
+    x.prefix_cols = (int32_t)plan.row_token.size() * g_total;
+    x.n_items = (int32_t)plan.pre.size();
+    x.num_blocks = pool->num_blocks;
+    x.num_kv_heads = pool->num_kv_heads;
+    x.num_q_heads = num_q_heads;
+    x.g = g_total;
+    x.causal = 0;
+    x.scale_log2 = softmax_scale * log2e * kscale;
+    x.k_scale = kscale;
+    x.v_scale = vscale;
+    e = launch_prefix(*pool, x, s);
+    if (e != hipSuccess) return hip_fail(e, "k_prefix launch");
   }
   if (!plan.dec.empty()) {
     DecodeArgs a{};

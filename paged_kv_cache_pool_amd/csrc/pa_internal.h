@@ -50,6 +50,19 @@ struct ExtendItem {
   int32_t pad[2];
 };
 
+// One workgroup of the shared-prefix (cascade) pass: columns [col0, col0 +
+// kExtCols) of the prefix rows of kv head `kvh`, where column k is (prefix row
+// k / g, q head k % g), over keys [key0, key1) of the common prefix; the
+// result is the partial (m, l, o) at slot row_slot0[row] + kc.
+struct PrefixItem {
+  int32_t kvh;
+  int32_t col0;
+  int32_t key0;
+  int32_t key1;
+  int32_t kc;
+  int32_t pad[3];
+};
+
 struct DecodeArgs {
   const void *q;          // [T][Hq][D]
   void *out;              // [T][Hq][D]
@@ -88,6 +101,14 @@ struct ExtendArgs {
   const void *v_cache;
   const int32_t *block_table;
   const ExtendItem *items;
+  // shared-prefix pass only
+  const PrefixItem *pitems;
+  const int32_t *row_token;   // token (flat row) of each prefix row
+  const int32_t *row_slot0;   // first partial slot of each prefix row
+  const int32_t *prefix_bt;   // block-table row whose leading entries are the common prefix
+  float *part_ml;             // [slots][Hq][2]
+  float *part_o;              // [slots][Hq][D]
+  int32_t prefix_cols;        // prefix rows x g
   int32_t n_items;
   int32_t bt_stride;
   int32_t num_blocks;
@@ -111,6 +132,7 @@ hipError_t launch_decode(const pa_kv_pool &p, pa_dtype q_dtype, const DecodeArgs
                          int g_tmpl, hipStream_t s);
 hipError_t launch_merge(pa_dtype q_dtype, int head_dim, const MergeArgs &a, hipStream_t s);
 hipError_t launch_extend(const pa_kv_pool &p, const ExtendArgs &a, hipStream_t s);
+hipError_t launch_prefix(const pa_kv_pool &p, const ExtendArgs &a, hipStream_t s);
 
 // Kernel timing hooks (no-ops unless profiling is enabled).
 void prof_begin(const char *name, hipStream_t s);

@@ -25,7 +25,7 @@ def to_device(a: np.ndarray, io_dtype: str, device="cuda") -> torch.Tensor:
 
 class GpuStep:
     def __init__(self, w: Workload, device: str = "cuda", canary: bool = True, causal: bool = True,
-                 stream: Optional[torch.cuda.Stream] = None):
+                 stream: Optional[torch.cuda.Stream] = None, shared_prefix: bool = True):
         self.w, self.device, self.causal = w, device, causal
         self.stream = stream or torch.cuda.current_stream()
         self.pool = B.KVPool.allocate(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim,
@@ -39,7 +39,10 @@ class GpuStep:
                 B.write_kv(self.pool, to_device(h.key, w.io_dtype, device),
                            to_device(h.value, w.io_dtype, device), slots, stream=self.stream)
             qsl, sl = B.prepare_metadata(w.num_computed, w.num_scheduled)
-            self.batch = B.Batch.from_host(qsl, sl, w.block_table, device)
+            # the workload's common prefix (blocks every request starts with) is
+            # passed as the scheduler's shared-prefix hint unless disabled
+            npref = w.shared_prefix_blocks if shared_prefix else 0
+            self.batch = B.Batch.from_host(qsl, sl, w.block_table, device, num_common_prefix_blocks=npref)
             self.query = to_device(w.query, w.io_dtype, device)
             self.key = to_device(w.key, w.io_dtype, device)
             self.value = to_device(w.value, w.io_dtype, device)

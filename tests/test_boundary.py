@@ -171,6 +171,25 @@ def test_write_and_slots_reject_bad_arguments(B):
     assert B.lib.pa_slot_mapping(None, 16, 0x9000, None) == 1
 
 
+def test_shared_prefix_hint_sizes_workspace(B):
+    """A usable shared-prefix hint adds the prefix partial slots to the
+    workspace; an unusable one (prefix beyond a request's history) is ignored;
+    a negative one is rejected."""
+    p = _pool(B)
+    qsl = np.array([0, 1, 2, 3], np.int32)
+    sl = np.array([300, 200, 100], np.int32)
+    base = B.PaBatch(3, 3, 0x3000, 0x4000, 0x5000, 32, qsl.ctypes.data, sl.ctypes.data, 0)
+    n0 = B.lib.pa_attention_workspace_bytes(C.byref(p), C.byref(base), 32)
+    hint = B.PaBatch(3, 3, 0x3000, 0x4000, 0x5000, 32, qsl.ctypes.data, sl.ctypes.data, 4)
+    n1 = B.lib.pa_attention_workspace_bytes(C.byref(p), C.byref(hint), 32)
+    assert n1 > n0 > 0
+    big = B.PaBatch(3, 3, 0x3000, 0x4000, 0x5000, 32, qsl.ctypes.data, sl.ctypes.data, 7)
+    assert B.lib.pa_attention_workspace_bytes(C.byref(p), C.byref(big), 32) == n0
+    neg = B.PaBatch(3, 3, 0x3000, 0x4000, 0x5000, 32, qsl.ctypes.data, sl.ctypes.data, -1)
+    assert B.lib.pa_attention_workspace_bytes(C.byref(p), C.byref(neg), 32) == 0
+    assert "prefix" in B.lib.pa_last_error().decode()
+
+
 def test_empty_calls_are_no_ops(B):
     p = _pool(B)
     assert B.lib.pa_write_kv(C.byref(p), None, None, 1, None, 0, None) == 0

@@ -304,6 +304,65 @@ def test_page_mixed_batch(R):
     _check_attention(w, step)
 
 
+# ------------------------------------------------------ shared prefix ------
+
+def _cascade_workload(kv, g, seed=11):
+    """Seven requests sharing a 3-block prefix: five decodes (own history 0 ..
+    60 tokens), a 3-token chunk (split-K rows, also cascaded) and a 20-token
+    chunk (MFMA prefill rows, not cascaded)."""
+    own = [0, 1, 17, 33, 60, 9, 5]
+    ns = [1, 1, 1, 1, 1, 3, 20]
+    nc = [48 + o for o in own]
+    return W.build(f"casc_{kv}_{g}", seed, num_q_heads=2 * g, num_kv_heads=2, head_dim=128,
+                   block_size=16, num_blocks=80, kv_dtype=kv, io_dtype=W.BF16, num_computed=nc,
+                   num_scheduled=ns, shared_prefix_tokens=48)
+
+
+@pytest.mark.parametrize("kv", [W.BF16, W.FP8])
+@pytest.mark.parametrize("g", [1, 4, 8])
+def test_cascade_shared_prefix(R, kv, g):
+    """Cascade attention: the rows' attention over the shared prefix comes from
+    the MFMA prefix pass and is merged with their own keys; equal to the
+    oracle (plain attention), with and without the hint."""
+    say("cascade", kv, "g", g)
+    w = _cascade_workload(kv, g)
+    assert w.shared_prefix_blocks == 3
+    for hint in (True, False):
+        step = R.GpuStep(w, shared_prefix=hint)
+        step.run()
+        torch.cuda.synchronize()
+        _check_attention(w, step)
+
+
+def test_cascade_hint_ignored_when_not_history(R):
+    """A hint that no request can honour (more prefix blocks than any request
+    holds in its history) is ignored: the result is still the oracle's."""
+    say("cascade hint ignored")
+    from paged_kv_cache_pool_amd import binding as B
+    w = _cascade_workload(W.BF16, 4)
+    step = R.GpuStep(w)
+    step.batch.num_common_prefix_blocks = 50
+    step.run()
+    torch.cuda.synchronize()
+    _check_attention(w, step)
+    assert B.attention_workspace_bytes(step.pool, step.batch, w.num_q_heads) > 0
+
+
+def test_cascade_wrong_hint_rejected_under_validation(R, monkeypatch):
+    """With PA_VALIDATE the block tables are checked against the hint."""
+    say("cascade wrong hint")
+    from paged_kv_cache_pool_amd import binding as B
+    w = W.build("casc_bad", 5, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                num_blocks=40, kv_dtype=W.BF16, io_dtype=W.BF16, num_computed=[40, 50],
+                num_scheduled=[1, 1])
+    step = R.GpuStep(w)
+    step.batch.num_common_prefix_blocks = 2      # the two requests' blocks differ
+    monkeypatch.setenv("PA_VALIDATE", "1")
+    with pytest.raises(B.PaError) as e:
+        step.run()
+    assert e.value.status == 4
+
+
 # ------------------------------------------------------------ MFMA extend --
 
 @pytest.mark.parametrize("g", [1, 2, 4, 8])
