@@ -33,7 +33,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -45,6 +45,9 @@ def parse():
                          "this workload, then of --copy-calibration) into the traffic record of "
                          "the dominant kernel under profiles/, and exit")
     ap.add_argument("--kernel", default="k_decode", help="kernel for --traffic-ingest")
+    ap.add_argument("--separate", action="store_true",
+                    help="time the step as three calls (slot derivation, KV write, attention) "
+                         "instead of the one call that includes the KV update")
     ap.add_argument("--cold", action="store_true",
                     help="also time steps that start with cold caches (a 1 GiB scratch read "
                          "before each step, outside the timed events)")
@@ -181,11 +184,14 @@ def cascade_prefix(w, seq_lens, qsl, ext_min_rows=16, extend_on=True, hint=True)
     return P if rows else 0
 
 
-def algorithmic_work(w, seq_lens, qsl, ext_min_rows=16, extend_on=True, prefix=0):
+def algorithmic_work(w, seq_lens, qsl, ext_min_rows=16, extend_on=True, prefix=0, fused=False):
     """Bytes the split-K decode kernel must move, flops the extend kernel must
     do and flops of the shared-prefix pass, per step, by the per-unit formulas
     in the design notes.  With a shared prefix of `prefix` keys taken over by
-    the cascade pass, the split-K rows' bytes count their own keys only."""
+    the cascade pass, the split-K rows' bytes count their own keys only.  In
+    the step with the KV update (`fused`), a decode row of a one-token request
+    takes its newest key from the input rows and also writes them to the
+    pool."""
     b_kv, b_io = ELEM[w.kv_dtype], ELEM[w.io_dtype]
     H, Hq, D, S = w.num_kv_heads, w.num_q_heads, w.head_dim, w.block_size
     dec_bytes = 0
@@ -204,6 +210,8 @@ def algorithmic_work(w, seq_lens, qsl, ext_min_rows=16, extend_on=True, prefix=0
             for t in range(c):
                 Lv = L - c + t + 1
                 dec_bytes += (Lv - prefix) * H * D * 2 * b_kv + Hq * D * b_io + (-(-Lv // S) - prefix // S) * 4
+                if fused and c == 1:
+                    dec_bytes += H * D * 2 * (b_io - b_kv) + H * D * 2 * b_kv
                 pre_flops += 4 * Hq * D * prefix
     return dec_bytes, ext_flops, ext_bytes, pre_flops
 
@@ -256,7 +264,7 @@ def main():
     w = W.make(a.config, a.seed)
     print(f"[bench] workload {w.name}: generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream()
-    step = runner.GpuStep(w, stream=stream)
+    step = runner.GpuStep(w, stream=stream, fused=not a.separate)
     print(f"[bench] device set-up done ({time.time() - t0:.1f}s)", file=sys.stderr, flush=True)
 
     for _ in range(a.warmup):
@@ -275,7 +283,8 @@ def main():
     torch.cuda.synchronize()
     ms_instr = ev0.elapsed_time(ev1) / a.steps
     kernels = {}
-    for name in ("k_slot_mapping", "k_write_kv", "k_prefix", "k_decode", "k_merge", "k_extend"):
+    for name in ("k_slot_mapping", "k_write_kv", "k_write_new", "k_prefix", "k_decode", "k_merge",
+                 "k_extend"):
         n, ms = B.profile_read(name)
         if n:
             kernels[name] = {"launches": n, "avg_us": 1000.0 * ms / n}
@@ -295,6 +304,22 @@ def main():
     spread = {"p10": round(float(np.percentile(per_step, 10)), 5),
               "p50": round(float(np.percentile(per_step, 50)), 5),
               "p90": round(float(np.percentile(per_step, 90)), 5)}
+    # the other form of the step on the same pool and inputs (the KV write is
+    # idempotent), for comparison
+    other = None
+    step.fused = a.separate
+    for _ in range(3):
+        step.run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(a.steps):
+        step.run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    other = round(e0.elapsed_time(e1) / a.steps, 5)
+    step.fused = not a.separate
+
     cold = None
     if a.cold:
         # each step starts after a 1 GiB read, so L2 and the 256 MB Infinity
@@ -322,7 +347,7 @@ def main():
     ext_min = int(os.environ.get("PA_EXTEND_MIN_ROWS", "16"))
     prefix = cascade_prefix(w, sl, qsl, ext_min, ext_on, hint=step.batch.num_common_prefix_blocks > 0)
     dec_bytes, ext_flops, ext_bytes, pre_flops = algorithmic_work(
-        w, sl, qsl, ext_min, ext_on and "k_extend" in kernels, prefix)
+        w, sl, qsl, ext_min, ext_on and "k_extend" in kernels, prefix, fused=not a.separate)
 
     if "k_decode" in kernels and (dec_bytes > 0):
         dom = "k_decode"
@@ -374,6 +399,8 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels_us": {k: round(v["avg_us"], 2) for k, v in kernels.items()},
+        "step_form": "separate calls" if a.separate else "one call with the KV update",
+        ("ms_per_step_one_call" if a.separate else "ms_per_step_separate_calls"): other,
         "ms_per_step_with_kernel_events": round(ms_instr, 5),
         "ms_per_step_spread": spread,
         "decode_kv_gbps": roof["achieved"] if roof["unit"] == "GB/s" else None,

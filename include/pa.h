@@ -167,8 +167,9 @@ pa_status pa_write_kv(const pa_kv_pool *pool, const void *key, const void *value
                       pa_dtype in_dtype, const int64_t *slot_mapping, int32_t num_tokens,
                       pa_stream_t stream);
 
-/* Device workspace pa_attention needs for this batch (bytes), or 0 when the
- * arguments are invalid (pa_last_error() says why). */
+/* Device workspace pa_attention and pa_write_kv_attention need for this
+ * batch (bytes), or 0 when the arguments are invalid (pa_last_error() says
+ * why). */
 size_t pa_attention_workspace_bytes(const pa_kv_pool *pool, const pa_batch *batch,
                                     int32_t num_q_heads);
 
@@ -193,6 +194,31 @@ pa_status pa_attention(const pa_kv_pool *pool, const pa_batch *batch, const void
                        pa_dtype q_dtype, int32_t num_q_heads, float softmax_scale,
                        int32_t causal, void *output, void *workspace, size_t workspace_bytes,
                        pa_stream_t stream);
+
+/* a1 + a2 + a3..a7 in one call: the attention whose forward includes the KV
+ * cache update ([P1] §6.1: a backend may write the new K/V inside its own
+ * forward instead of through a separate cache-update step).  The result is
+ * that of
+ *   pa_slot_mapping(batch, 16, slot_mapping);
+ *   pa_write_kv(pool, key, value, q_dtype, slot_mapping, num_tokens);
+ *   pa_attention(pool, batch, query, q_dtype, ...);
+ * on the same stream: the pool receives exactly the same bytes, and the
+ * attention reads the new keys as the pool holds them (quantised for FP8
+ * pools).  The output may differ from pa_attention's in the last bits,
+ * because the kernels may add a request's newest key in another order.
+ * key, value: device [num_tokens][num_kv_heads][head_dim] in q_dtype (BF16
+ * for BF16 and FP8 pools, F32 for F32 pools).  slot_mapping: device int64
+ * [num_tokens], written with the slots of the new tokens, or NULL.  The
+ * other arguments, the workspace (pa_attention_workspace_bytes() covers both
+ * calls) and the errors are those of pa_attention; on an error nothing is
+ * written.  A request's new tokens must go to slots that no other request
+ * of the batch reads (a block receiving new tokens belongs to one request,
+ * as any KV-cache manager arranges); otherwise the result is undefined. */
+pa_status pa_write_kv_attention(const pa_kv_pool *pool, const pa_batch *batch, const void *query,
+                                const void *key, const void *value, pa_dtype q_dtype,
+                                int32_t num_q_heads, float softmax_scale, int32_t causal,
+                                int64_t *slot_mapping, void *output, void *workspace,
+                                size_t workspace_bytes, pa_stream_t stream);
 
 /* Bytes of each of k_cache and v_cache for this pool's shape and dtype. */
 size_t pa_kv_cache_bytes(const pa_kv_pool *pool);

@@ -27,7 +27,8 @@ STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED", 3: "PA_E
 
 # Every symbol include/pa.h declares.
 EXPORTS = ["pa_prepare_metadata", "pa_slot_mapping", "pa_write_kv", "pa_attention_workspace_bytes",
-           "pa_attention", "pa_kv_cache_bytes", "pa_kv_elem_offset", "pa_status_string",
+           "pa_attention", "pa_write_kv_attention", "pa_kv_cache_bytes", "pa_kv_elem_offset",
+           "pa_status_string",
            "pa_last_error", "pa_profile_enable", "pa_profile_read"]
 
 
@@ -63,6 +64,8 @@ def _load():
         "pa_write_kv": (i32, [pool_p, P, P, i32, P, i32, P]),
         "pa_attention_workspace_bytes": (C.c_size_t, [pool_p, batch_p, i32]),
         "pa_attention": (i32, [pool_p, batch_p, P, i32, i32, f32, i32, P, P, C.c_size_t, P]),
+        "pa_write_kv_attention": (i32, [pool_p, batch_p, P, P, P, i32, i32, f32, i32, P, P, P,
+                                        C.c_size_t, P]),
         "pa_kv_cache_bytes": (C.c_size_t, [pool_p]),
         "pa_kv_elem_offset": (i64, [pool_p, i32, i64, i32, i32, i32]),
         "pa_status_string": (C.c_char_p, [i32]),
@@ -247,6 +250,28 @@ def attention(pool: KVPool, batch: Batch, query: torch.Tensor, num_q_heads: int,
     _check(lib.pa_attention(C.byref(p), C.byref(b), _ptr(query), torch_dtype_code(query),
                             num_q_heads, softmax_scale, int(causal), _ptr(out), _ptr(workspace),
                             workspace.numel(), _stream(stream)))
+    return out
+
+
+def write_kv_attention(pool: KVPool, batch: Batch, query: torch.Tensor, key: torch.Tensor,
+                       value: torch.Tensor, num_q_heads: int, softmax_scale: float,
+                       causal: bool = True, out: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None,
+                       slots: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """pa_write_kv_attention: the KV update and the attention in one call."""
+    assert query.is_contiguous() and key.is_contiguous() and value.is_contiguous()
+    assert key.dtype == query.dtype and value.dtype == query.dtype
+    assert slots is None or (slots.dtype == torch.int64 and slots.is_contiguous())
+    if out is None:
+        out = torch.empty_like(query)
+    if workspace is None:
+        workspace = torch.empty(attention_workspace_bytes(pool, batch, num_q_heads),
+                                dtype=torch.uint8, device=query.device)
+    p, b = pool.struct(), batch.struct()
+    _check(lib.pa_write_kv_attention(C.byref(p), C.byref(b), _ptr(query), _ptr(key), _ptr(value),
+                                     torch_dtype_code(query), num_q_heads, softmax_scale,
+                                     int(causal), _ptr(slots), _ptr(out), _ptr(workspace),
+                                     workspace.numel(), _stream(stream)))
     return out
 
 

@@ -64,6 +64,66 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
   const char *__restrict__ qbase = (const char *)a.q + ((int64_t)token * a.num_q_heads + qh0) * D *
                                                            (KV == KV_F32 ? 4 : 2);
 
+  // KV update (items with wpos >= 0): the row is its request's only new
+  // token, at position wpos = kv_end - 1.  The key loop below stops before
+  // it; the new key then enters the softmax as one more step, with the value
+  // the pool will hold (the scatter's own encoding), and its K/V rows are
+  // stored into the pool at the end.  No wave reads that slot in this launch.
+  // The new key's inputs are loaded here, before the loop, so that their
+  // latency overlaps the loop's first loads; they are used after the loop.
+  // Lane l handles K/V dims l + 64 j of the new rows, and the V dims of its
+  // own accumulators.
+  const int wpos = uniform(item.wpos);
+  const bool wnew = wpos >= 0 && a.knew != nullptr;
+  const int kv_last = wnew ? kv_end - 1 : kv_end;   // end of the keys read from the pool
+  constexpr int IN = KV == KV_F32 ? KV_F32 : KV_BF16;  // new rows come in the query dtype
+  constexpr int IB = KvTraits<IN>::bytes;
+  constexpr int KD = D / 64;
+  constexpr bool VSAME = VPR == 1 && DSTEP == 64 && NVL == KD;  // accumulator dims = l + 64 j
+  constexpr int NO = VSAME ? 1 : NVL;
+  constexpr bool QPRE = KV != KV_F32 && G <= 8;      // q of the new key also loaded early
+  auto load_in = [](const char *row, int e) -> uint32_t {
+    if constexpr (IB == 2) return ((const uint16_t *)row)[e];
+    else return ((const uint32_t *)row)[e];
+  };
+  // (seeded with a run-time zero, not a constant, so that the compiler does
+  // not fold the later conversions into this branch and wait for the loads)
+  uint32_t kraw[KD], vraw[KD], oraw[NO], qraw[QPRE ? G : 1][KD];
+  const uint32_t rz = (uint32_t)a.zero;
+#pragma unroll
+  for (int j2 = 0; j2 < KD; ++j2) kraw[j2] = vraw[j2] = rz;
+#pragma unroll
+  for (int i = 0; i < NO; ++i) oraw[i] = rz;
+#pragma unroll
+  for (int h = 0; h < (QPRE ? G : 1); ++h)
+#pragma unroll
+    for (int j2 = 0; j2 < KD; ++j2) qraw[h][j2] = rz;
+  const char *krow = (const char *)a.knew, *vrow = (const char *)a.vnew;
+  // block of the new slot (a block id outside the pool: no write and no key,
+  // as for a key the loop reads; the separate scatter skips such slots too)
+  const int wblk = wnew ? btrow[wpos / kBlock] : -1;
+  if (wnew) {
+    const int64_t th = (int64_t)token * a.num_kv_heads + kvh;
+    krow += th * D * IB;
+    vrow += th * D * IB;
+#pragma unroll
+    for (int j2 = 0; j2 < KD; ++j2) {
+      kraw[j2] = load_in(krow, lane + 64 * j2);
+      vraw[j2] = load_in(vrow, lane + 64 * j2);
+    }
+    if constexpr (!VSAME) {
+#pragma unroll
+      for (int i = 0; i < NVL; ++i) oraw[i] = load_in(vrow, i * DSTEP + lane / VPR);
+    }
+    if constexpr (QPRE) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int j2 = 0; j2 < KD; ++j2)
+          qraw[h][j2] = load_in(qbase + ((int64_t)(h < g ? h : 0) * D + lane + 64 * j2) * IB, 0);
+    }
+  }
+
   float m_run[G], l_run[G], o[G][NVL];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -73,13 +133,13 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
     for (int i = 0; i < NVL; ++i) o[h][i] = 0.0f;
   }
 
-  for (int it = kv_begin; it < kv_end; it += kKeysPerIter) {
+  for (int it = kv_begin; it < kv_last; it += kKeysPerIter) {
     const int tl = lane >> 4;                       // which of the 4 blocks
     const int j = it + lane;                        // this lane's key position
-    const bool tile_in = (it + tl * kBlock) < kv_end;
+    const bool tile_in = (it + tl * kBlock) < kv_last;
     int phys = tile_in ? btrow[(it >> 4) + tl] : -1;
     if (phys >= a.num_blocks) phys = -1;            // out-of-range id: never dereferenced
-    const bool key_ok = phys >= 0 && j < kv_end;
+    const bool key_ok = phys >= 0 && j < kv_last;
 
     // ---- K row of this lane's key ----
     uint4 kr[NCH];
@@ -167,7 +227,7 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // ---- PV ----
-    const bool tail = it + kKeysPerIter > kv_end;
+    const bool tail = it + kKeysPerIter > kv_last;
     const int key0 = (lane % VPR) * KPV;            // first key (in block) of this lane's vectors
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -200,7 +260,7 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
         if (tail) {
 #pragma unroll
           for (int k = 0; k < KPV; ++k)
-            if (kpos0 + k >= kv_end) v[i][k] = 0.0f;  // unwritten slots may hold anything
+            if (kpos0 + k >= kv_last) v[i][k] = 0.0f;  // unwritten slots may hold anything
         }
       }
 #pragma unroll
@@ -228,6 +288,67 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
+  // ---- the new key (KV update), then its rows into the pool ----
+  if (wnew && kvh == 0 && lane == 0 && a.slots_out)
+    a.slots_out[token] = (int64_t)wblk * kBlock + wpos % kBlock;
+  if (wnew && wblk >= 0 && wblk < a.num_blocks) {
+    uint32_t kbits[KD], vbits[KD];
+    float kval[KD], vval[NVL];
+#pragma unroll
+    for (int j2 = 0; j2 < KD; ++j2) {
+      kbits[j2] = pool_bits<IN, KV>(kraw[j2], a.enc_k_scale);
+      vbits[j2] = pool_bits<IN, KV>(vraw[j2], a.enc_v_scale);
+      kval[j2] = pool_value<KV>(kbits[j2]);
+    }
+#pragma unroll
+    for (int i = 0; i < NVL; ++i) {
+      if constexpr (VSAME) vval[i] = pool_value<KV>(vbits[i]);
+      else vval[i] = pool_value<KV>(pool_bits<IN, KV>(oraw[i], a.enc_v_scale));
+    }
+    const bool vlane = lane % VPR == 0;             // one lane per dim adds the new key's p * v
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float sp = 0.0f;
+#pragma unroll
+      for (int j2 = 0; j2 < KD; ++j2) {
+        uint32_t qb;
+        if constexpr (QPRE) qb = qraw[h][j2];
+        else qb = load_in(qbase + ((int64_t)(h < g ? h : 0) * D + lane + 64 * j2) * IB, 0);
+        sp = fmaf(in_to_f32<IN>(qb), kval[j2], sp);
+      }
+      const float sv = wave_sum_dpp(sp) * a.scale_log2;
+      const float mn = fmaxf(m_run[h], sv);
+      const bool any = mn != -INFINITY;
+      const float alpha = any ? __builtin_amdgcn_exp2f(m_run[h] - mn) : 1.0f;
+      const float p = any ? __builtin_amdgcn_exp2f(sv - mn) : 0.0f;
+      l_run[h] = l_run[h] * alpha + (lane == 0 ? p : 0.0f);
+#pragma unroll
+      for (int i = 0; i < NVL; ++i) o[h][i] = o[h][i] * alpha + (vlane ? p * vval[i] : 0.0f);
+      m_run[h] = mn;
+    }
+    // the rows into the pool: element e of the K tile sits in chunk e / E at
+    // position e % E of slot off's 16 bytes; of the V tile, in row e
+    const int off = wpos % kBlock;
+    char *kt = (char *)a.k_store + ((int64_t)wblk * a.num_kv_heads + kvh) * TILE;
+    char *vt = (char *)a.v_store + ((int64_t)wblk * a.num_kv_heads + kvh) * TILE;
+#pragma unroll
+    for (int j2 = 0; j2 < KD; ++j2) {
+      const int e = lane + 64 * j2;
+      char *kd = kt + (e / E) * (kBlock * 16) + off * 16 + (e % E) * PB;
+      char *vd = vt + (e * kBlock + off) * PB;
+      if constexpr (PB == 4) {
+        *(uint32_t *)kd = kbits[j2];
+        *(uint32_t *)vd = vbits[j2];
+      } else if constexpr (PB == 2) {
+        *(uint16_t *)kd = (uint16_t)kbits[j2];
+        *(uint16_t *)vd = (uint16_t)vbits[j2];
+      } else {
+        *(uint8_t *)kd = (uint8_t)kbits[j2];
+        *(uint8_t *)vd = (uint8_t)vbits[j2];
+      }
+    }
+  }
+
   // ---- combine lanes that share dims; totals ----
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -236,7 +357,7 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
 #pragma unroll
       for (int x = 1; x < VPR; x <<= 1) o[h][i] += __shfl_xor(o[h][i], x, 64);
     }
-    l_run[h] = wave_sum(l_run[h]);
+    l_run[h] = wave_sum_dpp(l_run[h]);
   }
 
   if (lane % VPR != 0) return;

@@ -61,11 +61,8 @@ __global__ __launch_bounds__(256) void k_write_kv(const void *__restrict__ key,
                                                   float v_scale) {
   constexpr int IB = KvTraits<IN>::bytes;   // input element bytes
   constexpr int PB = KvTraits<KV>::bytes;   // pool element bytes
-  constexpr int E = 16 / PB;                // pool elements per 16-byte chunk
-  constexpr int NCH = D / E;                // chunks per key row
+  constexpr int NCH = D * PB / 16;          // chunks per key row
   constexpr int TILE = D * kBlock * PB;     // bytes of one (block, head) tile
-  static_assert(IN != KV_FP8, "fp8 is a pool format only");
-  static_assert(KV == KV_FP8 || IN == KV, "same-dtype copy or fp8 encode");
 
   const int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = (int64_t)num_tokens * num_kv_heads * NCH;
@@ -75,44 +72,45 @@ __global__ __launch_bounds__(256) void k_write_kv(const void *__restrict__ key,
   const int h = (int)(th % num_kv_heads);
   const int64_t n = th / num_kv_heads;
   const int64_t slot = slots[n];
-  // input elements c*E .. c*E+E-1 of the token's K and V rows
-  const char *ks = (const char *)key + (th * D + (int64_t)c * E) * IB;
-  const char *vs = (const char *)value + (th * D + (int64_t)c * E) * IB;
-  constexpr int NV = E * IB / 16;           // 16-byte input vectors per chunk
-  uint4 kin[NV], vin[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    kin[i] = ((const uint4 *)ks)[i];
-    vin[i] = ((const uint4 *)vs)[i];
-  }
+  const KvChunkIn<IN, KV> in = load_kv_chunk<IN, KV>((const char *)key + th * D * IB,
+                                                     (const char *)value + th * D * IB, c);
   if (slot < 0 || slot >= capacity) return;  // padding token / out-of-range slot
   const int64_t blk = slot / kBlock;
   const int off = (int)(slot - blk * kBlock);
-  const int64_t tile = (blk * num_kv_heads + h) * (int64_t)TILE;
-  char *kdst = (char *)kc + tile + (int64_t)c * (kBlock * 16) + off * 16;
-  char *vdst = (char *)vc + tile + ((int64_t)c * E * kBlock + off) * PB;  // row c*E, column off
-  if constexpr (KV != KV_FP8) {
-    *(uint4 *)kdst = kin[0];
-    const uint32_t *vw = (const uint32_t *)vin;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      if constexpr (KV == KV_F32) ((uint32_t *)vdst)[e * kBlock] = vw[e];
-      else ((uint16_t *)vdst)[e * kBlock] = (uint16_t)(vw[e / 2] >> (16 * (e & 1)));
-    }
-  } else {
-    const uint32_t *kw = (const uint32_t *)kin, *vw = (const uint32_t *)vin;
-    auto elem = [](const uint32_t *words, int e) -> float {
-      if constexpr (IN == KV_BF16) return __uint_as_float((words[e / 2] >> (16 * (e & 1))) << 16);
-      else return __uint_as_float(words[e]);
-    };
-    uint32_t out[4] = {0, 0, 0, 0};
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      out[e / 4] |= e4m3_encode(elem(kw, e) / k_scale) << (8 * (e & 3));
-      ((uint8_t *)vdst)[e * kBlock] = (uint8_t)e4m3_encode(elem(vw, e) / v_scale);
-    }
-    *(uint4 *)kdst = make_uint4(out[0], out[1], out[2], out[3]);
-  }
+  store_kv_chunk<IN, KV, D>(in, kc, vc, (blk * num_kv_heads + h) * (int64_t)TILE, off, c, k_scale,
+                            v_scale);
+}
+
+// The same scatter with the slots derived on the fly (a1 + a2 in one pass),
+// for the tokens the step's plan lists: token n of request req at position
+// pos goes to slot block_table[req][pos / 16] * 16 + pos % 16, which is also
+// stored to slots_out[n] when that pointer is set.  Used by the attention
+// call that includes the KV update.
+template <int IN, int KV, int D>
+__global__ __launch_bounds__(256) void k_write_new(const WriteArgs a) {
+  constexpr int IB = KvTraits<IN>::bytes;
+  constexpr int PB = KvTraits<KV>::bytes;
+  constexpr int NCH = D * PB / 16;
+  constexpr int TILE = D * kBlock * PB;
+
+  const int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)a.n_toks * a.num_kv_heads * NCH;
+  if (w >= total) return;
+  const int c = (int)(w % NCH);
+  const int64_t wh = w / NCH;               // list entry * num_kv_heads + head
+  const int h = (int)(wh % a.num_kv_heads);
+  const WriteTok t = a.toks[wh / a.num_kv_heads];
+  const int64_t slot =
+      (int64_t)a.block_table[(int64_t)t.req * a.bt_stride + t.pos / kBlock] * kBlock + t.pos % kBlock;
+  if (a.slots_out && h == 0 && c == 0) a.slots_out[t.token] = slot;
+  const int64_t th = (int64_t)t.token * a.num_kv_heads + h;
+  const KvChunkIn<IN, KV> in = load_kv_chunk<IN, KV>((const char *)a.key + th * D * IB,
+                                                     (const char *)a.value + th * D * IB, c);
+  if (slot < 0 || slot >= a.capacity) return;
+  const int64_t blk = slot / kBlock;
+  const int off = (int)(slot - blk * kBlock);
+  store_kv_chunk<IN, KV, D>(in, a.k_cache, a.v_cache, (blk * a.num_kv_heads + h) * (int64_t)TILE,
+                            off, c, a.k_scale, a.v_scale);
 }
 
 template <int IN, int KV>
@@ -139,6 +137,25 @@ hipError_t launch_write_kv(const pa_kv_pool &p, const void *key, const void *val
   if (p.kv_dtype == PA_BF16) return write_dispatch_d<KV_BF16, KV_BF16>(p, key, value, slots, T, s);
   if (in_dtype == PA_BF16) return write_dispatch_d<KV_BF16, KV_FP8>(p, key, value, slots, T, s);
   return write_dispatch_d<KV_F32, KV_FP8>(p, key, value, slots, T, s);
+}
+
+template <int IN, int KV>
+static hipError_t write_new_d(const pa_kv_pool &p, const WriteArgs &a, hipStream_t s) {
+  const int64_t threads = (int64_t)a.n_toks * p.num_kv_heads * (p.head_dim * KvTraits<KV>::bytes / 16);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  prof_begin("k_write_new", s);
+  if (p.head_dim == 128) hipLaunchKernelGGL((k_write_new<IN, KV, 128>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_write_new<IN, KV, 64>), grid, dim3(256), 0, s, a);
+  prof_end(s);
+  return hipGetLastError();
+}
+
+hipError_t launch_write_new(const pa_kv_pool &p, pa_dtype in_dtype, const WriteArgs &a, hipStream_t s) {
+  if (a.n_toks == 0) return hipSuccess;
+  if (p.kv_dtype == PA_F32) return write_new_d<KV_F32, KV_F32>(p, a, s);
+  if (p.kv_dtype == PA_BF16) return write_new_d<KV_BF16, KV_BF16>(p, a, s);
+  if (in_dtype == PA_BF16) return write_new_d<KV_BF16, KV_FP8>(p, a, s);
+  return write_new_d<KV_F32, KV_FP8>(p, a, s);
 }
 
 }  // namespace pa

@@ -294,9 +294,13 @@ struct Plan {
   std::vector<PrefixItem> pre;
   std::vector<int32_t> row_token, row_slot0;
   int32_t prefix_req = -1;                       // request whose block-table row supplies the prefix
+  // attention that includes the KV update: tokens the plan-driven scatter
+  // writes before the attention kernels (the others are written by their
+  // decode unit, DecodeItem::wpos)
+  std::vector<WriteTok> wtok;
   int32_t n_slots = 0;
   int32_t part_len = 0;
-  size_t off_dec = 0, off_merge = 0, off_ext = 0, off_pre = 0, off_rtok = 0, off_rslot = 0;
+  size_t off_dec = 0, off_merge = 0, off_ext = 0, off_pre = 0, off_rtok = 0, off_rslot = 0, off_wtok = 0;
   size_t off_ml = 0, off_o = 0, bytes = 0;
 };
 
@@ -315,7 +319,7 @@ static bool extend_supported(const pa_kv_pool &p, pa_dtype q_dtype) {
 }
 
 static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dtype q_dtype,
-                       int causal, Plan &plan) {
+                       int causal, bool kv_update, Plan &plan) {
   const int32_t *q = b.query_start_loc_host, *L = b.seq_lens_host;
   const int Hkv = p.num_kv_heads, g = Hq / Hkv;
   const bool ext_ok = extend_supported(p, q_dtype) && env_flag("PA_DISABLE_EXTEND") == false;
@@ -370,6 +374,18 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
   for (int32_t i = 0; i < b.num_seqs; ++i) {
     const int32_t c = q[i + 1] - q[i];
     if (c == 0) continue;
+    // KV update: a split-K request with one new token has it written by the
+    // decode unit that holds its last key; every other new token is written
+    // by the scatter pass that runs before the attention kernels
+    const bool own_write = kv_update && c == 1 && !(ext_ok && c >= ext_min);
+    if (kv_update && !own_write)
+      for (int32_t t = 0; t < c; ++t) plan.wtok.push_back(WriteTok{q[i] + t, i, L[i] - c + t, 0});
+    const size_t dec0 = plan.dec.size();
+    auto mark_own_write = [&]() {
+      if (!own_write) return;
+      for (size_t k = dec0; k < plan.dec.size(); ++k)
+        if (plan.dec[k].kv_end == L[i]) plan.dec[k].wpos = L[i] - 1;
+    };
     if (ext_ok && c >= ext_min) {
       const int64_t cols = (int64_t)c * g;
       for (int kvh = 0; kvh < Hkv; ++kvh)
@@ -388,23 +404,24 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
         plan.merge.push_back(MergeItem{tok, plan.n_slots, n_kc + nparts, 0});
         for (int32_t r = 0; r < nparts; ++r) {
           const int32_t b0 = (int32_t)(P + r * part), b1 = (int32_t)std::min<int64_t>(nvis, P + (r + 1) * part);
-          plan.dec.push_back(DecodeItem{tok, i, b0, b1, plan.n_slots + n_kc + r, {0, 0, 0}});
+          plan.dec.push_back(DecodeItem{tok, i, b0, b1, plan.n_slots + n_kc + r, -1, {0, 0}});
         }
         plan.n_slots += n_kc + nparts;
         continue;
       }
       const int32_t nparts = (int32_t)((nvis + part - 1) / part);
       if (nparts <= 1) {
-        plan.dec.push_back(DecodeItem{tok, i, 0, nvis, -1, {0, 0, 0}});
+        plan.dec.push_back(DecodeItem{tok, i, 0, nvis, -1, -1, {0, 0}});
         continue;
       }
       plan.merge.push_back(MergeItem{tok, plan.n_slots, nparts, 0});
       for (int32_t r = 0; r < nparts; ++r) {
         const int32_t b0 = (int32_t)(r * part), b1 = (int32_t)std::min<int64_t>(nvis, (r + 1) * part);
-        plan.dec.push_back(DecodeItem{tok, i, b0, b1, plan.n_slots + r, {0, 0, 0}});
+        plan.dec.push_back(DecodeItem{tok, i, b0, b1, plan.n_slots + r, -1, {0, 0}});
       }
       plan.n_slots += nparts;
     }
+    mark_own_write();
   }
   // Extend tiles: workgroup b runs on XCD b % 8 (round-robin dispatch), and
   // all tiles of one (request, kv head) read the same K/V, so each (request,
@@ -466,6 +483,8 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
   off = align256(off + plan.row_token.size() * sizeof(int32_t));
   plan.off_rslot = off;
   off = align256(off + plan.row_slot0.size() * sizeof(int32_t));
+  plan.off_wtok = off;
+  off = align256(off + plan.wtok.size() * sizeof(WriteTok));
   plan.off_ml = off;
   off = align256(off + (size_t)plan.n_slots * Hq * 2 * sizeof(float));
   plan.off_o = off;
@@ -555,27 +574,40 @@ size_t pa_attention_workspace_bytes(const pa_kv_pool *pool, const pa_batch *batc
   // the dtype only selects kernels; BF16 gives the largest (extend-capable) plan shape
   const pa_dtype qd = pool && pool->kv_dtype == PA_F32 ? PA_F32 : PA_BF16;
   if (check_attention_args(pool, batch, qd, num_q_heads, false) != PA_OK) return 0;
+  // the plan with the KV update holds every section the plan without it has
   Plan plan;
-  build_plan(*pool, *batch, num_q_heads, qd, 1, plan);
+  build_plan(*pool, *batch, num_q_heads, qd, 1, true, plan);
   Plan plan_nc;
-  build_plan(*pool, *batch, num_q_heads, qd, 0, plan_nc);
+  build_plan(*pool, *batch, num_q_heads, qd, 0, true, plan_nc);
   return std::max(plan.bytes, plan_nc.bytes);
 }
 
-pa_status pa_attention(const pa_kv_pool *pool, const pa_batch *batch, const void *query,
-                       pa_dtype q_dtype, int32_t num_q_heads, float softmax_scale, int32_t causal,
-                       void *output, void *workspace, size_t workspace_bytes, pa_stream_t stream) {
+}  // extern "C"
+
+namespace pa {
+
+// The new rows of the attention call that includes the KV update.
+struct KvUpdate {
+  const void *key;
+  const void *value;
+  int64_t *slot_mapping;   // may be null
+};
+
+static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, const void *query,
+                                pa_dtype q_dtype, int32_t num_q_heads, float softmax_scale,
+                                int32_t causal, void *output, void *workspace,
+                                size_t workspace_bytes, hipStream_t s, const KvUpdate *kvu) {
   pa_status st = check_attention_args(pool, batch, q_dtype, num_q_heads, true);
   if (st != PA_OK) return st;
   if (batch->num_tokens > 0 && (!query || !output)) return fail(PA_ERR_INVALID_ARG, "NULL query/output");
+  if (kvu && batch->num_tokens > 0 && (!kvu->key || !kvu->value)) return fail(PA_ERR_INVALID_ARG, "NULL key/value");
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0f))
     return fail(PA_ERR_INVALID_ARG, "softmax_scale must be finite and positive");
   if (batch->num_tokens == 0) return PA_OK;
-  hipStream_t s = (hipStream_t)stream;
   if (env_flag("PA_VALIDATE") && (st = validate_block_table(batch, pool->num_blocks, s)) != PA_OK) return st;
 
   Plan plan;
-  build_plan(*pool, *batch, num_q_heads, q_dtype, causal ? 1 : 0, plan);
+  build_plan(*pool, *batch, num_q_heads, q_dtype, causal ? 1 : 0, kvu != nullptr, plan);
   if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL");
   if (((uintptr_t)workspace & 255) != 0) return fail(PA_ERR_WORKSPACE, "workspace not 256-byte aligned");
   if (workspace_bytes < plan.bytes)
@@ -601,6 +633,7 @@ pa_status pa_attention(const pa_kv_pool *pool, const pa_batch *batch, const void
       memcpy(host + plan.off_rtok, plan.row_token.data(), plan.row_token.size() * sizeof(int32_t));
       memcpy(host + plan.off_rslot, plan.row_slot0.data(), plan.row_slot0.size() * sizeof(int32_t));
     }
+    if (!plan.wtok.empty()) memcpy(host + plan.off_wtok, plan.wtok.data(), plan.wtok.size() * sizeof(WriteTok));
     if (env_flag("PA_PLAN_UPLOAD")) {
       hipError_t ce = hipMemcpyAsync(workspace, host, plan_bytes, hipMemcpyHostToDevice, s);
       if (ce != hipSuccess) return hip_fail(ce, "plan upload");
@@ -615,6 +648,26 @@ pa_status pa_attention(const pa_kv_pool *pool, const pa_batch *batch, const void
   const float vscale = pool->kv_dtype == PA_FP8_E4M3 ? pool->v_scale : 1.0f;
 
   hipError_t e = hipSuccess;
+  // KV update, first part: the new rows no decode unit writes itself (slots
+  // derived on the fly), before any kernel that may read them
+  if (!plan.wtok.empty()) {
+    WriteArgs w{};
+    w.key = kvu->key;
+    w.value = kvu->value;
+    w.toks = (const WriteTok *)(items + plan.off_wtok);
+    w.block_table = batch->block_table;
+    w.slots_out = kvu->slot_mapping;
+    w.k_cache = pool->k_cache;
+    w.v_cache = pool->v_cache;
+    w.capacity = (int64_t)pool->num_blocks * pool->block_size;
+    w.n_toks = (int32_t)plan.wtok.size();
+    w.bt_stride = batch->bt_stride;
+    w.num_kv_heads = pool->num_kv_heads;
+    w.k_scale = kscale;
+    w.v_scale = vscale;
+    e = launch_write_new(*pool, q_dtype, w, s);
+    if (e != hipSuccess) return hip_fail(e, "k_write_new launch");
+  }
   // the extend kernel goes to the side stream when decode work runs beside it
   hipStream_t xs = s;
   SideStream *side = nullptr;
@@ -688,6 +741,15 @@ pa_status pa_attention(const pa_kv_pool *pool, const pa_batch *batch, const void
     a.g_total = g_total;
     a.scale_log2 = softmax_scale * log2e * kscale;
     a.v_scale = vscale;
+    if (kvu) {
+      a.knew = kvu->key;
+      a.vnew = kvu->value;
+      a.slots_out = kvu->slot_mapping;
+      a.k_store = pool->k_cache;
+      a.v_store = pool->v_cache;
+      a.enc_k_scale = kscale;
+      a.enc_v_scale = vscale;
+    }
     // q heads per launch: the whole GQA group where the registers allow it,
     // otherwise the group is covered by several launches (fp32 pools)
     const int g_max = 16;
@@ -697,6 +759,8 @@ pa_status pa_attention(const pa_kv_pool *pool, const pa_batch *batch, const void
       const int g_tmpl = a.g <= 1 ? 1 : a.g <= 2 ? 2 : a.g <= 4 ? 4 : a.g <= 8 ? 8 : 16;
       e = launch_decode(*pool, q_dtype, a, g_tmpl, s);
       if (e != hipSuccess) return hip_fail(e, "k_decode launch");
+      a.knew = a.vnew = nullptr;                  // rows written by the first launch
+      a.slots_out = nullptr;
     }
   }
   if (!plan.merge.empty()) {
@@ -715,6 +779,27 @@ pa_status pa_attention(const pa_kv_pool *pool, const pa_batch *batch, const void
     if ((e = hipStreamWaitEvent(s, side->join, 0)) != hipSuccess) return hip_fail(e, "join wait");
   }
   return PA_OK;
+}
+
+}  // namespace pa
+
+extern "C" {
+
+pa_status pa_attention(const pa_kv_pool *pool, const pa_batch *batch, const void *query,
+                       pa_dtype q_dtype, int32_t num_q_heads, float softmax_scale, int32_t causal,
+                       void *output, void *workspace, size_t workspace_bytes, pa_stream_t stream) {
+  return attention_impl(pool, batch, query, q_dtype, num_q_heads, softmax_scale, causal, output,
+                        workspace, workspace_bytes, (hipStream_t)stream, nullptr);
+}
+
+pa_status pa_write_kv_attention(const pa_kv_pool *pool, const pa_batch *batch, const void *query,
+                                const void *key, const void *value, pa_dtype q_dtype,
+                                int32_t num_q_heads, float softmax_scale, int32_t causal,
+                                int64_t *slot_mapping, void *output, void *workspace,
+                                size_t workspace_bytes, pa_stream_t stream) {
+  const KvUpdate kvu{key, value, slot_mapping};
+  return attention_impl(pool, batch, query, q_dtype, num_q_heads, softmax_scale, causal, output,
+                        workspace, workspace_bytes, (hipStream_t)stream, &kvu);
 }
 
 size_t pa_kv_cache_bytes(const pa_kv_pool *pool) {

@@ -70,6 +70,96 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
   return sign | code;
 }
 
+// ---------------------------------------------------------------------------
+// Pool encoding of new K/V elements.  Every writer of new rows (the scatter
+// kernel, its plan-driven variant and the decode kernel's own-token write)
+// derives the stored bits with pool_bits(), so the pool bytes do not depend on
+// which of them wrote a token.  IN / KV are the input and pool element kinds.
+// ---------------------------------------------------------------------------
+
+// Input element bits (a bf16 or an fp32 word, zero-extended) as a float.
+template <int IN>
+__device__ __forceinline__ float in_to_f32(uint32_t raw) {
+  if constexpr (IN == KV_BF16) return __uint_as_float(raw << 16);
+  else return __uint_as_float(raw);
+}
+
+// Stored bits of one element: the input bits for a same-dtype pool, the
+// E4M3FN code of x / scale (fp32 division) for an fp8 pool.
+template <int IN, int KV>
+__device__ __forceinline__ uint32_t pool_bits(uint32_t raw, float scale) {
+  static_assert(IN != KV_FP8, "fp8 is a pool format only");
+  static_assert(KV == KV_FP8 || IN == KV, "same-dtype copy or fp8 encode");
+  if constexpr (KV == KV_FP8) return e4m3_encode(in_to_f32<IN>(raw) / scale);
+  else return raw;
+}
+
+// The value the attention kernels compute with for stored bits (fp8: the
+// code's own value; the per-tensor scale is applied outside the dot products).
+template <int KV>
+__device__ __forceinline__ float pool_value(uint32_t bits) {
+  if constexpr (KV == KV_FP8) return fp8x2_to_f32(bits, false).x;
+  else return in_to_f32<KV>(bits);
+}
+
+// One 16-byte pool chunk of a new token's K and V rows for one kv head: the
+// elements c*E .. c*E+E-1 of the head's input rows (E = 16 / pool element
+// bytes).  The K chunk is 16 contiguous bytes of the chunk-major K tile; the
+// same dims of V go to rows c*E .. of the dimension-major V tile, one element
+// per row.
+template <int IN, int KV> struct KvChunkIn {
+  static constexpr int IB = KvTraits<IN>::bytes;
+  static constexpr int E = 16 / KvTraits<KV>::bytes;
+  static constexpr int NV = E * IB / 16;   // 16-byte input vectors per chunk
+  uint4 k[NV], v[NV];
+};
+
+template <int IN, int KV>
+__device__ __forceinline__ KvChunkIn<IN, KV> load_kv_chunk(const void *key_row, const void *value_row,
+                                                           int c) {
+  using In = KvChunkIn<IN, KV>;
+  In r;
+  const uint4 *ks = (const uint4 *)((const char *)key_row + (int64_t)c * In::E * In::IB);
+  const uint4 *vs = (const uint4 *)((const char *)value_row + (int64_t)c * In::E * In::IB);
+#pragma unroll
+  for (int i = 0; i < In::NV; ++i) {
+    r.k[i] = ks[i];
+    r.v[i] = vs[i];
+  }
+  return r;
+}
+
+// Stores chunk c of slot offset `off` of the (block, head) tiles whose byte
+// offset in k_cache / v_cache is `tile`.
+template <int IN, int KV, int D>
+__device__ __forceinline__ void store_kv_chunk(const KvChunkIn<IN, KV> &in, void *kc, void *vc,
+                                               int64_t tile, int off, int c, float k_scale,
+                                               float v_scale) {
+  constexpr int PB = KvTraits<KV>::bytes;
+  constexpr int IB = KvTraits<IN>::bytes;
+  constexpr int E = 16 / PB;
+  constexpr int S = 16;                      // slots per block
+  char *kdst = (char *)kc + tile + (int64_t)c * (S * 16) + off * 16;
+  char *vdst = (char *)vc + tile + ((int64_t)c * E * S + off) * PB;  // row c*E, column off
+  const uint32_t *kw = (const uint32_t *)in.k, *vw = (const uint32_t *)in.v;
+  // input element e of a chunk (zero-extended bits)
+  auto elem = [](const uint32_t *words, int e) -> uint32_t {
+    if constexpr (IB == 2) return (words[e / 2] >> (16 * (e & 1))) & 0xffffu;
+    else return words[e];
+  };
+  uint32_t out[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t kb = pool_bits<IN, KV>(elem(kw, e), k_scale);
+    const uint32_t vb = pool_bits<IN, KV>(elem(vw, e), v_scale);
+    out[e * PB / 4] |= kb << (8 * ((e * PB) & 3));
+    if constexpr (PB == 4) ((uint32_t *)vdst)[e * S] = vb;
+    else if constexpr (PB == 2) ((uint16_t *)vdst)[e * S] = (uint16_t)vb;
+    else ((uint8_t *)vdst)[e * S] = (uint8_t)vb;
+  }
+  *(uint4 *)kdst = make_uint4(out[0], out[1], out[2], out[3]);
+}
+
 // Wave-wide reductions (64 lanes).
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll

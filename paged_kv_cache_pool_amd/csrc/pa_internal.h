@@ -19,13 +19,42 @@ constexpr int kWavesPerGroup = 4;    // waves per workgroup in the split-K kerne
 // token `token` (row of the flat stream) belonging to request `req`.  When
 // `part` < 0 the range is the token's whole visible range and the kernel
 // writes the final output; otherwise it writes partial (m, l, o) at slot `part`.
+// When `wpos` >= 0 (attention that includes the KV update) the token is its
+// request's only new token, at position wpos inside this unit's key range:
+// the unit first stores the token's K/V rows into the pool, then attends.
 struct DecodeItem {
   int32_t token;
   int32_t req;
   int32_t kv_begin;
   int32_t kv_end;
   int32_t part;
-  int32_t pad[3];
+  int32_t wpos;
+  int32_t pad[2];
+};
+
+// A new token whose K/V rows the plan-driven scatter writes: flat row
+// `token`, request `req`, position `pos`.
+struct WriteTok {
+  int32_t token;
+  int32_t req;
+  int32_t pos;
+  int32_t pad;
+};
+
+struct WriteArgs {
+  const void *key;        // [T][Hkv][D] input rows
+  const void *value;
+  const WriteTok *toks;
+  const int32_t *block_table;
+  int64_t *slots_out;     // [T] or null
+  void *k_cache;
+  void *v_cache;
+  int64_t capacity;       // num_blocks * 16
+  int32_t n_toks;
+  int32_t bt_stride;
+  int32_t num_kv_heads;
+  float k_scale;          // pool scales (fp8 encode), 1 otherwise
+  float v_scale;
 };
 
 // Merge of the partials of one token: slots [first, first + count).
@@ -83,6 +112,14 @@ struct DecodeArgs {
   float scale_log2;       // softmax_scale * log2(e) (* k_scale for fp8 pools)
   float v_scale;          // 1 for non-fp8 pools
   int32_t zero;           // always 0 (used to keep per-step loads inside the loop)
+  // KV update of items with wpos >= 0 (null knew: no update in this launch)
+  const void *knew;       // [T][Hkv][D] new K rows (query dtype)
+  const void *vnew;
+  int64_t *slots_out;     // [T] or null
+  void *k_store;          // the pool arrays, writable
+  void *v_store;
+  float enc_k_scale;      // pool scales for the fp8 encode, 1 otherwise
+  float enc_v_scale;
 };
 
 struct MergeArgs {
@@ -128,6 +165,8 @@ hipError_t launch_slot_mapping(const pa_batch &b, int64_t *slots, int max_c, hip
 hipError_t launch_write_kv(const pa_kv_pool &p, const void *key, const void *value,
                            pa_dtype in_dtype, const int64_t *slots, int32_t num_tokens,
                            hipStream_t s);
+hipError_t launch_write_new(const pa_kv_pool &p, pa_dtype in_dtype, const WriteArgs &a,
+                            hipStream_t s);
 hipError_t launch_decode(const pa_kv_pool &p, pa_dtype q_dtype, const DecodeArgs &a,
                          int g_tmpl, hipStream_t s);
 hipError_t launch_merge(pa_dtype q_dtype, int head_dim, const MergeArgs &a, hipStream_t s);

@@ -4,7 +4,8 @@ Device set-up for tests, the smoke check and the benchmark: allocate the
 pool (every byte 0xFF, a NaN in each element type, so unwritten slots are
 canaries), populate it with the workload's earlier steps using the library's
 own metadata, slot derivation and KV write, and then run the step:
-slot derivation -> KV write -> attention, all on one stream.
+slot derivation -> KV write -> attention, all on one stream (or the one call
+that does all three).
 """
 from __future__ import annotations
 
@@ -25,8 +26,9 @@ def to_device(a: np.ndarray, io_dtype: str, device="cuda") -> torch.Tensor:
 
 class GpuStep:
     def __init__(self, w: Workload, device: str = "cuda", canary: bool = True, causal: bool = True,
-                 stream: Optional[torch.cuda.Stream] = None, shared_prefix: bool = True):
-        self.w, self.device, self.causal = w, device, causal
+                 stream: Optional[torch.cuda.Stream] = None, shared_prefix: bool = True,
+                 fused: bool = False):
+        self.w, self.device, self.causal, self.fused = w, device, causal, fused
         self.stream = stream or torch.cuda.current_stream()
         self.pool = B.KVPool.allocate(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim,
                                       w.kv_dtype, w.k_scale, w.v_scale, device=device,
@@ -53,8 +55,14 @@ class GpuStep:
         self.stream.synchronize()
 
     def run(self) -> torch.Tensor:
-        """One step: a1 slots, a2 KV write, a3-a7 attention (asynchronous)."""
+        """One step: a1 slots, a2 KV write, a3-a7 attention (asynchronous); with
+        `fused`, all of them in the one call that includes the KV update."""
         w = self.w
+        if self.fused:
+            B.write_kv_attention(self.pool, self.batch, self.query, self.key, self.value,
+                                 w.num_q_heads, w.softmax_scale, causal=self.causal, out=self.out,
+                                 workspace=self.workspace, slots=self.slots, stream=self.stream)
+            return self.out
         B.slot_mapping(self.batch, w.block_size, out=self.slots, stream=self.stream)
         B.write_kv(self.pool, self.key, self.value, self.slots, stream=self.stream)
         B.attention(self.pool, self.batch, self.query, w.num_q_heads, w.softmax_scale,

@@ -1,0 +1,222 @@
+"""GPU parity of the attention call that includes the KV update
+(pa_write_kv_attention), through the C ABI.
+
+* slots and pool bytes: bit-exact against the oracle's slot derivation and
+  scatter, and identical to what the separate calls (pa_slot_mapping,
+  pa_write_kv) leave in the pool;
+* attention: within the same tolerance as pa_attention against the oracle
+  (the newest key of a decode row may be added in another order than in the
+  separate path, so the two outputs agree to rounding, not bit for bit).
+"""
+import ctypes as C
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from paged_kv_cache_pool_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {W.F32: 1e-5, W.BF16: 2e-2, W.FP8: 2e-2}
+
+
+def say(*a):
+    print("[gpu-fused]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def R():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from paged_kv_cache_pool_amd import runner
+    return runner
+
+
+def _pool_bits(pool, which):
+    a = pool.logical(which)
+    return a.view(np.uint32) if a.dtype == np.float32 else a
+
+
+def _assert_same_pool(p1, p2):
+    for which in ("k", "v"):
+        a, b = _pool_bits(p1, which), _pool_bits(p2, which)
+        bad = np.argwhere(a != b)
+        assert bad.size == 0, f"{which} pools differ at {bad[:5].tolist()} (of {len(bad)})"
+
+
+def _assert_pool_is_oracle(w, pool):
+    orc = O.build_pool(w)
+    O.write_kv(orc, w.key, w.value, w.io_dtype, _want_slots(w))
+    for which in ("k", "v"):
+        o = orc.k if which == "k" else orc.v
+        o = o.view(np.uint32) if o.dtype == np.float32 else o
+        bad = np.argwhere(_pool_bits(pool, which) != o)
+        assert bad.size == 0, f"{which} pool differs from the oracle at {bad[:5].tolist()} (of {len(bad)})"
+
+
+def _want_slots(w):
+    qsl = O.query_start_loc(w.num_scheduled)
+    sl = O.seq_lens(w.num_computed, w.num_scheduled)
+    return O.slot_mapping(qsl, sl, w.block_table, w.block_size)
+
+
+def _check_out(w, step, tokens=None):
+    ref = O.run_step(w, tokens=tokens).out
+    got = step.out_f64()
+    if tokens is not None:
+        got = got[tokens]
+    err = np.abs(got - ref)
+    say(w.name, "max_abs_err", float(err.max()), "max|O|", float(np.abs(ref).max()))
+    assert np.isfinite(got).all()
+    assert err.max() <= TOL[w.kv_dtype], (float(err.max()), np.unravel_index(err.argmax(), err.shape))
+
+
+def _sample(w, n, seed):
+    rng = np.random.default_rng(seed)
+    if w.num_tokens <= n:
+        return np.arange(w.num_tokens, dtype=np.int32)
+    qsl = O.query_start_loc(w.num_scheduled)
+    must = {int(qsl[i]) for i in range(w.num_seqs) if w.num_scheduled[i] > 0}
+    must |= {int(qsl[i + 1]) - 1 for i in range(w.num_seqs) if w.num_scheduled[i] > 0}
+    must = set(sorted(must)[: n // 2])
+    rest = rng.choice(w.num_tokens, size=max(0, n - len(must)), replace=False).tolist()
+    return np.array(sorted(must | set(rest)), dtype=np.int32)
+
+
+def _fused_and_separate(R, w, **kw):
+    fused = R.GpuStep(w, fused=True, **kw)
+    fused.run()
+    sep = R.GpuStep(w, **kw)
+    sep.run()
+    torch.cuda.synchronize()
+    return fused, sep
+
+
+@pytest.mark.parametrize("cfg,n", [(1, None), (2, 24), (3, 40), (5, 24)])
+def test_fused_workloads(R, cfg, n):
+    """The five-workload set's configs 1, 2, 3 and 5 through the one call:
+    slots and written pool bytes exactly the oracle's, attention within
+    tolerance (sampled rows for the full-size ones)."""
+    say("fused config", cfg)
+    w = W.make(cfg)
+    step = R.GpuStep(w, fused=True)
+    step.run()
+    torch.cuda.synchronize()
+    assert (step.slots.cpu().numpy() == _want_slots(w)).all()
+    used = np.unique(w.block_table[w.block_table >= 0])
+    orc = O.build_pool(w)
+    O.write_kv(orc, w.key, w.value, w.io_dtype, _want_slots(w))
+    for which in ("k", "v"):
+        o = orc.k if which == "k" else orc.v
+        o = (o.view(np.uint32) if o.dtype == np.float32 else o)[used]
+        assert (_pool_bits(step.pool, which)[used] == o).all(), which
+    _check_out(w, step, None if n is None else _sample(w, n, cfg))
+
+
+@pytest.mark.parametrize("seed", range(18))
+def test_fused_equals_separate_random(R, seed):
+    """Random ragged batches over every pool type, head size and GQA ratio:
+    the one call leaves the same pool bytes and slots as the separate calls,
+    and both outputs match the oracle."""
+    kv = [W.F32, W.BF16, W.FP8][seed % 3]
+    io = W.F32 if kv == W.F32 else W.BF16
+    g = [1, 2, 4][(seed // 3) % 3]
+    D = [64, 128][(seed // 9) % 2]
+    say("fused random", seed, kv, "g", g, "D", D)
+    w = W.random_small(seed + 100, max_seqs=6, max_len=300, num_q_heads=2 * g, num_kv_heads=2,
+                       head_dim=D, kv_dtype=kv, io_dtype=io, spare_blocks=4)
+    if kv == W.FP8:
+        w = W.build(w.name, seed + 100, num_q_heads=2 * g, num_kv_heads=2, head_dim=D,
+                    block_size=16, num_blocks=w.num_blocks, kv_dtype=W.FP8, io_dtype=W.BF16,
+                    num_computed=w.num_computed, num_scheduled=w.num_scheduled)
+    fused, sep = _fused_and_separate(R, w)
+    assert (fused.slots.cpu().numpy() == sep.slots.cpu().numpy()).all()
+    _assert_same_pool(fused.pool, sep.pool)
+    _assert_pool_is_oracle(w, fused.pool)
+    _check_out(w, fused)
+    _check_out(w, sep)
+
+
+@pytest.mark.parametrize("kv", [W.BF16, W.FP8])
+def test_fused_decode_partitions_and_verify_rows(R, monkeypatch, kv):
+    """Decode rows split into 64-key partitions (the newest key is written by
+    the last partition's unit, which may hold that key alone), next to
+    speculative-verify-sized chunks of 2 to 8 rows (written by the scatter
+    pass before the split-K kernel reads them) and one prefill chunk."""
+    monkeypatch.setenv("PA_PARTITION_KEYS", "64")
+    say("fused partitions + verify rows", kv)
+    nc = [64, 0, 127, 128, 300, 5, 64, 200, 40]
+    ns = [1, 1, 1, 1, 1, 4, 8, 2, 24]
+    w = W.build(f"fused_parts_{kv}", 7, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                num_blocks=140, kv_dtype=kv, io_dtype=W.BF16, num_computed=nc, num_scheduled=ns)
+    fused, sep = _fused_and_separate(R, w)
+    assert (fused.slots.cpu().numpy() == _want_slots(w)).all()
+    _assert_same_pool(fused.pool, sep.pool)
+    _assert_pool_is_oracle(w, fused.pool)
+    _check_out(w, fused)
+
+
+@pytest.mark.parametrize("kv", [W.BF16, W.FP8])
+def test_fused_cascade(R, kv):
+    """The shared-prefix pass with the KV update: the decode rows' own keys
+    (written inside the split-K kernel) follow the prefix."""
+    say("fused cascade", kv)
+    own = [0, 1, 17, 33, 60, 9, 5]
+    w = W.build(f"fused_casc_{kv}", 11, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                block_size=16, num_blocks=80, kv_dtype=kv, io_dtype=W.BF16,
+                num_computed=[48 + o for o in own], num_scheduled=[1, 1, 1, 1, 1, 3, 20],
+                shared_prefix_tokens=48)
+    fused, sep = _fused_and_separate(R, w)
+    _assert_same_pool(fused.pool, sep.pool)
+    _assert_pool_is_oracle(w, fused.pool)
+    _check_out(w, fused)
+
+
+def test_fused_page_mixed_batch(R):
+    """The source-map page's mixed batch (one decode row, a 256-token chunk, a
+    3-token chunk) through the one call."""
+    say("fused page mixed batch")
+    w = W.build("page_mixed", 3, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                num_blocks=200, kv_dtype=W.BF16, io_dtype=W.BF16, num_computed=[1024, 512, 600],
+                num_scheduled=[1, 256, 3])
+    fused, sep = _fused_and_separate(R, w)
+    _assert_same_pool(fused.pool, sep.pool)
+    _check_out(w, fused)
+
+
+def test_fused_block_id_outside_pool(R):
+    """A decode request whose newest key falls in a block id outside the pool:
+    as with the separate calls, its slot is reported but nothing is written,
+    and the key takes no part in the attention."""
+    say("fused invalid block id")
+    w = W.build("fused_bad_block", 4, num_q_heads=4, num_kv_heads=2, head_dim=128, block_size=16,
+                num_blocks=20, kv_dtype=W.BF16, io_dtype=W.BF16, num_computed=[16, 40, 70],
+                num_scheduled=[1, 1, 1])
+    bt = w.block_table.copy()
+    bt[0, 1] = -1                   # request 0's new token (position 16)
+    bt[1, 2] = w.num_blocks + 3     # request 1's new token (position 40)
+    w = dataclasses.replace(w, block_table=bt)
+    fused, sep = _fused_and_separate(R, w)
+    fs, ss = fused.slots.cpu().numpy(), sep.slots.cpu().numpy()
+    assert (fs == ss).all() and fs[0] < 0 and fs[1] >= w.num_blocks * 16
+    _assert_same_pool(fused.pool, sep.pool)
+    a, b = fused.out_f64(), sep.out_f64()
+    assert np.isfinite(a).all()
+    assert np.abs(a - b).max() <= TOL[W.BF16]
+
+
+def test_fused_rejects_null_rows(R):
+    from paged_kv_cache_pool_amd import binding as B
+    say("fused null key")
+    w = W.make(1)
+    step = R.GpuStep(w, fused=True)
+    p, b = step.pool.struct(), step.batch.struct()
+    st = B.lib.pa_write_kv_attention(C.byref(p), C.byref(b), B._ptr(step.query), None, None,
+                                     B.torch_dtype_code(step.query), w.num_q_heads,
+                                     w.softmax_scale, 1, None, B._ptr(step.out),
+                                     B._ptr(step.workspace), step.workspace.numel(), None)
+    assert st == 1
