@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--separate", action="store_true",
                     help="time the step as three calls (slot derivation, KV write, attention) "
                          "instead of the one call that includes the KV update")
+    ap.add_argument("--compare", action="store_true",
+                    help="also time the other form of the step (same pool and inputs)")
     ap.add_argument("--cold", action="store_true",
                     help="also time steps that start with cold caches (a 1 GiB scratch read "
                          "before each step, outside the timed events)")
@@ -307,18 +309,19 @@ def main():
     # the other form of the step on the same pool and inputs (the KV write is
     # idempotent), for comparison
     other = None
-    step.fused = a.separate
-    for _ in range(3):
-        step.run()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(a.steps):
-        step.run()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    other = round(e0.elapsed_time(e1) / a.steps, 5)
-    step.fused = not a.separate
+    if a.compare:
+        step.fused = a.separate
+        for _ in range(a.warmup):
+            step.run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(a.steps):
+            step.run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        other = round(e0.elapsed_time(e1) / a.steps, 5)
+        step.fused = not a.separate
 
     cold = None
     if a.cold:
@@ -400,7 +403,8 @@ def main():
         "cpu_baseline": cpu,
         "kernels_us": {k: round(v["avg_us"], 2) for k, v in kernels.items()},
         "step_form": "separate calls" if a.separate else "one call with the KV update",
-        ("ms_per_step_one_call" if a.separate else "ms_per_step_separate_calls"): other,
+        **({("ms_per_step_one_call" if a.separate else "ms_per_step_separate_calls"): other}
+           if other is not None else {}),
         "ms_per_step_with_kernel_events": round(ms_instr, 5),
         "ms_per_step_spread": spread,
         "decode_kv_gbps": roof["achieved"] if roof["unit"] == "GB/s" else None,
