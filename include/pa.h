@@ -117,8 +117,8 @@ typedef struct pa_batch {
   int32_t num_common_prefix_blocks;     /* shared-prefix hint, see below (0: none) */
 } pa_batch;
 
-/* num_common_prefix_blocks ([P1] common prefix of all requests, the
- * num_common_prefix_blocks the scheduler reports; cascade attention): n > 0
+/* num_common_prefix_blocks ([P1] §4.4: the scheduler reports the number of
+ * blocks common to all requests; §5.1.3: cascade attention): n > 0
  * states that the first n block-table entries of every request that has new
  * tokens are the same n physical blocks, and that these blocks lie wholly in
  * every such request's history (16 * n <= seq_lens[i] - c_i).  The library
