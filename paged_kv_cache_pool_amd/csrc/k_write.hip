@@ -82,35 +82,81 @@ __global__ __launch_bounds__(256) void k_write_kv(const void *__restrict__ key,
 }
 
 // The same scatter with the slots derived on the fly (a1 + a2 in one pass),
-// for the tokens the step's plan lists: token n of request req at position
-// pos goes to slot block_table[req][pos / 16] * 16 + pos % 16, which is also
-// stored to slots_out[n] when that pointer is set.  Used by the attention
-// call that includes the KV update.
+// for the new tokens the step's plan lists as block segments: up to 16
+// consecutive tokens of one request whose positions fall in one logical
+// block.  Token n of the segment at position p goes to slot
+// block_table[req][p / 16] * 16 + p % 16, which is also stored to slots_out[n]
+// when that pointer is set.  One workgroup per (segment, kv head) fills the
+// segment's slots of the head's K and V tiles:
+//  K: one thread per (token, 16-byte chunk), one 16-byte store each (the
+//     chunks of consecutive slots are contiguous in the chunk-major tile);
+//  V: the tokens' elements are first placed in LDS in the tile's own
+//     dimension-major layout, then the tile is written as 16-byte vectors;
+//     a vector that also covers slots outside the segment is written
+//     element by element, leaving the other slots untouched.
+// Used by the attention call that includes the KV update.
 template <int IN, int KV, int D>
 __global__ __launch_bounds__(256) void k_write_new(const WriteArgs a) {
   constexpr int IB = KvTraits<IN>::bytes;
   constexpr int PB = KvTraits<KV>::bytes;
-  constexpr int NCH = D * PB / 16;
-  constexpr int TILE = D * kBlock * PB;
+  constexpr int E = 16 / PB;                // elements per 16 bytes of the pool
+  constexpr int NCH = D / E;                // chunks per key row
+  constexpr int TILE = D * kBlock * PB;     // bytes of one (block, head) tile
+  constexpr int NVEC = TILE / 16;           // 16-byte vectors per tile
+  __shared__ __attribute__((aligned(16))) uint8_t vt[TILE];
+  __shared__ WriteSeg seg_s;
+  __shared__ int32_t blk_s;
 
-  const int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)a.n_toks * a.num_kv_heads * NCH;
-  if (w >= total) return;
-  const int c = (int)(w % NCH);
-  const int64_t wh = w / NCH;               // list entry * num_kv_heads + head
-  const int h = (int)(wh % a.num_kv_heads);
-  const WriteTok t = a.toks[wh / a.num_kv_heads];
-  const int64_t slot =
-      (int64_t)a.block_table[(int64_t)t.req * a.bt_stride + t.pos / kBlock] * kBlock + t.pos % kBlock;
-  if (a.slots_out && h == 0 && c == 0) a.slots_out[t.token] = slot;
-  const int64_t th = (int64_t)t.token * a.num_kv_heads + h;
-  const KvChunkIn<IN, KV> in = load_kv_chunk<IN, KV>((const char *)a.key + th * D * IB,
-                                                     (const char *)a.value + th * D * IB, c);
-  if (slot < 0 || slot >= a.capacity) return;
-  const int64_t blk = slot / kBlock;
-  const int off = (int)(slot - blk * kBlock);
-  store_kv_chunk<IN, KV, D>(in, a.k_cache, a.v_cache, (blk * a.num_kv_heads + h) * (int64_t)TILE,
-                            off, c, a.k_scale, a.v_scale);
+  const int tid = threadIdx.x;
+  const int h = (int)(blockIdx.x % (unsigned)a.num_kv_heads);
+  const int si = (int)(blockIdx.x / (unsigned)a.num_kv_heads);
+  if (tid == 0) {
+    const WriteSeg sg = a.segs[si];
+    seg_s = sg;
+    blk_s = a.block_table[(int64_t)sg.req * a.bt_stride + sg.pos0 / kBlock];
+  }
+  __syncthreads();
+  const WriteSeg sg = seg_s;
+  const int blk = blk_s;
+  const int off0 = sg.pos0 % kBlock;
+  if (a.slots_out && h == 0 && tid < sg.count)
+    a.slots_out[sg.tok0 + tid] = (int64_t)blk * kBlock + off0 + tid;
+  if (blk < 0 || blk >= a.num_blocks) return;   // slot outside the pool: not written
+
+  const int64_t tile = ((int64_t)blk * a.num_kv_heads + h) * TILE;
+  for (int w = tid; w < sg.count * NCH; w += blockDim.x) {
+    const int t = w / NCH, c = w % NCH;
+    const int64_t th = (int64_t)(sg.tok0 + t) * a.num_kv_heads + h;
+    const KvChunkIn<IN, KV> in = load_kv_chunk<IN, KV>((const char *)a.key + th * D * IB,
+                                                       (const char *)a.value + th * D * IB, c);
+    *(uint4 *)((char *)a.k_cache + tile + c * (kBlock * 16) + (off0 + t) * 16) = k_chunk_bits<IN, KV>(in, a.k_scale);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const uint32_t b = v_elem_bits<IN, KV>(in, e, a.v_scale);
+      uint8_t *p = vt + ((c * E + e) * kBlock + off0 + t) * PB;
+      if constexpr (PB == 4) *(uint32_t *)p = b;
+      else if constexpr (PB == 2) *(uint16_t *)p = (uint16_t)b;
+      else *p = (uint8_t)b;
+    }
+  }
+  __syncthreads();
+  // a vector holds E consecutive slots of one dim row
+  char *vdst = (char *)a.v_cache + tile;
+  for (int w = tid; w < NVEC; w += blockDim.x) {
+    const int s0 = (w * E) % kBlock;          // first slot of the vector
+    if (s0 >= off0 && s0 + E <= off0 + sg.count) {
+      *(uint4 *)(vdst + w * 16) = *(const uint4 *)(vt + w * 16);
+    } else if (s0 + E > off0 && s0 < off0 + sg.count) {
+      for (int e = 0; e < E; ++e) {
+        const int sl = s0 + e;
+        if (sl < off0 || sl >= off0 + sg.count) continue;
+        const int o = w * 16 + e * PB;
+        if constexpr (PB == 4) *(uint32_t *)(vdst + o) = *(const uint32_t *)(vt + o);
+        else if constexpr (PB == 2) *(uint16_t *)(vdst + o) = *(const uint16_t *)(vt + o);
+        else vdst[o] = (char)vt[o];
+      }
+    }
+  }
 }
 
 template <int IN, int KV>
@@ -141,8 +187,7 @@ hipError_t launch_write_kv(const pa_kv_pool &p, const void *key, const void *val
 
 template <int IN, int KV>
 static hipError_t write_new_d(const pa_kv_pool &p, const WriteArgs &a, hipStream_t s) {
-  const int64_t threads = (int64_t)a.n_toks * p.num_kv_heads * (p.head_dim * KvTraits<KV>::bytes / 16);
-  const dim3 grid((unsigned)((threads + 255) / 256));
+  const dim3 grid((unsigned)((int64_t)a.n_segs * p.num_kv_heads));
   prof_begin("k_write_new", s);
   if (p.head_dim == 128) hipLaunchKernelGGL((k_write_new<IN, KV, 128>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((k_write_new<IN, KV, 64>), grid, dim3(256), 0, s, a);
@@ -151,7 +196,7 @@ static hipError_t write_new_d(const pa_kv_pool &p, const WriteArgs &a, hipStream
 }
 
 hipError_t launch_write_new(const pa_kv_pool &p, pa_dtype in_dtype, const WriteArgs &a, hipStream_t s) {
-  if (a.n_toks == 0) return hipSuccess;
+  if (a.n_segs == 0) return hipSuccess;
   if (p.kv_dtype == PA_F32) return write_new_d<KV_F32, KV_F32>(p, a, s);
   if (p.kv_dtype == PA_BF16) return write_new_d<KV_BF16, KV_BF16>(p, a, s);
   if (in_dtype == PA_BF16) return write_new_d<KV_BF16, KV_FP8>(p, a, s);

@@ -294,13 +294,13 @@ struct Plan {
   std::vector<PrefixItem> pre;
   std::vector<int32_t> row_token, row_slot0;
   int32_t prefix_req = -1;                       // request whose block-table row supplies the prefix
-  // attention that includes the KV update: tokens the plan-driven scatter
-  // writes before the attention kernels (the others are written by their
-  // decode unit, DecodeItem::wpos)
-  std::vector<WriteTok> wtok;
+  // attention that includes the KV update: block segments of the tokens the
+  // plan-driven scatter writes before the attention kernels (the others are
+  // written by their decode unit, DecodeItem::wpos)
+  std::vector<WriteSeg> wseg;
   int32_t n_slots = 0;
   int32_t part_len = 0;
-  size_t off_dec = 0, off_merge = 0, off_ext = 0, off_pre = 0, off_rtok = 0, off_rslot = 0, off_wtok = 0;
+  size_t off_dec = 0, off_merge = 0, off_ext = 0, off_pre = 0, off_rtok = 0, off_rslot = 0, off_wseg = 0;
   size_t off_ml = 0, off_o = 0, bytes = 0;
 };
 
@@ -379,7 +379,11 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
     // by the scatter pass that runs before the attention kernels
     const bool own_write = kv_update && c == 1 && !(ext_ok && c >= ext_min);
     if (kv_update && !own_write)
-      for (int32_t t = 0; t < c; ++t) plan.wtok.push_back(WriteTok{q[i] + t, i, L[i] - c + t, 0});
+      for (int32_t pos = L[i] - c; pos < L[i];) {
+        const int32_t end = std::min(L[i], (pos / kBlock + 1) * kBlock);
+        plan.wseg.push_back(WriteSeg{i, q[i] + pos - (L[i] - c), pos, end - pos});
+        pos = end;
+      }
     const size_t dec0 = plan.dec.size();
     auto mark_own_write = [&]() {
       if (!own_write) return;
@@ -483,8 +487,8 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
   off = align256(off + plan.row_token.size() * sizeof(int32_t));
   plan.off_rslot = off;
   off = align256(off + plan.row_slot0.size() * sizeof(int32_t));
-  plan.off_wtok = off;
-  off = align256(off + plan.wtok.size() * sizeof(WriteTok));
+  plan.off_wseg = off;
+  off = align256(off + plan.wseg.size() * sizeof(WriteSeg));
   plan.off_ml = off;
   off = align256(off + (size_t)plan.n_slots * Hq * 2 * sizeof(float));
   plan.off_o = off;
@@ -633,7 +637,7 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
       memcpy(host + plan.off_rtok, plan.row_token.data(), plan.row_token.size() * sizeof(int32_t));
       memcpy(host + plan.off_rslot, plan.row_slot0.data(), plan.row_slot0.size() * sizeof(int32_t));
     }
-    if (!plan.wtok.empty()) memcpy(host + plan.off_wtok, plan.wtok.data(), plan.wtok.size() * sizeof(WriteTok));
+    if (!plan.wseg.empty()) memcpy(host + plan.off_wseg, plan.wseg.data(), plan.wseg.size() * sizeof(WriteSeg));
     if (env_flag("PA_PLAN_UPLOAD")) {
       hipError_t ce = hipMemcpyAsync(workspace, host, plan_bytes, hipMemcpyHostToDevice, s);
       if (ce != hipSuccess) return hip_fail(ce, "plan upload");
@@ -650,17 +654,17 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
   hipError_t e = hipSuccess;
   // KV update, first part: the new rows no decode unit writes itself (slots
   // derived on the fly), before any kernel that may read them
-  if (!plan.wtok.empty()) {
+  if (!plan.wseg.empty()) {
     WriteArgs w{};
     w.key = kvu->key;
     w.value = kvu->value;
-    w.toks = (const WriteTok *)(items + plan.off_wtok);
+    w.segs = (const WriteSeg *)(items + plan.off_wseg);
     w.block_table = batch->block_table;
     w.slots_out = kvu->slot_mapping;
     w.k_cache = pool->k_cache;
     w.v_cache = pool->v_cache;
-    w.capacity = (int64_t)pool->num_blocks * pool->block_size;
-    w.n_toks = (int32_t)plan.wtok.size();
+    w.num_blocks = pool->num_blocks;
+    w.n_segs = (int32_t)plan.wseg.size();
     w.bt_stride = batch->bt_stride;
     w.num_kv_heads = pool->num_kv_heads;
     w.k_scale = kscale;

@@ -129,6 +129,32 @@ __device__ __forceinline__ KvChunkIn<IN, KV> load_kv_chunk(const void *key_row, 
   return r;
 }
 
+// Input element e of a chunk (zero-extended bits).
+template <int IN, int KV>
+__device__ __forceinline__ uint32_t chunk_elem(const uint4 *words4, int e) {
+  const uint32_t *words = (const uint32_t *)words4;
+  if constexpr (KvTraits<IN>::bytes == 2) return (words[e / 2] >> (16 * (e & 1))) & 0xffffu;
+  else return words[e];
+}
+
+// The 16 stored bytes of a K chunk.
+template <int IN, int KV>
+__device__ __forceinline__ uint4 k_chunk_bits(const KvChunkIn<IN, KV> &in, float k_scale) {
+  constexpr int PB = KvTraits<KV>::bytes;
+  constexpr int E = 16 / PB;
+  uint32_t out[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    out[e * PB / 4] |= pool_bits<IN, KV>(chunk_elem<IN, KV>(in.k, e), k_scale) << (8 * ((e * PB) & 3));
+  return make_uint4(out[0], out[1], out[2], out[3]);
+}
+
+// Stored bits of element e of a V chunk.
+template <int IN, int KV>
+__device__ __forceinline__ uint32_t v_elem_bits(const KvChunkIn<IN, KV> &in, int e, float v_scale) {
+  return pool_bits<IN, KV>(chunk_elem<IN, KV>(in.v, e), v_scale);
+}
+
 // Stores chunk c of slot offset `off` of the (block, head) tiles whose byte
 // offset in k_cache / v_cache is `tile`.
 template <int IN, int KV, int D>
@@ -136,28 +162,18 @@ __device__ __forceinline__ void store_kv_chunk(const KvChunkIn<IN, KV> &in, void
                                                int64_t tile, int off, int c, float k_scale,
                                                float v_scale) {
   constexpr int PB = KvTraits<KV>::bytes;
-  constexpr int IB = KvTraits<IN>::bytes;
   constexpr int E = 16 / PB;
   constexpr int S = 16;                      // slots per block
   char *kdst = (char *)kc + tile + (int64_t)c * (S * 16) + off * 16;
   char *vdst = (char *)vc + tile + ((int64_t)c * E * S + off) * PB;  // row c*E, column off
-  const uint32_t *kw = (const uint32_t *)in.k, *vw = (const uint32_t *)in.v;
-  // input element e of a chunk (zero-extended bits)
-  auto elem = [](const uint32_t *words, int e) -> uint32_t {
-    if constexpr (IB == 2) return (words[e / 2] >> (16 * (e & 1))) & 0xffffu;
-    else return words[e];
-  };
-  uint32_t out[4] = {0, 0, 0, 0};
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const uint32_t kb = pool_bits<IN, KV>(elem(kw, e), k_scale);
-    const uint32_t vb = pool_bits<IN, KV>(elem(vw, e), v_scale);
-    out[e * PB / 4] |= kb << (8 * ((e * PB) & 3));
+    const uint32_t vb = v_elem_bits<IN, KV>(in, e, v_scale);
     if constexpr (PB == 4) ((uint32_t *)vdst)[e * S] = vb;
     else if constexpr (PB == 2) ((uint16_t *)vdst)[e * S] = (uint16_t)vb;
     else ((uint8_t *)vdst)[e * S] = (uint8_t)vb;
   }
-  *(uint4 *)kdst = make_uint4(out[0], out[1], out[2], out[3]);
+  *(uint4 *)kdst = k_chunk_bits<IN, KV>(in, k_scale);
 }
 
 // Wave-wide reductions (64 lanes).

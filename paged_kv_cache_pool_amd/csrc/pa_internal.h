@@ -32,26 +32,27 @@ struct DecodeItem {
   int32_t pad[2];
 };
 
-// A new token whose K/V rows the plan-driven scatter writes: flat row
-// `token`, request `req`, position `pos`.
-struct WriteTok {
-  int32_t token;
+// New tokens whose K/V rows the plan-driven scatter writes: `count` (1..16)
+// consecutive tokens of request `req`, flat rows tok0 .., positions pos0 ..,
+// all in logical block pos0 / 16.
+struct WriteSeg {
   int32_t req;
-  int32_t pos;
-  int32_t pad;
+  int32_t tok0;
+  int32_t pos0;
+  int32_t count;
 };
 
 struct WriteArgs {
   const void *key;        // [T][Hkv][D] input rows
   const void *value;
-  const WriteTok *toks;
+  const WriteSeg *segs;
   const int32_t *block_table;
   int64_t *slots_out;     // [T] or null
   void *k_cache;
   void *v_cache;
-  int64_t capacity;       // num_blocks * 16
-  int32_t n_toks;
+  int32_t n_segs;
   int32_t bt_stride;
+  int32_t num_blocks;
   int32_t num_kv_heads;
   float k_scale;          // pool scales (fp8 encode), 1 otherwise
   float v_scale;

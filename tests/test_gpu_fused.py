@@ -189,20 +189,23 @@ def test_fused_page_mixed_batch(R):
 
 
 def test_fused_block_id_outside_pool(R):
-    """A decode request whose newest key falls in a block id outside the pool:
-    as with the separate calls, its slot is reported but nothing is written,
-    and the key takes no part in the attention."""
+    """New tokens whose blocks lie outside the pool: as with the separate calls,
+    their slots are reported but nothing is written, and those keys take no
+    part in the attention.  Covers a decode row's own write and a 5-token
+    chunk split over a valid and an invalid block (scatter pass)."""
     say("fused invalid block id")
     w = W.build("fused_bad_block", 4, num_q_heads=4, num_kv_heads=2, head_dim=128, block_size=16,
-                num_blocks=20, kv_dtype=W.BF16, io_dtype=W.BF16, num_computed=[16, 40, 70],
-                num_scheduled=[1, 1, 1])
+                num_blocks=20, kv_dtype=W.BF16, io_dtype=W.BF16, num_computed=[16, 40, 70, 30],
+                num_scheduled=[1, 1, 1, 5])
     bt = w.block_table.copy()
     bt[0, 1] = -1                   # request 0's new token (position 16)
     bt[1, 2] = w.num_blocks + 3     # request 1's new token (position 40)
+    bt[3, 2] = -1                   # request 3's tokens at positions 32..34
     w = dataclasses.replace(w, block_table=bt)
     fused, sep = _fused_and_separate(R, w)
     fs, ss = fused.slots.cpu().numpy(), sep.slots.cpu().numpy()
     assert (fs == ss).all() and fs[0] < 0 and fs[1] >= w.num_blocks * 16
+    assert (fs[3:5] >= 0).all() and (fs[5:8] < 0).all()
     _assert_same_pool(fused.pool, sep.pool)
     a, b = fused.out_f64(), sep.out_f64()
     assert np.isfinite(a).all()
