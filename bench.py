@@ -167,7 +167,7 @@ def load_traffic(kernel, workload):
     return rec["hbm_bytes"]
 
 
-def cascade_prefix(w, seq_lens, qsl, ext_min_rows=16, extend_on=True, hint=True):
+def cascade_prefix(w, seq_lens, qsl, ext_min_rows=2, extend_on=True, hint=True):
     """Keys of the shared prefix that the library's cascade pass takes over
     from the split-K rows (0 when it does not apply): the same rule as the
     library's plan."""
@@ -186,7 +186,7 @@ def cascade_prefix(w, seq_lens, qsl, ext_min_rows=16, extend_on=True, hint=True)
     return P if rows else 0
 
 
-def algorithmic_work(w, seq_lens, qsl, ext_min_rows=16, extend_on=True, prefix=0, fused=False):
+def algorithmic_work(w, seq_lens, qsl, ext_min_rows=2, extend_on=True, prefix=0, fused=False):
     """Bytes the split-K decode kernel must move, flops the extend kernel must
     do and flops of the shared-prefix pass, per step, by the per-unit formulas
     in the design notes.  With a shared prefix of `prefix` keys taken over by
@@ -354,12 +354,25 @@ def main():
     tokens_per_s = T / (ms_per_step / 1000.0)
     qsl, sl = B.prepare_metadata(w.num_computed, w.num_scheduled)
     ext_on = os.environ.get("PA_DISABLE_EXTEND", "0") in ("", "0")
-    ext_min = int(os.environ.get("PA_EXTEND_MIN_ROWS", "16"))
+    ext_min = int(os.environ.get("PA_EXTEND_MIN_ROWS", "2"))
     prefix = cascade_prefix(w, sl, qsl, ext_min, ext_on, hint=step.batch.num_common_prefix_blocks > 0)
     dec_bytes, ext_flops, ext_bytes, pre_flops = algorithmic_work(
         w, sl, qsl, ext_min, ext_on and "k_extend" in kernels, prefix, fused=not a.separate)
 
-    if "k_decode" in kernels and (dec_bytes > 0):
+    # dominant kernel: the attention kernel that takes the longer time.  The
+    # extend kernel is priced against MFMA when its work is compute-heavy
+    # (prefill chunks), against HBM when it is not (short verify chunks over
+    # long histories: flops per byte below the peaks' ratio)
+    t_dec = kernels.get("k_decode", {}).get("avg_us", 0.0) if dec_bytes > 0 else 0.0
+    t_ext = kernels.get("k_extend", {}).get("avg_us", 0.0) if ext_flops > 0 else 0.0
+    ext_hbm = ext_flops > 0 and ext_flops / max(ext_bytes, 1) < MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBPS * 1e3
+    if t_ext > t_dec and ext_hbm:
+        dom = "k_extend"
+        achieved = ext_bytes / (t_ext * 1e-6) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": load_traffic(dom, w.name), "algorithmic_bytes_per_launch": ext_bytes}
+    elif t_dec >= t_ext:
         dom = "k_decode"
         achieved = dec_bytes / (kernels[dom]["avg_us"] * 1e-6) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
@@ -414,11 +427,11 @@ def main():
            if other is not None else {}),
         "ms_per_step_with_kernel_events": round(ms_instr, 5),
         "ms_per_step_spread": spread,
-        "decode_kv_gbps": roof["achieved"] if roof["unit"] == "GB/s" else None,
+        "decode_kv_gbps": roof["achieved"] if dom == "k_decode" else None,
     }
     if cold is not None:
         out["ms_per_step_cold"] = cold
-    if roof["unit"] == "GB/s":
+    if dom == "k_decode":
         uniq = unique_kv_bytes(w, sl, qsl, prefix)
         out["decode_kv_bytes_logical"] = dec_bytes
         out["decode_kv_bytes_unique"] = uniq

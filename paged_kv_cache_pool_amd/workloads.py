@@ -273,12 +273,27 @@ def prefix_fp8_decode(seed: int = 0, num_seqs: int = 128, prefix: int = 2048, lo
                  num_computed=ctx - ns, num_scheduled=ns, shared_prefix_tokens=prefix, rng=rng)
 
 
+def spec_verify(seed: int = 0, num_seqs: int = 64, lo: int = 512, hi: int = 4096, c_lo: int = 2,
+                c_hi: int = 8, num_blocks: int = 40000) -> Workload:
+    """Speculative-decoding verify step on the Llama-3-8B decode layer: 64 requests, each
+    with a chunk of U[2, 8] draft tokens after a history such that the context is
+    U[512, 4096] tokens; 32 q / 8 kv heads, d = 128, bf16.  Not one of the five reference
+    workloads: the shape of the batches the verify rows of the scope table describe."""
+    rng = np.random.default_rng(seed)
+    ctx = rng.integers(lo, hi + 1, size=num_seqs).astype(np.int32)
+    ns = rng.integers(c_lo, c_hi + 1, size=num_seqs).astype(np.int32)
+    return build("spec_verify", seed, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                 block_size=16, num_blocks=num_blocks, kv_dtype=BF16, io_dtype=BF16,
+                 num_computed=ctx - ns, num_scheduled=ns, rng=rng)
+
+
 CONFIGS = {
     1: tiny_f32,
     2: llama8b_decode,
     3: mixed_step,
     4: long_decode_70b,
     5: prefix_fp8_decode,
+    6: spec_verify,
 }
 
 

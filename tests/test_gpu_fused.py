@@ -141,14 +141,18 @@ def test_fused_equals_separate_random(R, seed):
     _check_out(w, sep)
 
 
+@pytest.mark.parametrize("min_rows", ["16", "2"])
 @pytest.mark.parametrize("kv", [W.BF16, W.FP8])
-def test_fused_decode_partitions_and_verify_rows(R, monkeypatch, kv):
+def test_fused_decode_partitions_and_verify_rows(R, monkeypatch, kv, min_rows):
     """Decode rows split into 64-key partitions (the newest key is written by
     the last partition's unit, which may hold that key alone), next to
-    speculative-verify-sized chunks of 2 to 8 rows (written by the scatter
-    pass before the split-K kernel reads them) and one prefill chunk."""
+    speculative-verify-sized chunks of 2 to 8 rows and one prefill chunk.  The
+    chunks' K/V are written by the scatter pass before the attention kernels
+    read them; the verify chunks run on the split-K kernel (threshold 16) or on
+    the MFMA extend kernel (threshold 2, the default)."""
     monkeypatch.setenv("PA_PARTITION_KEYS", "64")
-    say("fused partitions + verify rows", kv)
+    monkeypatch.setenv("PA_EXTEND_MIN_ROWS", min_rows)
+    say("fused partitions + verify rows", kv, "extend threshold", min_rows)
     nc = [64, 0, 127, 128, 300, 5, 64, 200, 40]
     ns = [1, 1, 1, 1, 1, 4, 8, 2, 24]
     w = W.build(f"fused_parts_{kv}", 7, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
@@ -223,3 +227,19 @@ def test_fused_rejects_null_rows(R):
                                      w.softmax_scale, 1, None, B._ptr(step.out),
                                      B._ptr(step.workspace), step.workspace.numel(), None)
     assert st == 1
+
+
+@pytest.mark.parametrize("min_rows", ["16", "2"])
+def test_spec_verify_workload(R, monkeypatch, min_rows):
+    """The speculative-verify workload (64 requests with 2..8 draft tokens after
+    long histories) with the verify chunks on the split-K kernel (threshold 16)
+    and on the MFMA extend kernel (threshold 2), one call with the KV update:
+    sampled rows against the oracle, slots and pool bytes exact."""
+    monkeypatch.setenv("PA_EXTEND_MIN_ROWS", min_rows)
+    say("spec verify, extend threshold", min_rows)
+    w = W.make(6)
+    step = R.GpuStep(w, fused=True)
+    step.run()
+    torch.cuda.synchronize()
+    assert (step.slots.cpu().numpy() == _want_slots(w)).all()
+    _check_out(w, step, _sample(w, 48, 6))
