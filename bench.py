@@ -50,6 +50,9 @@ def parse():
                          "instead of the one call that includes the KV update")
     ap.add_argument("--compare", action="store_true",
                     help="also time the other form of the step (same pool and inputs)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured once into a HIP graph and replayed "
+                         "(same batch every replay)")
     ap.add_argument("--cold", action="store_true",
                     help="also time steps that start with cold caches (a 1 GiB scratch read "
                          "before each step, outside the timed events)")
@@ -330,6 +333,32 @@ def main():
         other = round(e0.elapsed_time(e1) / a.steps, 5)
         step.fused = not a.separate
 
+    graph_ms = None
+    if a.graph:
+        # the step captured on a side stream, then replayed on the step's stream
+        gs = torch.cuda.Stream()
+        gs.wait_stream(stream)
+        step.stream = gs
+        with torch.cuda.stream(gs):
+            step.run()
+        gs.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=gs):
+            step.run()
+        step.stream = stream
+        torch.cuda.synchronize()
+        for _ in range(a.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(a.steps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = round(e0.elapsed_time(e1) / a.steps, 5)
+        del g
+
     cold = None
     if a.cold:
         # each step starts after a 1 GiB read, so L2 and the 256 MB Infinity
@@ -425,6 +454,7 @@ def main():
         "step_form": "separate calls" if a.separate else "one call with the KV update",
         **({("ms_per_step_one_call" if a.separate else "ms_per_step_separate_calls"): other}
            if other is not None else {}),
+        **({"ms_per_step_graph_replay": graph_ms} if graph_ms is not None else {}),
         "ms_per_step_with_kernel_events": round(ms_instr, 5),
         "ms_per_step_spread": spread,
         "decode_kv_gbps": roof["achieved"] if dom == "k_decode" else None,

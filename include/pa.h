@@ -35,6 +35,17 @@
  * - The library is thread-compatible: concurrent calls on different streams
  *   are allowed; the workspace passed to pa_attention must not be shared by
  *   calls that may run concurrently.
+ * - HIP graphs: every launching call may be captured into a HIP graph
+ *   (stream capture).  pa_attention and pa_write_kv_attention then write
+ *   their work lists into the workspace from inside the graph, so a replay
+ *   recomputes the captured batch on the current contents of the device
+ *   buffers.  The batch's shape (the host mirrors, num_tokens and the hint)
+ *   is fixed at capture; the device arrays, the pool, query/key/value and
+ *   the block-table contents are read at replay.  The workspace and every
+ *   buffer must stay allocated while the graph is replayed.  With
+ *   PA_VALIDATE set a captured call returns PA_ERR_UNSUPPORTED (the checks
+ *   read the block table back synchronously), and launches are not timed
+ *   by pa_profile_enable while captured.
  *
  * KV pool layout (chosen for gfx950, differs from the pages' layout)
  * ------------------------------------------------------------------
@@ -239,7 +250,7 @@ const char *pa_last_error(void);
  * runs on.  pa_profile_read() waits for the recorded events and returns,
  * for the kernel named `kernel`, the number of launches and their summed
  * duration in milliseconds since the last reset.  Enabling or disabling
- * resets the records.  Not for use under HIP graph capture. */
+ * resets the records.  Launches captured into a HIP graph are not timed. */
 pa_status pa_profile_enable(int32_t enable);
 pa_status pa_profile_read(const char *kernel, int32_t *launches, double *total_ms);
 

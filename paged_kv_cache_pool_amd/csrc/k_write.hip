@@ -8,6 +8,9 @@
 // fp8).  The pool tiles are laid out for gfx950 (see include/pa.h):
 //   K tile of (block, head): [head_dim / E][16 slots][E elements]  (16-byte chunks)
 //   V tile of (block, head): [head_dim][16 slots]
+#include <algorithm>
+#include <cstring>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -174,6 +177,36 @@ static hipError_t write_dispatch_d(const pa_kv_pool &p, const void *key, const v
                        p.num_kv_heads, cap, p.k_cache, p.v_cache, p.k_scale, p.v_scale);
   prof_end(s);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Plan copy for launches captured into a HIP graph: the work lists travel as
+// kernel arguments (captured by value into the graph node) and are written
+// into the caller's workspace, so every replay rebuilds the same lists
+// without any host buffer that the library might reuse later.
+// ---------------------------------------------------------------------------
+constexpr int kPieceWords = 992;     // 3968 bytes of payload per launch
+
+struct PlanPiece {
+  uint32_t words[kPieceWords];
+};
+
+__global__ __launch_bounds__(256) void k_plan_copy(const PlanPiece piece, uint32_t *__restrict__ dst,
+                                                   int32_t nwords) {
+  for (int i = threadIdx.x; i < nwords; i += blockDim.x) dst[i] = piece.words[i];
+}
+
+hipError_t launch_plan_copy(void *dst, const void *src, size_t bytes, hipStream_t s) {
+  const size_t words = bytes / 4;
+  for (size_t w0 = 0; w0 < words; w0 += kPieceWords) {
+    const int n = (int)std::min<size_t>(kPieceWords, words - w0);
+    PlanPiece piece;
+    memcpy(piece.words, (const uint32_t *)src + w0, (size_t)n * 4);
+    hipLaunchKernelGGL(k_plan_copy, dim3(1), dim3(256), 0, s, piece, (uint32_t *)dst + w0, n);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_write_kv(const pa_kv_pool &p, const void *key, const void *value,

@@ -60,8 +60,15 @@ static hipEvent_t prof_event() {
   return e;
 }
 
+static bool capturing(hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(s, &st) == hipSuccess && st != hipStreamCaptureStatusNone;
+}
+
+// Launches captured into a graph are not timed (their events would become
+// graph nodes).
 void prof_begin(const char *name, hipStream_t s) {
-  if (!g_prof_on) return;
+  if (!g_prof_on || capturing(s)) return;
   std::lock_guard<std::mutex> lk(g_prof_mu);
   ProfRec r{name, prof_event(), prof_event()};
   if (!r.start || !r.stop) return;
@@ -611,6 +618,9 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0f))
     return fail(PA_ERR_INVALID_ARG, "softmax_scale must be finite and positive");
   if (batch->num_tokens == 0) return PA_OK;
+  const bool graph = capturing(s);
+  if (graph && env_flag("PA_VALIDATE"))
+    return fail(PA_ERR_UNSUPPORTED, "PA_VALIDATE reads the block table back synchronously; not under graph capture");
   if (env_flag("PA_VALIDATE") && (st = validate_block_table(batch, pool->num_blocks, s)) != PA_OK) return st;
 
   Plan plan;
@@ -621,16 +631,14 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
     return fail(PA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, plan.bytes);
 
   // the work lists: written into a staging slot that the kernels read
-  // directly, or (PA_PLAN_UPLOAD=1) copied into the workspace
+  // directly, or (PA_PLAN_UPLOAD=1) copied into the workspace.  Under graph
+  // capture they are written into the workspace by captured copy kernels
+  // that carry them as arguments, so the graph owns its plan.
   const size_t plan_bytes = plan.off_ml;
   StageSlot *slot = nullptr;
   StageGuard guard;
   const char *items = (const char *)workspace;
-  if (plan_bytes) {
-    if ((st = stage_acquire(plan_bytes, &slot)) != PA_OK) return st;
-    guard.slot = slot;
-    guard.s = s;
-    char *host = (char *)slot->host;
+  auto fill = [&](char *host) {
     memset(host, 0, plan_bytes);
     if (!plan.dec.empty()) memcpy(host + plan.off_dec, plan.dec.data(), plan.dec.size() * sizeof(DecodeItem));
     if (!plan.merge.empty()) memcpy(host + plan.off_merge, plan.merge.data(), plan.merge.size() * sizeof(MergeItem));
@@ -641,6 +649,18 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
       memcpy(host + plan.off_rslot, plan.row_slot0.data(), plan.row_slot0.size() * sizeof(int32_t));
     }
     if (!plan.wseg.empty()) memcpy(host + plan.off_wseg, plan.wseg.data(), plan.wseg.size() * sizeof(WriteSeg));
+  };
+  if (plan_bytes && graph) {
+    std::vector<char> host(plan_bytes);
+    fill(host.data());
+    hipError_t ce = launch_plan_copy(workspace, host.data(), plan_bytes, s);
+    if (ce != hipSuccess) return hip_fail(ce, "plan copy launch");
+  } else if (plan_bytes) {
+    if ((st = stage_acquire(plan_bytes, &slot)) != PA_OK) return st;
+    guard.slot = slot;
+    guard.s = s;
+    char *host = (char *)slot->host;
+    fill(host);
     if (env_flag("PA_PLAN_UPLOAD")) {
       hipError_t ce = hipMemcpyAsync(workspace, host, plan_bytes, hipMemcpyHostToDevice, s);
       if (ce != hipSuccess) return hip_fail(ce, "plan upload");

@@ -166,6 +166,7 @@ hipError_t launch_slot_mapping(const pa_batch &b, int64_t *slots, int max_c, hip
 hipError_t launch_write_kv(const pa_kv_pool &p, const void *key, const void *value,
                            pa_dtype in_dtype, const int64_t *slots, int32_t num_tokens,
                            hipStream_t s);
+hipError_t launch_plan_copy(void *dst, const void *src, size_t bytes, hipStream_t s);
 hipError_t launch_write_new(const pa_kv_pool &p, pa_dtype in_dtype, const WriteArgs &a,
                             hipStream_t s);
 hipError_t launch_decode(const pa_kv_pool &p, pa_dtype q_dtype, const DecodeArgs &a,

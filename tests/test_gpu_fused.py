@@ -243,3 +243,62 @@ def test_spec_verify_workload(R, monkeypatch, min_rows):
     torch.cuda.synchronize()
     assert (step.slots.cpu().numpy() == _want_slots(w)).all()
     _check_out(w, step, _sample(w, 48, 6))
+
+
+# ------------------------------------------------------------- HIP graphs --
+
+@pytest.mark.parametrize("cfg,fused", [(1, True), (1, False), (2, True), (6, True)])
+def test_graph_capture_replays(R, cfg, fused):
+    """A step captured into a HIP graph (torch's stream capture around the
+    library's calls) replays the same batch: every replay equals the eager
+    step bit for bit, with unrelated eager steps of another batch (other
+    pool, own plans) run between the replays; new query contents written
+    between replays are read by the next replay."""
+    say("graph capture config", cfg, "fused", fused)
+    w = W.make(cfg)
+    s = torch.cuda.Stream()
+    step = R.GpuStep(w, stream=s, fused=fused)
+    with torch.cuda.stream(s):
+        step.run()
+    s.synchronize()
+    eager = step.out.clone()
+    eager_pool_k = step.pool.k_cache.clone()
+    other = R.GpuStep(W.make(1, seed=5), fused=True)
+    g = torch.cuda.CUDAGraph()
+    step.out.zero_()
+    with torch.cuda.graph(g, stream=s):
+        step.run()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        step.out.fill_(float("nan"))
+        other.run()                      # eager calls between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(step.out.view(torch.uint8), eager.view(torch.uint8)), rep
+        assert torch.equal(step.pool.k_cache, eager_pool_k)
+    # new query contents: the replay reads them
+    step.query.mul_(0.5)
+    g.replay()
+    torch.cuda.synchronize()
+    replayed = step.out.clone()
+    with torch.cuda.stream(s):
+        step.run()
+    s.synchronize()
+    assert torch.equal(replayed.view(torch.uint8), step.out.view(torch.uint8))
+    assert not torch.equal(replayed.view(torch.uint8), eager.view(torch.uint8))
+
+
+def test_graph_capture_rejects_validation(R, monkeypatch):
+    from paged_kv_cache_pool_amd import binding as B
+    say("graph capture + PA_VALIDATE")
+    w = W.make(1)
+    s = torch.cuda.Stream()
+    step = R.GpuStep(w, stream=s, fused=True)
+    monkeypatch.setenv("PA_VALIDATE", "1")
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(B.PaError) as e:
+        with torch.cuda.graph(g, stream=s):
+            step.run()
+    assert e.value.status == 2
+    torch.cuda.synchronize()
