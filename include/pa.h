@@ -82,7 +82,8 @@ typedef enum pa_status {
   PA_ERR_UNSUPPORTED = 2,  /* a valid request this build does not implement        */
   PA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required           */
   PA_ERR_VALIDATION = 4,   /* metadata failed the consistency checks (PA_VALIDATE) */
-  PA_ERR_HIP = 5           /* a HIP runtime call failed                            */
+  PA_ERR_HIP = 5,          /* a HIP runtime call failed                            */
+  PA_ERR_CAPACITY = 6      /* the block pool has too few free blocks               */
 } pa_status;
 
 typedef enum pa_dtype {
@@ -230,6 +231,86 @@ pa_status pa_write_kv_attention(const pa_kv_pool *pool, const pa_batch *batch, c
                                 int32_t num_q_heads, float softmax_scale, int32_t causal,
                                 int64_t *slot_mapping, void *output, void *workspace,
                                 size_t workspace_bytes, pa_stream_t stream);
+
+/* ---------------------------------------------------------------------- */
+/* Host block pool (the KV-cache manager on either side of the step).
+ *
+ * [P1] §4.2-4.3 (allocate_slots for running and waiting requests,
+ * get_computed_blocks for prefix-cache hits), §8.1 (free: every block's
+ * reference count drops, a block at zero returns to the free queue), §10
+ * (a request's blocks over prefill, decode and prefix reuse); [P5] second
+ * walk-through path (a free block keeps its contents for prefix hits until
+ * it is reused; the cache key covers the parent prefix and extra identity).
+ *
+ * Policy where the pages leave it open: the free queue starts in ascending
+ * block order and hands out from its head; a freed request returns its
+ * blocks last block first; a block handed out again leaves the hash map.
+ * Block hash: FNV-1a 64 over the little-endian bytes of the parent block's
+ * hash (0 for a request's first block), extra_key, and the block's
+ * block_size token ids as int32; lookups also compare the stored key.
+ *
+ * The manager is host memory only and never touches the device; calls on
+ * one manager are serialised by an internal lock.  Request ids are the
+ * caller's.  Errors: PA_ERR_INVALID_ARG for bad arguments or an unknown
+ * request; PA_ERR_CAPACITY when allocate_slots cannot be satisfied (then
+ * nothing changes). */
+typedef struct pa_kv_manager pa_kv_manager;
+
+/* A manager of blocks 0 .. num_blocks-1 of block_size tokens, all free. */
+pa_status pa_kv_manager_create(int32_t num_blocks, int32_t block_size, pa_kv_manager **manager);
+void pa_kv_manager_destroy(pa_kv_manager *manager);
+
+/* Blocks in the free queue (reference count 0, cached or not); -1 for NULL. */
+int32_t pa_kv_manager_num_free_blocks(pa_kv_manager *manager);
+
+/* get_computed_blocks: the longest run of leading full blocks of token_ids
+ * (num_tokens host int32 ids) whose contents are cached under extra_key.
+ * The block holding the last token is never reported, so a step always
+ * computes at least one token.  Writes up to max_blocks ids to blocks (host)
+ * and their number to *num_blocks; takes no reference (allocate_slots does). */
+pa_status pa_kv_manager_get_computed_blocks(pa_kv_manager *manager, const int32_t *token_ids,
+                                            int32_t num_tokens, uint64_t extra_key,
+                                            int32_t *blocks, int32_t max_blocks,
+                                            int32_t *num_blocks);
+
+/* allocate_slots: request_id will hold num_tokens tokens after the step.  A
+ * request without blocks first takes computed_blocks (from
+ * get_computed_blocks; each gets a reference and leaves the free queue).
+ * Then blocks are taken from the head of the free queue until the request
+ * has ceil(num_tokens / block_size).  The new blocks' ids (the ones to
+ * zero, new_block_ids_to_zero in [P1] §4.4) go to new_blocks (host, room
+ * for max_new) and their number to *num_new.  All or nothing:
+ * PA_ERR_CAPACITY leaves every count unchanged. */
+pa_status pa_kv_manager_allocate_slots(pa_kv_manager *manager, int64_t request_id,
+                                       int32_t num_tokens, const int32_t *computed_blocks,
+                                       int32_t num_computed_blocks, int32_t *new_blocks,
+                                       int32_t max_new, int32_t *num_new);
+
+/* Enters the request's full blocks among its first num_tokens tokens
+ * (token_ids, host) into the prefix cache under extra_key.  A block already
+ * cached, or whose key another block already holds, is left as it is. */
+pa_status pa_kv_manager_cache_blocks(pa_kv_manager *manager, int64_t request_id,
+                                     const int32_t *token_ids, int32_t num_tokens,
+                                     uint64_t extra_key);
+
+/* free: drops the request's reference on each of its blocks, last block
+ * first; blocks reaching zero join the tail of the free queue (still
+ * cached).  The request is forgotten. */
+pa_status pa_kv_manager_free(pa_kv_manager *manager, int64_t request_id);
+
+/* The request's block ids in logical order (its block-table row). */
+pa_status pa_kv_manager_block_ids(pa_kv_manager *manager, int64_t request_id, int32_t *blocks,
+                                  int32_t max_blocks, int32_t *num_blocks);
+
+/* Reference count of one block. */
+pa_status pa_kv_manager_ref_count(pa_kv_manager *manager, int32_t block, int32_t *ref_count);
+
+/* Zeroes every byte of the listed blocks in k_cache and v_cache (all kv
+ * heads), as the model runner clears newly allocated blocks ([P1] §5.1.1,
+ * _zero_block_ids).  block_ids: device int32 [num_ids]; ids outside the pool
+ * are skipped. */
+pa_status pa_zero_blocks(const pa_kv_pool *pool, const int32_t *block_ids, int32_t num_ids,
+                         pa_stream_t stream);
 
 /* Bytes of each of k_cache and v_cache for this pool's shape and dtype. */
 size_t pa_kv_cache_bytes(const pa_kv_pool *pool);

@@ -23,13 +23,17 @@ LIB_PATH = os.environ.get("PA_LIB") or os.path.join(_HERE, "_build", "libpa.so")
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 DTYPES = {"f32": PA_F32, "bf16": PA_BF16, "fp8": PA_FP8_E4M3}
 STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED", 3: "PA_ERR_WORKSPACE",
-          4: "PA_ERR_VALIDATION", 5: "PA_ERR_HIP"}
+          4: "PA_ERR_VALIDATION", 5: "PA_ERR_HIP", 6: "PA_ERR_CAPACITY"}
 
 # Every symbol include/pa.h declares.
 EXPORTS = ["pa_prepare_metadata", "pa_slot_mapping", "pa_write_kv", "pa_attention_workspace_bytes",
            "pa_attention", "pa_write_kv_attention", "pa_kv_cache_bytes", "pa_kv_elem_offset",
            "pa_status_string",
-           "pa_last_error", "pa_profile_enable", "pa_profile_read"]
+           "pa_last_error", "pa_profile_enable", "pa_profile_read",
+           "pa_kv_manager_create", "pa_kv_manager_destroy", "pa_kv_manager_num_free_blocks",
+           "pa_kv_manager_get_computed_blocks", "pa_kv_manager_allocate_slots",
+           "pa_kv_manager_cache_blocks", "pa_kv_manager_free", "pa_kv_manager_block_ids",
+           "pa_kv_manager_ref_count", "pa_zero_blocks"]
 
 
 class PaError(RuntimeError):
@@ -72,6 +76,16 @@ def _load():
         "pa_last_error": (C.c_char_p, []),
         "pa_profile_enable": (i32, [i32]),
         "pa_profile_read": (i32, [C.c_char_p, C.POINTER(i32), C.POINTER(C.c_double)]),
+        "pa_kv_manager_create": (i32, [i32, i32, C.POINTER(P)]),
+        "pa_kv_manager_destroy": (None, [P]),
+        "pa_kv_manager_num_free_blocks": (i32, [P]),
+        "pa_kv_manager_get_computed_blocks": (i32, [P, P, i32, C.c_uint64, P, i32, C.POINTER(i32)]),
+        "pa_kv_manager_allocate_slots": (i32, [P, i64, i32, P, i32, P, i32, C.POINTER(i32)]),
+        "pa_kv_manager_cache_blocks": (i32, [P, i64, P, i32, C.c_uint64]),
+        "pa_kv_manager_free": (i32, [P, i64]),
+        "pa_kv_manager_block_ids": (i32, [P, i64, P, i32, C.POINTER(i32)]),
+        "pa_kv_manager_ref_count": (i32, [P, i32, C.POINTER(i32)]),
+        "pa_zero_blocks": (i32, [pool_p, P, i32, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -273,6 +287,77 @@ def write_kv_attention(pool: KVPool, batch: Batch, query: torch.Tensor, key: tor
                                      int(causal), _ptr(slots), _ptr(out), _ptr(workspace),
                                      workspace.numel(), _stream(stream)))
     return out
+
+
+class KVManager:
+    """The library's host block pool (pa_kv_manager_*): allocate_slots, free,
+    reference counts, the free queue and block-hash prefix hits."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        h = C.c_void_p()
+        _check(lib.pa_kv_manager_create(num_blocks, block_size, C.byref(h)))
+        self._h = h
+        self.num_blocks, self.block_size = num_blocks, block_size
+
+    def close(self) -> None:
+        if self._h:
+            lib.pa_kv_manager_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def num_free_blocks(self) -> int:
+        return int(lib.pa_kv_manager_num_free_blocks(self._h))
+
+    def get_computed_blocks(self, token_ids, extra_key: int = 0) -> list:
+        t = np.ascontiguousarray(token_ids, dtype=np.int32)
+        out = np.empty(max(1, t.size // self.block_size + 1), dtype=np.int32)
+        n = C.c_int32(0)
+        _check(lib.pa_kv_manager_get_computed_blocks(self._h, _np_ptr(t), t.size, extra_key,
+                                                     _np_ptr(out), out.size, C.byref(n)))
+        return out[:n.value].tolist()
+
+    def allocate_slots(self, request_id: int, num_tokens: int, computed_blocks=()) -> Optional[list]:
+        """New block ids, or None when the pool has too few free blocks."""
+        cb = np.ascontiguousarray(list(computed_blocks), dtype=np.int32)
+        out = np.empty(max(1, -(-num_tokens // self.block_size)), dtype=np.int32)
+        n = C.c_int32(0)
+        st = lib.pa_kv_manager_allocate_slots(self._h, request_id, num_tokens,
+                                              _np_ptr(cb) if cb.size else None, cb.size,
+                                              _np_ptr(out), out.size, C.byref(n))
+        if st == 6:
+            return None
+        _check(st)
+        return out[:n.value].tolist()
+
+    def cache_blocks(self, request_id: int, token_ids, num_tokens: int, extra_key: int = 0) -> None:
+        t = np.ascontiguousarray(token_ids, dtype=np.int32)
+        assert num_tokens <= t.size
+        _check(lib.pa_kv_manager_cache_blocks(self._h, request_id, _np_ptr(t), num_tokens, extra_key))
+
+    def free(self, request_id: int) -> None:
+        _check(lib.pa_kv_manager_free(self._h, request_id))
+
+    def block_ids(self, request_id: int) -> list:
+        out = np.empty(self.num_blocks, dtype=np.int32)
+        n = C.c_int32(0)
+        _check(lib.pa_kv_manager_block_ids(self._h, request_id, _np_ptr(out), out.size, C.byref(n)))
+        return out[:n.value].tolist()
+
+    def ref_count(self, block: int) -> int:
+        r = C.c_int32(0)
+        _check(lib.pa_kv_manager_ref_count(self._h, block, C.byref(r)))
+        return int(r.value)
+
+
+def zero_blocks(pool: KVPool, block_ids: torch.Tensor, stream=None) -> None:
+    assert block_ids.dtype == torch.int32 and block_ids.is_contiguous()
+    p = pool.struct()
+    _check(lib.pa_zero_blocks(C.byref(p), _ptr(block_ids), int(block_ids.numel()), _stream(stream)))
 
 
 def profile_enable(on: bool) -> None:

@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(OUT_DIR, "libpa.so")
-SOURCES = ["pa_api.hip", "k_write.hip", "k_decode.hip", "k_extend.hip"]
+SOURCES = ["pa_api.hip", "k_write.hip", "k_decode.hip", "k_extend.hip", "kv_manager.cpp"]
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
 
@@ -36,7 +36,7 @@ def build(verbose: bool = False) -> str:
     cc = hipcc()
 
     def compile_one(src):
-        obj = os.path.join(OUT_DIR, src.replace(".hip", ".o"))
+        obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
         cmd = [cc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)

@@ -209,6 +209,35 @@ hipError_t launch_plan_copy(void *dst, const void *src, size_t bytes, hipStream_
   return hipSuccess;
 }
 
+// ---------------------------------------------------------------------------
+// Zeroing of newly allocated blocks ("vLLM 推理流程分析" §5.1.1, the model
+// runner clears the blocks the scheduler lists in new_block_ids_to_zero, so
+// that no stale K/V of an earlier owner can be read).  A block's tiles of all
+// kv heads are contiguous in each of k_cache and v_cache; one workgroup per
+// (block, array) clears them with 16-byte stores.  Ids outside the pool are
+// skipped.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_zero_blocks(const int32_t *__restrict__ ids, int32_t num_blocks,
+                                                     int64_t block_bytes, char *__restrict__ kc,
+                                                     char *__restrict__ vc) {
+  const int32_t b = ids[blockIdx.x];
+  if (b < 0 || b >= num_blocks) return;
+  char *base = (blockIdx.y == 0 ? kc : vc) + (int64_t)b * block_bytes;
+  for (int64_t o = threadIdx.x * 16; o < block_bytes; o += blockDim.x * 16)
+    *(uint4 *)(base + o) = make_uint4(0, 0, 0, 0);
+}
+
+hipError_t launch_zero_blocks(const pa_kv_pool &p, const int32_t *block_ids, int32_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int elem = p.kv_dtype == PA_F32 ? 4 : p.kv_dtype == PA_BF16 ? 2 : 1;
+  const int64_t block_bytes = (int64_t)p.num_kv_heads * p.head_dim * p.block_size * elem;
+  prof_begin("k_zero_blocks", s);
+  hipLaunchKernelGGL(k_zero_blocks, dim3((unsigned)n, 2), dim3(256), 0, s, block_ids, p.num_blocks,
+                     block_bytes, (char *)p.k_cache, (char *)p.v_cache);
+  prof_end(s);
+  return hipGetLastError();
+}
+
 hipError_t launch_write_kv(const pa_kv_pool &p, const void *key, const void *value,
                            pa_dtype in_dtype, const int64_t *slots, int32_t T, hipStream_t s) {
   if (T == 0) return hipSuccess;

@@ -32,6 +32,16 @@ static pa_status fail(pa_status st, const char *fmt, ...) {
   return st;
 }
 
+pa_status pa_set_error(pa_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
 static pa_status hip_fail(hipError_t e, const char *what) {
   return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -829,6 +839,15 @@ pa_status pa_write_kv_attention(const pa_kv_pool *pool, const pa_batch *batch, c
                         workspace, workspace_bytes, (hipStream_t)stream, &kvu);
 }
 
+pa_status pa_zero_blocks(const pa_kv_pool *pool, const int32_t *block_ids, int32_t num_ids,
+                         pa_stream_t stream) {
+  pa_status st = check_pool(pool, true);
+  if (st != PA_OK) return st;
+  if (num_ids < 0 || (num_ids > 0 && !block_ids)) return fail(PA_ERR_INVALID_ARG, "invalid block id list");
+  hipError_t e = launch_zero_blocks(*pool, block_ids, num_ids, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : hip_fail(e, "k_zero_blocks launch");
+}
+
 size_t pa_kv_cache_bytes(const pa_kv_pool *pool) {
   if (!pool || pool->num_blocks <= 0 || pool->block_size <= 0 || pool->num_kv_heads <= 0 || pool->head_dim <= 0)
     return 0;
@@ -856,6 +875,7 @@ const char *pa_status_string(pa_status status) {
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
     case PA_ERR_VALIDATION: return "PA_ERR_VALIDATION";
     case PA_ERR_HIP: return "PA_ERR_HIP";
+    case PA_ERR_CAPACITY: return "PA_ERR_CAPACITY";
   }
   return "PA_ERR_UNKNOWN";
 }

@@ -175,6 +175,11 @@ hipError_t launch_merge(pa_dtype q_dtype, int head_dim, const MergeArgs &a, hipS
 hipError_t launch_extend(const pa_kv_pool &p, const ExtendArgs &a, hipStream_t s);
 hipError_t launch_prefix(const pa_kv_pool &p, const ExtendArgs &a, hipStream_t s);
 
+// Records the error detail for pa_last_error() and returns `st`.
+pa_status pa_set_error(pa_status st, const char *fmt, ...);
+
+hipError_t launch_zero_blocks(const pa_kv_pool &p, const int32_t *block_ids, int32_t n, hipStream_t s);
+
 // Kernel timing hooks (no-ops unless profiling is enabled).
 void prof_begin(const char *name, hipStream_t s);
 void prof_end(hipStream_t s);
