@@ -133,12 +133,18 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
     for (int i = 0; i < NVL; ++i) o[h][i] = 0.0f;
   }
 
+  // block ids of the step's four blocks (lane l: block l / 16), read one
+  // step ahead so that the K/V loads never wait for the block table
+  const int tl = lane >> 4;                         // which of the 4 blocks
+  int phys_next = (kv_begin + tl * kBlock) < kv_last ? btrow[(kv_begin >> 4) + tl] : -1;
   for (int it = kv_begin; it < kv_last; it += kKeysPerIter) {
-    const int tl = lane >> 4;                       // which of the 4 blocks
     const int j = it + lane;                        // this lane's key position
-    const bool tile_in = (it + tl * kBlock) < kv_last;
-    int phys = tile_in ? btrow[(it >> 4) + tl] : -1;
+    int phys = phys_next;
     if (phys >= a.num_blocks) phys = -1;            // out-of-range id: never dereferenced
+    {
+      const int itn = it + kKeysPerIter;
+      phys_next = (itn + tl * kBlock) < kv_last ? btrow[(itn >> 4) + tl] : -1;
+    }
     const bool key_ok = phys >= 0 && j < kv_last;
 
     // ---- K row of this lane's key ----
@@ -211,7 +217,7 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float sv = key_ok ? s[h] * a.scale_log2 : -INFINITY;
-      const float mt = wave_max(sv);
+      const float mt = wave_max_dpp(sv);
       const float mn = fmaxf(m_run[h], mt);
       const bool any = mn != -INFINITY;
       const float alpha = any ? __builtin_amdgcn_exp2f(m_run[h] - mn) : 1.0f;
