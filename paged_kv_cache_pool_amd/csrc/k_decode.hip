@@ -1,6 +1,8 @@
 // Token-parallel split-K attention over the paged pool (decode tokens, and
 // any query row the plan does not give to the MFMA extend kernel), plus the
-// merge of partial results.
+// merge of partial results.  The vector-ALU kernel below serves fp32 pools
+// (fp32 arithmetic end to end); bf16 and fp8 pools use the matrix-core
+// version of the same work items, k_decode_mfma.
 //
 // What is computed ("vLLM 源码完全拆解（十六）", third walk-through path): for a
 // query row q of kv head kvh, the keys are walked through the block table
@@ -478,10 +480,8 @@ hipError_t launch_decode(const pa_kv_pool &p, pa_dtype q_dtype, const DecodeArgs
   if (a.n_items == 0) return hipSuccess;
   prof_begin("k_decode", s);
   hipError_t e;
-  if (p.kv_dtype == PA_BF16)
-    e = p.head_dim == 128 ? decode_g<KV_BF16, 128>(a, g_tmpl, s) : decode_g<KV_BF16, 64>(a, g_tmpl, s);
-  else if (p.kv_dtype == PA_FP8_E4M3)
-    e = p.head_dim == 128 ? decode_g<KV_FP8, 128>(a, g_tmpl, s) : decode_g<KV_FP8, 64>(a, g_tmpl, s);
+  if (p.kv_dtype == PA_BF16 || p.kv_dtype == PA_FP8_E4M3)
+    e = launch_decode_mfma(p, a, s);
   else
     e = p.head_dim == 128 ? decode_g<KV_F32, 128>(a, g_tmpl, s) : decode_g<KV_F32, 64>(a, g_tmpl, s);
   prof_end(s);

@@ -447,6 +447,21 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
     }
     mark_own_write();
   }
+  // Split-K units, longest first: workgroups are handed to compute units as
+  // earlier ones finish, so starting the long units first leaves short ones
+  // for the tail (longest-processing-time-first list scheduling).  A stable
+  // counting sort on the number of 64-key steps keeps this O(n).
+  if (plan.dec.size() > 1) {
+    auto steps = [](const DecodeItem &d) { return (d.kv_end - d.kv_begin + kKeysPerIter - 1) / kKeysPerIter; };
+    int32_t max_steps = 0;
+    for (const DecodeItem &d : plan.dec) max_steps = std::max(max_steps, steps(d));
+    std::vector<int32_t> start(max_steps + 2, 0);
+    for (const DecodeItem &d : plan.dec) ++start[max_steps - std::max(0, steps(d)) + 1];
+    for (int32_t k = 1; k <= max_steps + 1; ++k) start[k] += start[k - 1];
+    std::vector<DecodeItem> sorted(plan.dec.size());
+    for (const DecodeItem &d : plan.dec) sorted[start[max_steps - std::max(0, steps(d))]++] = d;
+    plan.dec.swap(sorted);
+  }
   // Extend tiles: workgroup b runs on XCD b % 8 (round-robin dispatch), and
   // all tiles of one (request, kv head) read the same K/V, so each (request,
   // kv head) is pinned to one XCD, whose L2 then serves the repeats.  Within

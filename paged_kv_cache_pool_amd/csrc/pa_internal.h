@@ -171,6 +171,8 @@ hipError_t launch_write_new(const pa_kv_pool &p, pa_dtype in_dtype, const WriteA
                             hipStream_t s);
 hipError_t launch_decode(const pa_kv_pool &p, pa_dtype q_dtype, const DecodeArgs &a,
                          int g_tmpl, hipStream_t s);
+// split-K decode on the matrix cores (bf16 and fp8 pools)
+hipError_t launch_decode_mfma(const pa_kv_pool &p, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_merge(pa_dtype q_dtype, int head_dim, const MergeArgs &a, hipStream_t s);
 hipError_t launch_extend(const pa_kv_pool &p, const ExtendArgs &a, hipStream_t s);
 hipError_t launch_prefix(const pa_kv_pool &p, const ExtendArgs &a, hipStream_t s);
