@@ -61,7 +61,7 @@ def parse():
 
 # Sources whose change invalidates a kernel's measured traffic.
 KERNEL_SOURCES = {
-    "k_decode": ["k_decode.hip", "pa_device.h", "pa_internal.h", "pa_api.hip"],
+    "k_decode": ["k_decode.hip", "k_decode_mfma.hip", "pa_device.h", "pa_internal.h", "pa_api.hip"],
     "k_extend": ["k_extend.hip", "pa_device.h", "pa_internal.h", "pa_api.hip"],
 }
 COPY_BYTES = 1 << 30
