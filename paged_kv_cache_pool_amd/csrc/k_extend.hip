@@ -123,9 +123,138 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | (((N >> 4) & 3) << 14));
 }
 
+// s_waitcnt lgkmcnt(0) only (vmcnt and expcnt left free).
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
+
+// Which 8-element k group of a 32x32x16 MFMA operand a lane feeds.
+__device__ __forceinline__ int hsel_of(int lane) { return lane >> 5; }
+
 // Workgroup barrier that leaves outstanding vector loads in flight (the
 // compiler's __syncthreads waits for every copy first).
 __device__ __forceinline__ void barrier_keep_loads() { asm volatile("s_barrier" ::: "memory"); }
+
+// x combined with its value in lane l ^ 32.  v_permlane32_swap of x with
+// itself returns, per lane, x and the partner's x (in an order that depends
+// on the half), so only symmetric combinations are formed.
+__device__ __forceinline__ float max_x32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_x32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One 64-key tile for this wave's 32 columns: S^T = K . Q^T, online
+// softmax, O^T += V^T . P^T.  `mask` (wave-uniform) applies the causal
+// limit of each column; it is set only on tiles that cross some column's
+// limit (the last one or two of a wave).
+template <int KV>
+__device__ __forceinline__ void xtile(const char *kb, const char *vb, int kbase, bool mask, int nvis, int lane,
+                                      float scale_log2, const bf16x8_t (&qop)[8], f32x16_t (&oacc)[4],
+                                      float &m_run, float &l_run) {
+  const int hsel = lane >> 5;
+  f32x16_t sacc[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {             // the two chains alternate
+      const int rho = mt * 32 + (lane & 31);
+      const int chunk = 2 * ks + hsel;
+      bf16x8_t aop;
+      if constexpr (KV == KV_BF16)
+        aop = as_bf16x8(*(const uint4 *)(kb + rho * 256 + ((chunk ^ (rho & 15)) * 16)));
+      else
+        aop = fp8x8_to_bf16x8(*(const uint2 *)(kb + rho * 128 + ((ks ^ ((rho >> 1) & 7)) * 16) + hsel * 8));
+      sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, qop[ks], sacc[mt], 0, 0, 0);
+    }
+  // Schedule: four LDS operand reads ahead, then alternate one MFMA and
+  // one read, so each read has about four MFMAs (~128 clocks) to land.
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int i = 0; i < 12; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+
+  // Online softmax (column = lane % 32).  Scores stay unscaled until the
+  // exponent (scale > 0 commutes with max).  The reference max is raised
+  // only when a column's maximum exceeds it by more than 2^8 (decided for
+  // the whole wave), so O and l are rescaled rarely; exp2(s * c - m_ref) <=
+  // 2^8 stays well inside bf16 and fp32, and O / l does not depend on the
+  // reference.
+  if (mask) {
+    const int lim = nvis - kbase;              // keys of this tile the column sees
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = swap23(mt * 32 + 8 * (r >> 2) + 4 * hsel + (r & 3));
+        sacc[mt][r] = key < lim ? sacc[mt][r] : -INFINITY;
+      }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
+  mx = max_x32(mx);
+  const float cand = mx * scale_log2;
+  const bool raise = cand > m_run + 8.0f;
+  if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+    const float m_new = raise ? cand : m_run;
+    const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int md = 0; md < 4; ++md)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[md][r] *= alpha;
+    m_run = m_new;
+  }
+  const float neg_m = m_run == -INFINITY ? 0.0f : -m_run;  // fully masked column: p = 0
+  float psum = 0.0f;
+  uint32_t pp[2][8];                           // P^T as bf16 pairs [mt][r / 2]
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[mt][r], scale_log2, neg_m));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[mt][r + 1], scale_log2, neg_m));
+      psum += p0 + p1;
+      pp[mt][r >> 1] = pack_bf16x2(p0, p1);
+    }
+  l_run += psum;
+
+  // O^T += V^T . P^T (k-step ks covers keys 16 ks .. 16 ks + 15)
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int mt = ks >> 1, half = ks & 1;
+    const bf16x8_t bop = as_bf16x8(make_uint4(pp[mt][half * 4 + 0], pp[mt][half * 4 + 1],
+                                              pp[mt][half * 4 + 2], pp[mt][half * 4 + 3]));
+#pragma unroll
+    for (int md = 0; md < 4; ++md) {                // keys 16 ks + 8 hsel .. +8 of dim d
+      const int d = md * 32 + (lane & 31);
+      bf16x8_t aop;
+      if constexpr (KV == KV_BF16)
+        aop = as_bf16x8(*(const uint4 *)(vb + vt_offset(d, 16 * ks + 8 * hsel)));
+      else
+        aop = fp8x8_to_bf16x8(*(const uint2 *)(vb + vt8_offset(d, 16 * ks + 8 * hsel)));
+      oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, oacc[md], 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+  for (int i = 0; i < 12; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+}
 
 // PREFIX = false: a prefill chunk of one request (columns = its new tokens x
 // GQA heads, causal or not), written to the output.  PREFIX = true: the
@@ -133,9 +262,8 @@ __device__ __forceinline__ void barrier_keep_loads() { asm volatile("s_barrier" 
 // request that shares the common prefix) x GQA heads, keys = one chunk of the
 // common prefix, all visible; written as partial (m, l, o) for the merge.
 template <int KV, bool PREFIX>
-__global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
+__device__ __forceinline__ void extend_split_body(const ExtendArgs &a, char *smem) {
   using X = XLayout<KV>;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
@@ -249,113 +377,6 @@ __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
     for (int r = 0; r < 16; ++r) oacc[md][r] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
-  // One 64-key tile for this wave's 32 columns: S^T = K . Q^T, online
-  // softmax, O^T += V^T . P^T.  `mask` (wave-uniform) applies the causal
-  // limit of each column; it is set only on tiles that cross some column's
-  // limit (the last one or two of a wave).
-  auto tile = [&](const char *kb, const char *vb, int kbase, bool mask) __attribute__((always_inline)) {
-    f32x16_t sacc[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.0f;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {             // the two chains alternate
-        const int rho = mt * 32 + (lane & 31);
-        const int chunk = 2 * ks + hsel;
-        bf16x8_t aop;
-        if constexpr (KV == KV_BF16)
-          aop = as_bf16x8(*(const uint4 *)(kb + rho * 256 + ((chunk ^ (rho & 15)) * 16)));
-        else
-          aop = fp8x8_to_bf16x8(*(const uint2 *)(kb + rho * 128 + ((ks ^ ((rho >> 1) & 7)) * 16) + hsel * 8));
-        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, qop[ks], sacc[mt], 0, 0, 0);
-      }
-    // Schedule: four LDS operand reads ahead, then alternate one MFMA and
-    // one read, so each read has about four MFMAs (~128 clocks) to land.
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int i = 0; i < 12; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-
-    // Online softmax (column = lane % 32).  Scores stay unscaled until the
-    // exponent (scale > 0 commutes with max).  The reference max is raised
-    // only when a column's maximum exceeds it by more than 2^8 (decided for
-    // the whole wave), so O and l are rescaled rarely; exp2(s * c - m_ref) <=
-    // 2^8 stays well inside bf16 and fp32, and O / l does not depend on the
-    // reference.
-    if (mask) {
-      const int lim = nvis - kbase;              // keys of this tile the column sees
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = swap23(mt * 32 + 8 * (r >> 2) + 4 * hsel + (r & 3));
-          sacc[mt][r] = key < lim ? sacc[mt][r] : -INFINITY;
-        }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float cand = mx * a.scale_log2;
-    const bool raise = cand > m_run + 8.0f;
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-      const float m_new = raise ? cand : m_run;
-      const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int md = 0; md < 4; ++md)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[md][r] *= alpha;
-      m_run = m_new;
-    }
-    const float neg_m = m_run == -INFINITY ? 0.0f : -m_run;  // fully masked column: p = 0
-    float psum = 0.0f;
-    uint32_t pp[2][8];                           // P^T as bf16 pairs [mt][r / 2]
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[mt][r], a.scale_log2, neg_m));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[mt][r + 1], a.scale_log2, neg_m));
-        psum += p0 + p1;
-        pp[mt][r >> 1] = pack_bf16x2(p0, p1);
-      }
-    l_run += psum;
-
-    // O^T += V^T . P^T (k-step ks covers keys 16 ks .. 16 ks + 15)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int mt = ks >> 1, half = ks & 1;
-      const bf16x8_t bop = as_bf16x8(make_uint4(pp[mt][half * 4 + 0], pp[mt][half * 4 + 1],
-                                                pp[mt][half * 4 + 2], pp[mt][half * 4 + 3]));
-#pragma unroll
-      for (int md = 0; md < 4; ++md) {                // keys 16 ks + 8 hsel .. +8 of dim d
-        const int d = md * 32 + (lane & 31);
-        bf16x8_t aop;
-        if constexpr (KV == KV_BF16)
-          aop = as_bf16x8(*(const uint4 *)(vb + vt_offset(d, 16 * ks + 8 * hsel)));
-        else
-          aop = fp8x8_to_bf16x8(*(const uint2 *)(vb + vt8_offset(d, 16 * ks + 8 * hsel)));
-        oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, oacc[md], 0, 0, 0);
-      }
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
-#pragma unroll
-    for (int i = 0; i < 12; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
-  };
-
   // Tiles go in pairs (2p, 2p + 1): group 0 computes the even tile, group 1
   // the odd one, for the same columns.  The ring holds two pairs: while pair
   // p is computed, pair p + 1 is in flight.
@@ -416,7 +437,8 @@ __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
     const int kbase = kt * kXT;
     if (kt >= n_tiles || !wave_active || kbase >= kend_w) continue;
     const char *kb = smem + (kt % kXStages) * X::kStage;
-    tile(kb, kb + X::kKBytes, kbase, kbase + kXT > wave_min_nvis);
+    xtile<KV>(kb, kb + X::kKBytes, kbase, kbase + kXT > wave_min_nvis, nvis, lane, a.scale_log2, qop, oacc,
+              m_run, l_run);
   }
 
   // Merge the odd-tile partial (m, l, O) of each column into the even-tile
@@ -425,7 +447,7 @@ __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
   //   O = O_0 2^(m_0 - m) + O_1 2^(m_1 - m),  l likewise,  m = max(m_0, m_1);
   // m_0 is finite (tile 0, key 0 is visible to every column), m_1 may be
   // -inf when the odd tiles hold no visible key.
-  const float l_half = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_half = sum_x32(l_run);
   __syncthreads();
   float *xo = (float *)smem;                     // [cw][md * 16 + r][lane]
   float *xm = xo + 4 * 64 * 64;                  // [cw][lane]
@@ -508,6 +530,235 @@ __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
   }
 }
 
+template <int KV, bool PREFIX>
+__global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  extend_split_body<KV, PREFIX>(a, smem);
+}
+
+// Wide workgroups for long prefill chunks.  A workgroup of 8 waves owns
+// kWideCols = 256 columns of one (request, kv head), one wave per 32
+// columns, and every wave takes every 64-key tile of the item's key range
+// [key0, min(key1, visible end)).  Each K/V tile copied into LDS then feeds
+// twice the columns of the key-split layout above, and a 4-stage ring lets
+// the copies of a tile start three tiles before it is computed: the copies
+// of tile t + 3 go into the stage of tile t - 1, which every wave has left
+// once it reaches the barrier at the top of tile t.  Q of the 256 columns
+// (64 KB) is copied into stage 3 and the 32 KB above the ring together with
+// the first tiles and moved to registers before stage 3 is refilled.
+//
+// A request whose items are too long to balance over the compute units is
+// cut into key pieces (item.slot0 >= 0): each piece writes partial
+// (m, l, o) at partial slot slot0 + token * slot_stride, and the merge
+// kernel combines the pieces ("vLLM 源码完全拆解（十六）", third walk-through
+// path: partitions of the key range merged by their maxima).
+template <int KV>
+__global__ __launch_bounds__(512, 1) void k_extend_wide(const ExtendArgs a) {
+  using X = XLayout<KV>;
+  constexpr int CPT = 2 * X::kCopies;            // copy instructions per wave per tile
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int g = a.g;
+  const ExtendItem item = a.items[blockIdx.x];
+  if (uniform(item.mode) != 0) {                 // a key-split item (kExtCols columns)
+    extend_split_body<KV, false>(a, smem);
+    return;
+  }
+  const int req = uniform(item.req), c = uniform(item.c), L = uniform(item.L);
+  const int kvh = uniform(item.kvh), tok0 = uniform(item.tok0), col0 = uniform(item.col0);
+  const int key0 = uniform(item.key0), key1 = uniform(item.key1);
+  const int slot0 = uniform(item.slot0), sstride = uniform(item.slot_stride);
+  const int ncols = c * g;
+  const int hist = L - c;                        // tokens before this step's first new token
+  const int32_t *btrow = a.block_table + (int64_t)req * a.bt_stride;
+  const bool causal = a.causal;
+  // keys [0, vis(cc)) are visible to column cc within this item (key1 caps a piece)
+  auto vis = [&](int cc) { return min(key1, causal ? hist + cc / g + 1 : L); };
+
+  const int last_col_wg = min(ncols, col0 + kWideCols) - 1;
+  const int kend_wg = vis(last_col_wg);          // key range of the workgroup: [key0, kend_wg)
+  const int t_first = key0 / kXT;                // key0 is a multiple of 64
+  const int t_end = (kend_wg + kXT - 1) / kXT;
+  const int blk_last = (kend_wg - 1) / kBlock;   // last logical block read
+  const int wcol0 = col0 + wave * 32;
+  const bool wave_active = wcol0 < ncols;
+  const int kend_w = wave_active ? vis(min(ncols, wcol0 + 32) - 1) : 0;
+  const int wave_min_nvis = vis(min(wcol0, ncols - 1));
+  const int col_raw = wcol0 + (lane & 31);
+  const int col = min(col_raw, ncols - 1);       // clamped; columns past ncols are not stored
+  const int nvis = vis(col);
+
+  // q / output row of workgroup column cc (clamped to a valid column)
+  auto out_row = [&](int cc) -> int64_t {
+    const int cg = min(col0 + cc, ncols - 1);
+    const int tt = cg / g;
+    return (int64_t)(tok0 + tt) * a.num_q_heads + kvh * g + (cg - tt * g);
+  };
+
+  const char *kpool = (const char *)a.k_cache + (int64_t)kvh * X::kTileB;
+  const char *vpool = (const char *)a.v_cache + (int64_t)kvh * X::kTileB;
+  const int64_t bstride = (int64_t)a.num_kv_heads * X::kTileB;
+  auto blk_id = [&](int b) -> int {
+    const int v = load_uniform(btrow + min(b, blk_last));
+    return (v >= 0 && v < a.num_blocks) ? v : 0;
+  };
+  // copy share of a tile: as in the key-split kernel (wave w copies 1 KB
+  // pieces of tile block w / 2)
+  uint32_t koff[X::kCopies], voff[X::kCopies];
+#pragma unroll
+  for (int u = 0; u < X::kCopies; ++u) {
+    if constexpr (KV == KV_BF16) {
+      const int I = wave * 2 + u;
+      const int rho = 4 * I + (lane >> 4);
+      const int chunk = (lane & 15) ^ (rho & 15);
+      koff[u] = chunk * 256 + (swap23(rho) & 15) * 16;
+      const int d = 32 * (I & 3) + (lane >> 1);
+      const int half = (lane & 1) ^ vt_swz(d);
+      voff[u] = d * 32 + half * 16;
+    } else {
+      const int rho = 8 * wave + (lane >> 3);
+      const int chunk = (lane & 7) ^ ((rho >> 1) & 7);
+      koff[u] = chunk * 256 + (swap23(rho) & 15) * 16;
+      voff[u] = (wave & 1) * 1024 + lane * 16;
+    }
+  }
+  const int my_blk = wave >> 1;
+  int next_id = blk_id(t_first * 4 + my_blk);   // block id of the next tile to issue
+  // ring stage of tile t: counted from the item's first tile, so that the
+  // first three tiles never land on stage 3 (Q)
+  auto stage = [&](int t) { return (t - t_first) & (kXStages - 1); };
+  auto issue = [&](int kt) {
+    char *kst = smem + stage(kt) * X::kStage + wave * (X::kCopies * 1024);
+    char *vst = kst + X::kKBytes;
+    const char *ksrc = kpool + (int64_t)next_id * bstride;
+    const char *vsrc = vpool + (int64_t)next_id * bstride;
+#pragma unroll
+    for (int u = 0; u < X::kCopies; ++u) {
+      copy16_to_lds(ksrc, koff[u], kst + u * 1024);
+      copy16_to_lds(vsrc, voff[u], vst + u * 1024);
+    }
+    next_id = blk_id((kt + 1) * 4 + my_blk);
+  };
+
+  f32x16_t oacc[4];
+#pragma unroll
+  for (int md = 0; md < 4; ++md)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[md][r] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
+  bf16x8_t qop[8];
+
+  // Q: row cc (256 bytes) holds column cc's 16-byte chunk c in slot
+  // c ^ (cc & 15); instruction u of wave w moves columns 4 (8 w + u) .. +3.
+  char *qst = smem + 3 * X::kStage;
+  {
+    const char *qsrc = (const char *)a.q + out_row(0) * (kXD * 2);
+    const int64_t row0 = out_row(0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int J = wave * 8 + u;
+      const int cc = 4 * J + (lane >> 4);
+      const int chunk = (lane & 15) ^ (cc & 15);
+      copy16_to_lds(qsrc, (uint32_t)((out_row(cc) - row0) * (kXD * 2) + chunk * 16), qst + J * 1024);
+    }
+  }
+  issue(t_first);
+  if (t_first + 1 < t_end) issue(t_first + 1);
+  if (t_first + 2 < t_end) issue(t_first + 2);
+  for (int t = t_first; t < t_end; ++t) {
+    // this wave's copies of tile t (and Q) have landed when at most the
+    // copies of tiles t + 1 and t + 2 are outstanding; the barrier makes
+    // every wave's copies visible and frees the stage of tile t - 1
+    const int ahead = min(2, t_end - 1 - t);
+    if (ahead == 2) wait_vm_lgkm0<2 * CPT>();
+    else if (ahead == 1) wait_vm_lgkm0<CPT>();
+    else wait_vm_lgkm0<0>();
+    barrier_keep_loads();
+    if (t == t_first) {
+      const int cc = wave * 32 + (lane & 31);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        qop[ks] = as_bf16x8(*(const uint4 *)(qst + cc * 256 + (((2 * ks + hsel_of(lane)) ^ (cc & 15)) * 16)));
+      wait_lgkm0();
+      barrier_keep_loads();                      // every wave holds Q before stage 3 is refilled
+    }
+    if (t + 3 < t_end) issue(t + 3);
+    if (t == t_end - 1 && kend_wg < t_end * kXT) {
+      // keys past the range may hold anything (unwritten slots, stand-in
+      // blocks); zero their V so that 0 * v stays 0
+      char *vb = smem + stage(t) * X::kStage + X::kKBytes;
+      const int kv = kend_wg - t * kXT;
+      for (int e = tid; e < kXD * kXT; e += 512) {
+        const int d = e >> 6, k = e & 63;
+        if (k >= kv) {
+          if constexpr (KV == KV_BF16) *(uint16_t *)(vb + vt_offset(d, k)) = 0;
+          else *(uint8_t *)(vb + vt8_offset(d, k)) = 0;
+        }
+      }
+      __syncthreads();
+    }
+    const int kbase = t * kXT;
+    if (!wave_active || kbase >= kend_w) continue;
+    const char *kb = smem + stage(t) * X::kStage;
+    xtile<KV>(kb, kb + X::kKBytes, kbase, kbase + kXT > wave_min_nvis, nvis, lane, a.scale_log2, qop, oacc,
+              m_run, l_run);
+  }
+
+  const float l_tot = sum_x32(l_run);
+  const int hsel = hsel_of(lane);
+  if (slot0 >= 0) {
+    // a key piece: partial (m, l, o), o unnormalised relative to m (log2
+    // units) with v_scale applied -- the split-K kernel's format
+    if (!wave_active || col_raw >= ncols) return;
+    const int r = col / g;
+    const int head = kvh * g + (col - r * g);
+    const int64_t slot = (int64_t)slot0 + (int64_t)r * sstride;
+    float *po = a.part_o + (slot * a.num_q_heads + head) * kXD;
+#pragma unroll
+    for (int md = 0; md < 4; ++md)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int dim = md * 32 + 8 * q + 4 * hsel;  // rows r = 4q .. 4q+3
+        *(float4 *)(po + dim) = make_float4(oacc[md][4 * q] * a.v_scale, oacc[md][4 * q + 1] * a.v_scale,
+                                            oacc[md][4 * q + 2] * a.v_scale, oacc[md][4 * q + 3] * a.v_scale);
+      }
+    if (hsel == 0) {
+      float *pml = a.part_ml + (slot * a.num_q_heads + head) * 2;
+      pml[0] = m_run;
+      pml[1] = l_tot;
+    }
+    return;
+  }
+  // whole range: normalise, stage the bf16 rows in LDS (pitch 272 bytes) and
+  // write them out as whole 256-byte rows
+  constexpr int kOutPitch = kXD * 2 + 16;
+  __syncthreads();                               // every wave is done with the ring
+  if (wave_active) {
+    const float inv = a.v_scale / l_tot;
+    char *orow = smem + (wave * 32 + (lane & 31)) * kOutPitch;
+#pragma unroll
+    for (int md = 0; md < 4; ++md)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int dim = md * 32 + 8 * q + 4 * hsel;
+        *(uint2 *)(orow + dim * 2) = make_uint2(pack_bf16x2(oacc[md][4 * q] * inv, oacc[md][4 * q + 1] * inv),
+                                                pack_bf16x2(oacc[md][4 * q + 2] * inv, oacc[md][4 * q + 3] * inv));
+      }
+  }
+  __syncthreads();
+  const int ncols_wg = min(kWideCols, ncols - col0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int piece = tid + 512 * i;             // column piece / 16, 16-byte chunk piece % 16
+    const int cc = piece >> 4, chunk = piece & 15;
+    if (cc < ncols_wg)
+      *(uint4 *)((char *)a.out + out_row(cc) * (kXD * 2) + chunk * 16) =
+          *(const uint4 *)(smem + cc * kOutPitch + chunk * 16);
+  }
+}
+
 // The LDS size above the default limit is a per-device attribute of each
 // kernel: set it once for each (kernel, device) the library launches on.
 template <int KV, bool PREFIX>
@@ -537,11 +788,38 @@ static hipError_t launch_t(int n, const ExtendArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_extend(const pa_kv_pool &p, const ExtendArgs &a, hipStream_t s) {
+constexpr int kWLds = 160 * 1024;              // wide kernel: stages 0-2, then Q over stage 3 and above
+static_assert(3 * XLayout<KV_BF16>::kStage + 64 * 1024 <= kWLds, "Q fits after three stages");
+static_assert(kWideCols * (kXD * 2 + 16) <= kWLds, "output staging fits");
+
+template <int KV>
+static hipError_t launch_wide_t(int n, const ExtendArgs &a, hipStream_t s) {
+  static std::mutex mu;
+  static std::vector<char> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    if ((int)done.size() <= dev) done.resize(dev + 1, 0);
+    if (!done[dev]) {
+      e = hipFuncSetAttribute((const void *)k_extend_wide<KV>, hipFuncAttributeMaxDynamicSharedMemorySize, kWLds);
+      if (e != hipSuccess) return e;
+      done[dev] = 1;
+    }
+  }
+  prof_begin("k_extend", s);
+  hipLaunchKernelGGL((k_extend_wide<KV>), dim3(n), dim3(512), kWLds, s, a);
+  prof_end(s);
+  return hipGetLastError();
+}
+
+// Wide items (a.items, kWideCols columns each, possibly key pieces).
+hipError_t launch_extend_wide(const pa_kv_pool &p, const ExtendArgs &a, hipStream_t s) {
   if (a.n_items == 0) return hipSuccess;
   if (p.head_dim != kXD) return hipErrorNotSupported;
-  if (p.kv_dtype == PA_BF16) return launch_t<KV_BF16, false>(a.n_items, a, s);
-  if (p.kv_dtype == PA_FP8_E4M3) return launch_t<KV_FP8, false>(a.n_items, a, s);
+  if (p.kv_dtype == PA_BF16) return launch_wide_t<KV_BF16>(a.n_items, a, s);
+  if (p.kv_dtype == PA_FP8_E4M3) return launch_wide_t<KV_FP8>(a.n_items, a, s);
   return hipErrorNotSupported;
 }
 

@@ -306,7 +306,7 @@ static pa_status validate_block_table(const pa_batch *b, int32_t num_blocks, hip
 struct Plan {
   std::vector<DecodeItem> dec;
   std::vector<MergeItem> merge;
-  std::vector<ExtendItem> ext;
+  std::vector<ExtendItem> extw;                  // extend items (wide and key-split), one launch
   // shared-prefix (cascade) pass
   std::vector<PrefixItem> pre;
   std::vector<int32_t> row_token, row_slot0;
@@ -317,7 +317,7 @@ struct Plan {
   std::vector<WriteSeg> wseg;
   int32_t n_slots = 0;
   int32_t part_len = 0;
-  size_t off_dec = 0, off_merge = 0, off_ext = 0, off_pre = 0, off_rtok = 0, off_rslot = 0, off_wseg = 0;
+  size_t off_dec = 0, off_merge = 0, off_extw = 0, off_pre = 0, off_rtok = 0, off_rslot = 0, off_wseg = 0;
   size_t off_ml = 0, off_o = 0, bytes = 0;
 };
 
@@ -338,12 +338,30 @@ static bool extend_supported(const pa_kv_pool &p, pa_dtype q_dtype) {
   return q_dtype == PA_BF16 && (p.kv_dtype == PA_BF16 || p.kv_dtype == PA_FP8_E4M3) && p.head_dim == 128;
 }
 
+// Compute units of the current device (256 on MI355X), cached per device;
+// 256 when no device can be queried.
+static int device_cu_count() {
+  static std::mutex mu;
+  static std::vector<int> cus;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  if ((int)cus.size() <= dev) cus.resize(dev + 1, 0);
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dtype q_dtype,
                        int causal, bool kv_update, Plan &plan) {
   const int32_t *q = b.query_start_loc_host, *L = b.seq_lens_host;
   const int Hkv = p.num_kv_heads, g = Hq / Hkv;
   const bool ext_ok = extend_supported(p, q_dtype) && env_flag("PA_DISABLE_EXTEND") == false;
   const int ext_min = extend_min_rows();
+  std::vector<int32_t> ext_reqs;                 // requests on the MFMA extend kernel, planned after the loop
 
   // Shared prefix (cascade): the split-K rows' first P keys are the same
   // blocks for every request; their attention over them is computed once per
@@ -411,10 +429,7 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
         if (plan.dec[k].kv_end == L[i]) plan.dec[k].wpos = L[i] - 1;
     };
     if (ext_ok && c >= ext_min) {
-      const int64_t cols = (int64_t)c * g;
-      for (int kvh = 0; kvh < Hkv; ++kvh)
-        for (int64_t c0 = 0; c0 < cols; c0 += kExtCols)
-          plan.ext.push_back(ExtendItem{i, kvh, q[i], c, L[i], (int32_t)c0, {0, 0}});
+      ext_reqs.push_back(i);
       continue;
     }
     for (int32_t t = 0; t < c; ++t) {
@@ -447,6 +462,124 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
     }
     mark_own_write();
   }
+  // Extend items, all run by one launch of the wide kernel.
+  //  * A request with at most kExtCols (token, head) columns per kv head is
+  //    one key-split item (mode 1) per kv head: 4 x 32 columns, the key tiles
+  //    shared out between two wave groups of the workgroup.
+  //  * Wider requests are cut into blocks of kWideCols columns.  A wide item
+  //    (mode 0) gives each of its 8 waves 32 columns and every key tile: each
+  //    tile copied into LDS feeds twice the columns, and one wide step costs
+  //    about 1 / kSplitCost of a key-split step for the same MFMA work (a
+  //    64-key tile x 256 columns).  But a wide item's critical path is twice
+  //    as long, so a batch of a few long blocks runs them as key-split pairs.
+  //  * PA_WIDE_PIECES = n cuts every wide block into n key pieces whose
+  //    partial (m, l, o) the merge kernel combines (n is the same for all
+  //    blocks of a request: the merge of a row needs all its heads' pieces).
+  //    PA_DISABLE_WIDE runs every request as key-split items.
+  if (!ext_reqs.empty()) {
+    constexpr double kSplitCost = 1.38;          // key-split pair step / wide step (measured, mixed step)
+    constexpr int kXcds = 8;
+    const bool wide_ok = !env_flag("PA_DISABLE_WIDE");
+    const char *force = getenv("PA_WIDE_PIECES");
+    auto tiles = [&](int32_t i, int64_t c0, int64_t width) -> int64_t {
+      const int64_t c = q[i + 1] - q[i];
+      const int64_t kend = causal ? (int64_t)L[i] - c + std::min<int64_t>(c, (c0 + width + g - 1) / g) : L[i];
+      return (kend + 63) / 64;
+    };
+    struct Blk { int32_t req; int32_t c0; int64_t tw; double cost_w, cost_s; };
+    std::vector<Blk> fixed_split, wide;          // key-split-only blocks (128 cols); wide-capable blocks (256)
+    for (int32_t i : ext_reqs) {
+      const int64_t cols = (int64_t)(q[i + 1] - q[i]) * g;
+      if (!wide_ok || cols <= kExtCols) {
+        for (int64_t c0 = 0; c0 < cols; c0 += kExtCols)
+          fixed_split.push_back(Blk{i, (int32_t)c0, 0, 0.0, kSplitCost * ((tiles(i, c0, kExtCols) + 1) / 2)});
+      } else {
+        for (int64_t c0 = 0; c0 < cols; c0 += kWideCols) {
+          const int64_t tw = tiles(i, c0, kWideCols);
+          double cs = kSplitCost * ((tiles(i, c0, kExtCols) + 1) / 2);
+          if (c0 + kExtCols < cols) cs = std::max(cs, kSplitCost * ((tiles(i, c0 + kExtCols, kExtCols) + 1) / 2));
+          wide.push_back(Blk{i, (int32_t)c0, tw, (double)tw, cs});
+        }
+      }
+    }
+    // Wide items only when the batch is large enough that the longest one is
+    // at most half of a compute unit's average load: then the longest-first
+    // schedule balances them and the cheaper wide step wins.  Otherwise (a
+    // few long causal blocks, as in one mixed step with a 1.5k-token chunk)
+    // every block runs as key-split pairs, whose critical path is half as
+    // long: measured on such a step, both a mix of the two and key pieces
+    // were no faster than key-split alone.
+    int64_t X = INT64_MAX;                       // wide blocks with tw >= X run as key-split pairs
+    if (!wide.empty() && !force) {
+      double total = 0.0;
+      int64_t tmax = 0;
+      for (const Blk &b0 : fixed_split) total += b0.cost_s * Hkv;
+      for (const Blk &b0 : wide) {
+        total += b0.cost_w * Hkv;
+        tmax = std::max(tmax, b0.tw);
+      }
+      if ((double)tmax > 0.5 * total / device_cu_count()) X = 0;
+    }
+    int32_t np = force ? std::max(1, atoi(force)) : 1;
+    auto push = [&](int32_t i, int32_t c0, int32_t mode, int32_t k0, int32_t k1, int32_t slot0, int32_t stride) {
+      const int32_t c = q[i + 1] - q[i];
+      for (int kvh = 0; kvh < Hkv; ++kvh)
+        plan.extw.push_back(ExtendItem{i, kvh, q[i], c, L[i], c0, k0, k1, slot0, stride, mode, 0});
+    };
+    for (const Blk &b0 : fixed_split) push(b0.req, b0.c0, 1, 0, L[b0.req], -1, 0);
+    // forced key pieces: per request, np pieces (no more than the shortest block's tiles)
+    std::vector<int32_t> req_np(b.num_seqs, 1), req_base(b.num_seqs, -1);
+    if (np > 1) {
+      std::vector<int64_t> tmin(b.num_seqs, INT64_MAX);
+      for (const Blk &b0 : wide) tmin[b0.req] = std::min(tmin[b0.req], b0.tw);
+      for (int32_t i : ext_reqs) {
+        if (tmin[i] == INT64_MAX) continue;
+        const int32_t c = q[i + 1] - q[i];
+        req_np[i] = (int32_t)std::max<int64_t>(1, std::min<int64_t>(np, tmin[i]));
+        if (req_np[i] > 1) {
+          req_base[i] = plan.n_slots;
+          for (int32_t t = 0; t < c; ++t) plan.merge.push_back(MergeItem{q[i] + t, plan.n_slots + t * req_np[i], req_np[i], 0});
+          plan.n_slots += c * req_np[i];
+        }
+      }
+    }
+    for (const Blk &b0 : wide) {
+      const int32_t i = b0.req;
+      if (b0.tw >= X) {
+        push(i, b0.c0, 1, 0, L[i], -1, 0);
+        if ((int64_t)b0.c0 + kExtCols < (int64_t)(q[i + 1] - q[i]) * g) push(i, b0.c0 + kExtCols, 1, 0, L[i], -1, 0);
+        continue;
+      }
+      const int64_t n = req_np[i];
+      for (int64_t pc = 0; pc < n; ++pc) {
+        const int32_t k0 = (int32_t)(b0.tw * pc / n * 64);
+        const int32_t k1 = pc + 1 == n ? L[i] : (int32_t)(b0.tw * (pc + 1) / n * 64);
+        push(i, b0.c0, 0, k0, k1, n > 1 ? req_base[i] + (int32_t)pc : -1, n > 1 ? (int32_t)n : 0);
+      }
+    }
+    // workgroup b runs on XCD b % 8: each (request, kv head) is pinned to one
+    // XCD (its K/V stay in that XCD's L2), longest items first within an XCD
+    auto cost_of = [&](const ExtendItem &x) -> double {
+      const int64_t width = x.mode ? kExtCols : kWideCols;
+      const int64_t vis = causal ? (int64_t)x.L - x.c + std::min<int64_t>(x.c, (x.col0 + width + g - 1) / g) : x.L;
+      const int64_t t = (std::min<int64_t>(x.key1, vis) + 63) / 64 - x.key0 / 64;
+      return x.mode ? kSplitCost * ((t + 1) / 2) : (double)t;
+    };
+    std::vector<std::vector<ExtendItem>> qx(kXcds);
+    for (const ExtendItem &x : plan.extw) qx[(x.req * Hkv + x.kvh) % kXcds].push_back(x);
+    for (auto &v : qx)
+      std::stable_sort(v.begin(), v.end(), [&](const ExtendItem &x, const ExtendItem &y) { return cost_of(x) > cost_of(y); });
+    plan.extw.clear();
+    std::vector<size_t> pos(kXcds, 0);
+    for (bool more = true; more;) {
+      more = false;
+      for (int x = 0; x < kXcds; ++x)
+        if (pos[x] < qx[x].size()) {
+          plan.extw.push_back(qx[x][pos[x]++]);
+          more = true;
+        }
+    }
+  }
   // Split-K units, longest first: workgroups are handed to compute units as
   // earlier ones finish, so starting the long units first leaves short ones
   // for the tail (longest-processing-time-first list scheduling).  A stable
@@ -461,31 +594,6 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
     std::vector<DecodeItem> sorted(plan.dec.size());
     for (const DecodeItem &d : plan.dec) sorted[start[max_steps - std::max(0, steps(d))]++] = d;
     plan.dec.swap(sorted);
-  }
-  // Extend tiles: workgroup b runs on XCD b % 8 (round-robin dispatch), and
-  // all tiles of one (request, kv head) read the same K/V, so each (request,
-  // kv head) is pinned to one XCD, whose L2 then serves the repeats.  Within
-  // an XCD the longest tiles (key range grows with the column offset) go
-  // first.
-  if (!plan.ext.empty()) {
-    constexpr int kXcds = 8;
-    auto keys_of = [g](const ExtendItem &x) {
-      return (int64_t)x.L - x.c + std::min<int64_t>(x.c, (x.col0 + kExtCols + g - 1) / g);
-    };
-    std::vector<std::vector<ExtendItem>> q(kXcds);
-    for (const ExtendItem &x : plan.ext) q[(x.req * Hkv + x.kvh) % kXcds].push_back(x);
-    for (auto &v : q)
-      std::stable_sort(v.begin(), v.end(), [&](const ExtendItem &x, const ExtendItem &y) { return keys_of(x) > keys_of(y); });
-    plan.ext.clear();
-    std::vector<size_t> pos(kXcds, 0);
-    for (bool more = true; more;) {
-      more = false;
-      for (int x = 0; x < kXcds; ++x)
-        if (pos[x] < q[x].size()) {
-          plan.ext.push_back(q[x][pos[x]++]);
-          more = true;
-        }
-    }
   }
 
   // Prefix items: all chunks of one kv head read the same blocks, so each kv
@@ -514,8 +622,8 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
   off = align256(off + plan.dec.size() * sizeof(DecodeItem));
   plan.off_merge = off;
   off = align256(off + plan.merge.size() * sizeof(MergeItem));
-  plan.off_ext = off;
-  off = align256(off + plan.ext.size() * sizeof(ExtendItem));
+  plan.off_extw = off;
+  off = align256(off + plan.extw.size() * sizeof(ExtendItem));
   plan.off_pre = off;
   off = align256(off + plan.pre.size() * sizeof(PrefixItem));
   plan.off_rtok = off;
@@ -667,7 +775,7 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
     memset(host, 0, plan_bytes);
     if (!plan.dec.empty()) memcpy(host + plan.off_dec, plan.dec.data(), plan.dec.size() * sizeof(DecodeItem));
     if (!plan.merge.empty()) memcpy(host + plan.off_merge, plan.merge.data(), plan.merge.size() * sizeof(MergeItem));
-    if (!plan.ext.empty()) memcpy(host + plan.off_ext, plan.ext.data(), plan.ext.size() * sizeof(ExtendItem));
+    if (!plan.extw.empty()) memcpy(host + plan.off_extw, plan.extw.data(), plan.extw.size() * sizeof(ExtendItem));
     if (!plan.pre.empty()) {
       memcpy(host + plan.off_pre, plan.pre.data(), plan.pre.size() * sizeof(PrefixItem));
       memcpy(host + plan.off_rtok, plan.row_token.data(), plan.row_token.size() * sizeof(int32_t));
@@ -723,22 +831,25 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
   // the extend kernel goes to the side stream when decode work runs beside it
   hipStream_t xs = s;
   SideStream *side = nullptr;
-  const bool fork = !plan.ext.empty() && !plan.dec.empty() && env_flag("PA_OVERLAP");
+  // (not with key pieces: their partials are merged on the caller's stream)
+  const bool fork = !plan.extw.empty() && plan.merge.empty() && !plan.dec.empty() && env_flag("PA_OVERLAP");
   if (fork) {
     if ((st = side_stream(&side)) != PA_OK) return st;
     if ((e = hipEventRecord(side->fork, s)) != hipSuccess) return hip_fail(e, "fork record");
     if ((e = hipStreamWaitEvent(side->stream, side->fork, 0)) != hipSuccess) return hip_fail(e, "fork wait");
     xs = side->stream;
   }
-  if (!plan.ext.empty()) {
+  if (!plan.extw.empty()) {
     ExtendArgs x{};
     x.q = query;
     x.out = output;
     x.k_cache = pool->k_cache;
     x.v_cache = pool->v_cache;
     x.block_table = batch->block_table;
-    x.items = (const ExtendItem *)(items + plan.off_ext);
-    x.n_items = (int32_t)plan.ext.size();
+    x.items = (const ExtendItem *)(items + plan.off_extw);
+    x.part_ml = (float *)(ws + plan.off_ml);
+    x.part_o = (float *)(ws + plan.off_o);
+    x.n_items = (int32_t)plan.extw.size();
     x.bt_stride = batch->bt_stride;
     x.num_blocks = pool->num_blocks;
     x.num_kv_heads = pool->num_kv_heads;
@@ -748,8 +859,8 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
     x.scale_log2 = softmax_scale * log2e * kscale;
     x.k_scale = kscale;
     x.v_scale = vscale;
-    e = launch_extend(*pool, x, xs);
-    if (e != hipSuccess) return hip_fail(e, "k_extend launch");
+    e = launch_extend_wide(*pool, x, xs);
+    if (e != hipSuccess) return hip_fail(e, "k_extend_wide launch");
   }
   if (!plan.pre.empty()) {
     ExtendArgs x{};

@@ -66,10 +66,16 @@ struct MergeItem {
   int32_t pad;
 };
 
-// One workgroup of the MFMA extend kernel: columns [col0, col0 + kExtCols) of
-// request `req`, where column k is (token t = k / g, q head hg = k % g) of
-// kv head `kvh`; the request's new tokens start at stream row `tok0`, there
-// are `c` of them and the request holds `L` tokens in total.
+// One workgroup of an MFMA extend kernel: columns [col0, col0 + kExtCols)
+// (key-split kernel) or [col0, col0 + kWideCols) (wide kernel) of request
+// `req`, where column k is (token t = k / g, q head hg = k % g) of kv head
+// `kvh`; the request's new tokens start at stream row `tok0`, there are `c`
+// of them and the request holds `L` tokens in total.  Wide items only: the
+// item covers keys [key0, key1) of the columns' visible ranges (key0 a
+// multiple of 64); with slot0 >= 0 it is one key piece of its columns and
+// writes partial (m, l, o) of token t (0-based within the request) at
+// partial slot slot0 + t * slot_stride, else the output.  The wide kernel
+// also runs key-split items (mode 1), so that one launch can mix both.
 struct ExtendItem {
   int32_t req;
   int32_t kvh;
@@ -77,7 +83,12 @@ struct ExtendItem {
   int32_t c;
   int32_t L;
   int32_t col0;
-  int32_t pad[2];
+  int32_t key0;
+  int32_t key1;
+  int32_t slot0;
+  int32_t slot_stride;
+  int32_t mode;           // wide kernel: 0 = wide item, 1 = key-split item (kExtCols columns)
+  int32_t pad;
 };
 
 // One workgroup of the shared-prefix (cascade) pass: columns [col0, col0 +
@@ -160,6 +171,7 @@ struct ExtendArgs {
 };
 
 constexpr int kExtCols = 128;        // columns per extend workgroup (4 x 32, keys split over 2 waves)
+constexpr int kWideCols = 256;       // columns per wide extend workgroup (8 x 32, every wave every key)
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_slot_mapping(const pa_batch &b, int64_t *slots, int max_c, hipStream_t s);
@@ -174,7 +186,8 @@ hipError_t launch_decode(const pa_kv_pool &p, pa_dtype q_dtype, const DecodeArgs
 // split-K decode on the matrix cores (bf16 and fp8 pools)
 hipError_t launch_decode_mfma(const pa_kv_pool &p, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_merge(pa_dtype q_dtype, int head_dim, const MergeArgs &a, hipStream_t s);
-hipError_t launch_extend(const pa_kv_pool &p, const ExtendArgs &a, hipStream_t s);
+// all extend items (wide and key-split) in one launch
+hipError_t launch_extend_wide(const pa_kv_pool &p, const ExtendArgs &a, hipStream_t s);
 hipError_t launch_prefix(const pa_kv_pool &p, const ExtendArgs &a, hipStream_t s);
 
 // Records the error detail for pa_last_error() and returns `st`.
