@@ -277,14 +277,27 @@ def spec_verify(seed: int = 0, num_seqs: int = 64, lo: int = 512, hi: int = 4096
                 c_hi: int = 8, num_blocks: int = 40000) -> Workload:
     """Speculative-decoding verify step on the Llama-3-8B decode layer: 64 requests, each
     with a chunk of U[2, 8] draft tokens after a history such that the context is
-    U[512, 4096] tokens; 32 q / 8 kv heads, d = 128, bf16.  Not one of the five reference
-    workloads: the shape of the batches the verify rows of the scope table describe."""
+    U[512, 4096] tokens; 32 q / 8 kv heads, d = 128, bf16: the shape of a batch that
+    checks draft tokens (each request has a few new rows over a long history)."""
     rng = np.random.default_rng(seed)
     ctx = rng.integers(lo, hi + 1, size=num_seqs).astype(np.int32)
     ns = rng.integers(c_lo, c_hi + 1, size=num_seqs).astype(np.int32)
     return build("spec_verify", seed, num_q_heads=32, num_kv_heads=8, head_dim=128,
                  block_size=16, num_blocks=num_blocks, kv_dtype=BF16, io_dtype=BF16,
                  num_computed=ctx - ns, num_scheduled=ns, rng=rng)
+
+
+def long_prefill(seed: int = 0, num_seqs: int = 2, chunk: int = 4096, cached: int = 2048,
+                 num_blocks: int = 40000) -> Workload:
+    """Chunked prefill of long prompts on the Llama-3-8B layer: 2 requests, each a
+    4096-token chunk after 2048 cached tokens (causal over chunk + history); 32 q / 8 kv
+    heads, d = 128, bf16.  A batch large enough to fill the chip with prefill tiles."""
+    rng = np.random.default_rng(seed)
+    nc = np.full(num_seqs, cached, dtype=np.int32)
+    ns = np.full(num_seqs, chunk, dtype=np.int32)
+    return build("long_prefill", seed, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                 block_size=16, num_blocks=num_blocks, kv_dtype=BF16, io_dtype=BF16,
+                 num_computed=nc, num_scheduled=ns, rng=rng)
 
 
 CONFIGS = {
@@ -294,6 +307,7 @@ CONFIGS = {
     4: long_decode_70b,
     5: prefix_fp8_decode,
     6: spec_verify,
+    7: long_prefill,
 }
 
 

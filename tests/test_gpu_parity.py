@@ -174,7 +174,7 @@ def test_attention_tiny_f32_config(R):
     _check_attention(w, step)
 
 
-@pytest.mark.parametrize("cfg,n", [(2, 24), (3, 40), (5, 24)])
+@pytest.mark.parametrize("cfg,n", [(2, 24), (3, 40), (5, 24), (7, 24)])
 def test_attention_full_size_sampled(R, cfg, n):
     say("attention config", cfg)
     w = W.make(cfg)
