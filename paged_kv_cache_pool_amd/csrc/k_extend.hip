@@ -555,7 +555,6 @@ __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
 template <int KV>
 __global__ __launch_bounds__(512, 1) void k_extend_wide(const ExtendArgs a) {
   using X = XLayout<KV>;
-  constexpr int CPT = 2 * X::kCopies;            // copy instructions per wave per tile
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -666,15 +665,12 @@ __global__ __launch_bounds__(512, 1) void k_extend_wide(const ExtendArgs a) {
   }
   issue(t_first);
   if (t_first + 1 < t_end) issue(t_first + 1);
-  if (t_first + 2 < t_end) issue(t_first + 2);
-  for (int t = t_first; t < t_end; ++t) {
-    // this wave's copies of tile t (and Q) have landed when at most the
-    // copies of tiles t + 1 and t + 2 are outstanding; the barrier makes
-    // every wave's copies visible and frees the stage of tile t - 1
-    const int ahead = min(2, t_end - 1 - t);
-    if (ahead == 2) wait_vm_lgkm0<2 * CPT>();
-    else if (ahead == 1) wait_vm_lgkm0<CPT>();
-    else wait_vm_lgkm0<0>();
+  for (int t = t_first; t < t_end; t += 2) {
+    // Tiles go in steps of two with one barrier per step: only this step's
+    // copies (and, at the first step, Q's) are outstanding; the barrier makes
+    // every wave's copies visible and frees the stages of the previous step,
+    // into which the next step's tiles are copied while this step computes.
+    wait_vm_lgkm0<0>();
     barrier_keep_loads();
     if (t == t_first) {
       const int cc = wave * 32 + (lane & 31);
@@ -684,12 +680,14 @@ __global__ __launch_bounds__(512, 1) void k_extend_wide(const ExtendArgs a) {
       wait_lgkm0();
       barrier_keep_loads();                      // every wave holds Q before stage 3 is refilled
     }
+    if (t + 2 < t_end) issue(t + 2);
     if (t + 3 < t_end) issue(t + 3);
-    if (t == t_end - 1 && kend_wg < t_end * kXT) {
+    if (t + 2 >= t_end && kend_wg < t_end * kXT) {
       // keys past the range may hold anything (unwritten slots, stand-in
       // blocks); zero their V so that 0 * v stays 0
-      char *vb = smem + stage(t) * X::kStage + X::kKBytes;
-      const int kv = kend_wg - t * kXT;
+      const int tl = t_end - 1;
+      char *vb = smem + stage(tl) * X::kStage + X::kKBytes;
+      const int kv = kend_wg - tl * kXT;
       for (int e = tid; e < kXD * kXT; e += 512) {
         const int d = e >> 6, k = e & 63;
         if (k >= kv) {
@@ -699,11 +697,15 @@ __global__ __launch_bounds__(512, 1) void k_extend_wide(const ExtendArgs a) {
       }
       __syncthreads();
     }
-    const int kbase = t * kXT;
-    if (!wave_active || kbase >= kend_w) continue;
-    const char *kb = smem + stage(t) * X::kStage;
-    xtile<KV>(kb, kb + X::kKBytes, kbase, kbase + kXT > wave_min_nvis, nvis, lane, a.scale_log2, qop, oacc,
-              m_run, l_run);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int tt = t + u;
+      const int kbase = tt * kXT;
+      if (tt >= t_end || !wave_active || kbase >= kend_w) continue;
+      const char *kb = smem + stage(tt) * X::kStage;
+      xtile<KV>(kb, kb + X::kKBytes, kbase, kbase + kXT > wave_min_nvis, nvis, lane, a.scale_log2, qop, oacc,
+                m_run, l_run);
+    }
   }
 
   const float l_tot = sum_x32(l_run);
