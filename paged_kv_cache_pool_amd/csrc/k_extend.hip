@@ -159,6 +159,7 @@ __device__ __forceinline__ void xtile(const char *kb, const char *vb, int kbase,
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.0f;
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
@@ -181,6 +182,7 @@ __device__ __forceinline__ void xtile(const char *kb, const char *vb, int kbase,
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  __builtin_amdgcn_s_setprio(0);
 
   // Online softmax (column = lane % 32).  Scores stay unscaled until the
   // exponent (scale > 0 commutes with max).  The reference max is raised
@@ -231,6 +233,7 @@ __device__ __forceinline__ void xtile(const char *kb, const char *vb, int kbase,
   l_run += psum;
 
   // O^T += V^T . P^T (k-step ks covers keys 16 ks .. 16 ks + 15)
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const int mt = ks >> 1, half = ks & 1;
@@ -254,6 +257,7 @@ __device__ __forceinline__ void xtile(const char *kb, const char *vb, int kbase,
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // PREFIX = false: a prefill chunk of one request (columns = its new tokens x
