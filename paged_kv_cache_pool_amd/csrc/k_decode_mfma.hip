@@ -26,6 +26,10 @@
 // applied to the output, as in k_decode.  The probabilities are rounded to
 // bf16 for the PV product; l sums them in fp32.
 //
+// Loads: bf16 K/V tiles are read non-temporally (each byte is read once per
+// row); measured faster on the bf16 decode workloads (up to 6 % when prefill
+// data fills the caches), and slower on the fp8 pool, which keeps plain loads.
+//
 // Pipelining: the next step's K is read as soon as this step's S products have
 // consumed the K registers, and the next step's V as soon as the PV products
 // have consumed V, so a wave always has one step's K or V in flight while it
@@ -49,6 +53,14 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// 16 bytes from global memory, non-temporal (streamed: each K/V byte of a
+// decode row is read once, so it is not kept in the caches at the expense of
+// data that is reused).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const void *p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4_t *)p));
+}
 
 // 8 E4M3 codes -> 8 bf16 values (exact)
 __device__ __forceinline__ bf16x8_t fp8x8_bf16(uint32_t lo, uint32_t hi) {
@@ -181,7 +193,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int x = 0; x < NKX; ++x) kr[2 * c2 + h][x] = *(const uint4 *)(kp + 64 * h + 1024 * x);
+        for (int x = 0; x < NKX; ++x)
+          kr[2 * c2 + h][x] = F8 ? *(const uint4 *)(kp + 64 * h + 1024 * x) : load_stream(kp + 64 * h + 1024 * x);
     }
   };
   auto issue_v = [&](int b0, int b1, int b2, int b3) {
@@ -190,7 +203,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       const int p = c2 == 0 ? pick(vsel, b0, b1) : pick(vsel, b2, b3);
       const char *vp = vbase + (int64_t)(p < 0 ? 0 : p) * bstride + vofs;
 #pragma unroll
-      for (int dg = 0; dg < NDG; ++dg) vr[c2][dg] = *(const VReg *)(vp + 16 * VROW * dg);
+      for (int dg = 0; dg < NDG; ++dg) {
+        if constexpr (F8) vr[c2][dg] = *(const VReg *)(vp + 16 * VROW * dg);
+        else vr[c2][dg] = load_stream(vp + 16 * VROW * dg);
+      }
     }
   };
 
