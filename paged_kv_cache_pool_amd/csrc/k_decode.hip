@@ -403,7 +403,13 @@ __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
 // outputs are then summed with the weights broadcast from LDS.
 template <int D, bool F32OUT>
 __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
-  __shared__ float wts[4][64];
+  // Lanes are split into PPI groups of D / 4 lanes; group s takes partials
+  // r = s, s + PPI, ... and each of its lanes 4 dims of them (one float4 per
+  // partial), so one load instruction reads PPI whole partials and each
+  // lane keeps U of them in flight.
+  constexpr int LPP = D / 4;                     // lanes per partial
+  constexpr int PPI = 64 / LPP;                  // partials per load instruction
+  constexpr int U = 8;
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int unit = blockIdx.x * 4 + wave;
@@ -415,48 +421,63 @@ __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
   const float *ml = a.part_ml + ((int64_t)first * a.num_q_heads + qh) * 2;
   const int64_t ml_stride = (int64_t)a.num_q_heads * 2;
 
+  // m = max_r m_r, l = sum_r 2^(m_r - m) l_r (a partial without keys has m_r = -inf)
   float m = -INFINITY;
   for (int r0 = 0; r0 < count; r0 += 64)
     if (r0 + lane < count) m = fmaxf(m, ml[(r0 + lane) * ml_stride]);
   m = wave_max_dpp(m);
-
-  constexpr int NE = D / 64;
-  float acc[NE];
-#pragma unroll
-  for (int i = 0; i < NE; ++i) acc[i] = 0.0f;
   float l = 0.0f;
   for (int r0 = 0; r0 < count; r0 += 64) {
     const int r = r0 + lane;
-    float wgt = 0.0f;
     if (r < count) {
       const float mr = ml[r * ml_stride];
-      wgt = mr == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mr - m);
-      l = fmaf(wgt, ml[r * ml_stride + 1], l);
+      if (mr != -INFINITY) l = fmaf(__builtin_amdgcn_exp2f(mr - m), ml[r * ml_stride + 1], l);
     }
-    wts[wave][lane] = wgt;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int n = min(64, count - r0);
-    const float *po = a.part_o + ((int64_t)(first + r0) * a.num_q_heads + qh) * D + lane;
-    const int64_t po_stride = (int64_t)a.num_q_heads * D;
-#pragma unroll 4
-    for (int k = 0; k < n; ++k) {
-      const float w = wts[wave][k];
-#pragma unroll
-      for (int i = 0; i < NE; ++i) acc[i] = fmaf(w, po[k * po_stride + i * 64], acc[i]);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
   l = wave_sum_dpp(l);
-  const float inv = 1.0f / l;
+
+  // O = sum_r 2^(m_r - m) o_r / l
+  const int sub = lane / LPP, d4 = lane % LPP;
+  const float *po = a.part_o + ((int64_t)first * a.num_q_heads + qh) * D + 4 * d4;
+  const int64_t po_stride = (int64_t)a.num_q_heads * D;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int r0 = sub; r0 < count; r0 += PPI * U) {
+    float4 v[U];
+    float mr[U];
 #pragma unroll
-  for (int i = 0; i < NE; ++i) {
-    const int64_t idx = ((int64_t)token * a.num_q_heads + qh) * D + i * 64 + lane;
-    if constexpr (F32OUT) ((float *)a.out)[idx] = acc[i] * inv;
-    else ((uint16_t *)a.out)[idx] = f32_to_bf16(acc[i] * inv);
+    for (int u = 0; u < U; ++u) {
+      const int r = r0 + u * PPI;
+      const int rc = r < count ? r : r0;         // in range; its weight is dropped below
+      v[u] = *(const float4 *)(po + rc * po_stride);
+      mr[u] = r < count ? ml[rc * ml_stride] : -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w = mr[u] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mr[u] - m);
+      acc.x = fmaf(w, v[u].x, acc.x);
+      acc.y = fmaf(w, v[u].y, acc.y);
+      acc.z = fmaf(w, v[u].z, acc.z);
+      acc.w = fmaf(w, v[u].w, acc.w);
+    }
+  }
+  // sum the PPI groups (lanes d4, d4 + LPP, ...)
+#pragma unroll
+  for (int o = LPP; o < 64; o <<= 1) {
+    acc.x += __shfl_xor(acc.x, o, 64);
+    acc.y += __shfl_xor(acc.y, o, 64);
+    acc.z += __shfl_xor(acc.z, o, 64);
+    acc.w += __shfl_xor(acc.w, o, 64);
+  }
+  if (sub != 0) return;
+  const float inv = 1.0f / l;
+  const int64_t idx = ((int64_t)token * a.num_q_heads + qh) * D + 4 * d4;
+  if constexpr (F32OUT) {
+    *(float4 *)((float *)a.out + idx) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  } else {
+    uint2 w2;
+    w2.x = (uint32_t)f32_to_bf16(acc.x * inv) | ((uint32_t)f32_to_bf16(acc.y * inv) << 16);
+    w2.y = (uint32_t)f32_to_bf16(acc.z * inv) | ((uint32_t)f32_to_bf16(acc.w * inv) << 16);
+    *(uint2 *)((uint16_t *)a.out + idx) = w2;
   }
 }
 
