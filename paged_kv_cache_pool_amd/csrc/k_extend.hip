@@ -544,12 +544,12 @@ __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
 // kWideCols = 256 columns of one (request, kv head), one wave per 32
 // columns, and every wave takes every 64-key tile of the item's key range
 // [key0, min(key1, visible end)).  Each K/V tile copied into LDS then feeds
-// twice the columns of the key-split layout above, and a 4-stage ring lets
-// the copies of a tile start three tiles before it is computed: the copies
-// of tile t + 3 go into the stage of tile t - 1, which every wave has left
-// once it reaches the barrier at the top of tile t.  Q of the 256 columns
+// twice the columns of the key-split layout above.  Tiles go in steps of two
+// through a 4-stage ring with one barrier per step: the barrier at the top
+// of a step frees the previous step's two stages, and the next step's tiles
+// are copied into them while this step computes.  Q of the 256 columns
 // (64 KB) is copied into stage 3 and the 32 KB above the ring together with
-// the first tiles and moved to registers before stage 3 is refilled.
+// the first step's tiles and moved to registers before stage 3 is refilled.
 //
 // A request whose items are too long to balance over the compute units is
 // cut into key pieces (item.slot0 >= 0): each piece writes partial
@@ -630,7 +630,7 @@ __global__ __launch_bounds__(512, 1) void k_extend_wide(const ExtendArgs a) {
   const int my_blk = wave >> 1;
   int next_id = blk_id(t_first * 4 + my_blk);   // block id of the next tile to issue
   // ring stage of tile t: counted from the item's first tile, so that the
-  // first three tiles never land on stage 3 (Q)
+  // first step's two tiles never land on stage 3 (Q)
   auto stage = [&](int t) { return (t - t_first) & (kXStages - 1); };
   auto issue = [&](int kt) {
     char *kst = smem + stage(kt) * X::kStage + wave * (X::kCopies * 1024);
