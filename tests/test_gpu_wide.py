@@ -161,3 +161,41 @@ def test_wide_default_large_prefill(R, monkeypatch):
     err = float(np.abs(got - ref).max())
     say("large prefill sampled max_abs_err", err)
     assert np.isfinite(got).all() and err <= TOL
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_wide_pieces_graph_capture(R, monkeypatch, fused):
+    """A step with wide items cut into two key pieces (so the merge runs too),
+    captured into a HIP graph: every replay equals the eager step bit for bit,
+    with an eager step of another batch between replays, and a replay reads
+    new query contents."""
+    monkeypatch.setenv("PA_WIDE_PIECES", "2")
+    w = _chunk_batch("wide_graph", 4, 600, 1000, W.BF16)
+    s = torch.cuda.Stream()
+    step = R.GpuStep(w, stream=s, fused=fused)
+    with torch.cuda.stream(s):
+        step.run()
+    s.synchronize()
+    eager = step.out.clone()
+    other = R.GpuStep(_chunk_batch("wide_graph_other", 8, 257, 300, W.BF16), fused=True)
+    g = torch.cuda.CUDAGraph()
+    step.out.zero_()
+    with torch.cuda.graph(g, stream=s):
+        step.run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        say("wide graph replay", rep, "fused", fused)
+        step.out.fill_(float("nan"))
+        other.run()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(step.out.view(torch.uint8), eager.view(torch.uint8)), rep
+    step.query.mul_(0.5)
+    g.replay()
+    torch.cuda.synchronize()
+    replayed = step.out.clone()
+    with torch.cuda.stream(s):
+        step.run()
+    s.synchronize()
+    assert torch.equal(replayed.view(torch.uint8), step.out.view(torch.uint8))
