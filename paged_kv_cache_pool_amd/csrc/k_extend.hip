@@ -145,14 +145,42 @@ __device__ __forceinline__ float sum_x32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Per-lane byte offsets of a wave's MFMA operands inside a stage, computed
+// once per kernel.  K (S^T = K . Q^T), k-step ks: row rho = 32 mt +
+// (lane & 31) of the permuted tile, 16-byte chunk 2 ks + hsel at its
+// swizzled slot; the row block mt adds a constant (kKRowBlk).  The XOR of ks
+// with lane bits is not affine in ks, so one offset per ks is kept.  V^T
+// (O^T += V^T . P^T): dim d = 32 md + (lane & 31), keys 16 ks + 8 hsel; the
+// swizzle bit depends on d's low bits only, so md and ks add constants
+// (kVmd, kVks) and one offset serves every read.
+template <int KV>
+struct XOperands {
+  static constexpr int kKRowBlk = 32 * XLayout<KV>::kRow;       // 8192 / 4096
+  static constexpr int kVks = KV == KV_BF16 ? 4096 : 2048;
+  static constexpr int kVmd = KV == KV_BF16 ? 32 * 32 : 32 * 16;
+  int k[8];
+  int v;
+  __device__ __forceinline__ explicit XOperands(int lane) {
+    const int hsel = lane >> 5, r = lane & 31;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if constexpr (KV == KV_BF16) k[ks] = r * 256 + (((2 * ks + hsel) ^ (r & 15)) * 16);
+      else k[ks] = r * 128 + ((ks ^ ((r >> 1) & 7)) * 16) + hsel * 8;
+    }
+    if constexpr (KV == KV_BF16) v = XLayout<KV>::kKBytes + vt_offset(r, 8 * hsel);
+    else v = XLayout<KV>::kKBytes + vt8_offset(r, 8 * hsel);
+  }
+};
+
 // One 64-key tile for this wave's 32 columns: S^T = K . Q^T, online
 // softmax, O^T += V^T . P^T.  `mask` (wave-uniform) applies the causal
 // limit of each column; it is set only on tiles that cross some column's
 // limit (the last one or two of a wave).
 template <int KV>
-__device__ __forceinline__ void xtile(const char *kb, const char *vb, int kbase, bool mask, int nvis, int lane,
-                                      float scale_log2, const bf16x8_t (&qop)[8], f32x16_t (&oacc)[4],
+__device__ __forceinline__ void xtile(const char *stg, const XOperands<KV> &op, int kbase, bool mask, int nvis,
+                                      int lane, float scale_log2, const bf16x8_t (&qop)[8], f32x16_t (&oacc)[4],
                                       float &m_run, float &l_run) {
+  using OP = XOperands<KV>;
   const int hsel = lane >> 5;
   f32x16_t sacc[2];
 #pragma unroll
@@ -164,13 +192,10 @@ __device__ __forceinline__ void xtile(const char *kb, const char *vb, int kbase,
   for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {             // the two chains alternate
-      const int rho = mt * 32 + (lane & 31);
-      const int chunk = 2 * ks + hsel;
+      const char *ka = stg + op.k[ks] + mt * OP::kKRowBlk;
       bf16x8_t aop;
-      if constexpr (KV == KV_BF16)
-        aop = as_bf16x8(*(const uint4 *)(kb + rho * 256 + ((chunk ^ (rho & 15)) * 16)));
-      else
-        aop = fp8x8_to_bf16x8(*(const uint2 *)(kb + rho * 128 + ((ks ^ ((rho >> 1) & 7)) * 16) + hsel * 8));
+      if constexpr (KV == KV_BF16) aop = as_bf16x8(*(const uint4 *)ka);
+      else aop = fp8x8_to_bf16x8(*(const uint2 *)ka);
       sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, qop[ks], sacc[mt], 0, 0, 0);
     }
   // Schedule: four LDS operand reads ahead, then alternate one MFMA and
@@ -218,8 +243,12 @@ __device__ __forceinline__ void xtile(const char *kb, const char *vb, int kbase,
       for (int r = 0; r < 16; ++r) oacc[md][r] *= alpha;
     m_run = m_new;
   }
+  // P is rounded to bf16 for the PV product, and l sums those rounded
+  // values (one v_dot2 with (1, 1) per pair, two chains), so the weights the
+  // output is normalised by are exactly the ones it is made of.
   const float neg_m = m_run == -INFINITY ? 0.0f : -m_run;  // fully masked column: p = 0
-  float psum = 0.0f;
+  constexpr uint32_t kOnes = 0x3F803F80u;      // (1.0, 1.0) in bf16
+  float psum0 = 0.0f, psum1 = 0.0f;
   uint32_t pp[2][8];                           // P^T as bf16 pairs [mt][r / 2]
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
@@ -227,10 +256,11 @@ __device__ __forceinline__ void xtile(const char *kb, const char *vb, int kbase,
     for (int r = 0; r < 16; r += 2) {
       const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[mt][r], scale_log2, neg_m));
       const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[mt][r + 1], scale_log2, neg_m));
-      psum += p0 + p1;
       pp[mt][r >> 1] = pack_bf16x2(p0, p1);
+      if (mt == 0) psum0 = dot2_bf16(pp[mt][r >> 1], kOnes, psum0);
+      else psum1 = dot2_bf16(pp[mt][r >> 1], kOnes, psum1);
     }
-  l_run += psum;
+  l_run += psum0 + psum1;
 
   // O^T += V^T . P^T (k-step ks covers keys 16 ks .. 16 ks + 15)
   __builtin_amdgcn_s_setprio(1);
@@ -240,13 +270,11 @@ __device__ __forceinline__ void xtile(const char *kb, const char *vb, int kbase,
     const bf16x8_t bop = as_bf16x8(make_uint4(pp[mt][half * 4 + 0], pp[mt][half * 4 + 1],
                                               pp[mt][half * 4 + 2], pp[mt][half * 4 + 3]));
 #pragma unroll
-    for (int md = 0; md < 4; ++md) {                // keys 16 ks + 8 hsel .. +8 of dim d
-      const int d = md * 32 + (lane & 31);
+    for (int md = 0; md < 4; ++md) {                // keys 16 ks + 8 hsel .. +8 of dim 32 md + lane % 32
+      const char *va = stg + op.v + ks * OP::kVks + md * OP::kVmd;
       bf16x8_t aop;
-      if constexpr (KV == KV_BF16)
-        aop = as_bf16x8(*(const uint4 *)(vb + vt_offset(d, 16 * ks + 8 * hsel)));
-      else
-        aop = fp8x8_to_bf16x8(*(const uint2 *)(vb + vt8_offset(d, 16 * ks + 8 * hsel)));
+      if constexpr (KV == KV_BF16) aop = as_bf16x8(*(const uint4 *)va);
+      else aop = fp8x8_to_bf16x8(*(const uint2 *)va);
       oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, oacc[md], 0, 0, 0);
     }
   }
@@ -380,6 +408,7 @@ __device__ __forceinline__ void extend_split_body(const ExtendArgs &a, char *sme
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[md][r] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
+  const XOperands<KV> xop(lane);
 
   // Tiles go in pairs (2p, 2p + 1): group 0 computes the even tile, group 1
   // the odd one, for the same columns.  The ring holds two pairs: while pair
@@ -441,8 +470,7 @@ __device__ __forceinline__ void extend_split_body(const ExtendArgs &a, char *sme
     const int kbase = kt * kXT;
     if (kt >= n_tiles || !wave_active || kbase >= kend_w) continue;
     const char *kb = smem + (kt % kXStages) * X::kStage;
-    xtile<KV>(kb, kb + X::kKBytes, kbase, kbase + kXT > wave_min_nvis, nvis, lane, a.scale_log2, qop, oacc,
-              m_run, l_run);
+    xtile<KV>(kb, xop, kbase, kbase + kXT > wave_min_nvis, nvis, lane, a.scale_log2, qop, oacc, m_run, l_run);
   }
 
   // Merge the odd-tile partial (m, l, O) of each column into the even-tile
@@ -651,6 +679,7 @@ __global__ __launch_bounds__(512, 1) void k_extend_wide(const ExtendArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[md][r] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
+  const XOperands<KV> xop(lane);
   bf16x8_t qop[8];
 
   // Q: row cc (256 bytes) holds column cc's 16-byte chunk c in slot
@@ -707,8 +736,7 @@ __global__ __launch_bounds__(512, 1) void k_extend_wide(const ExtendArgs a) {
       const int kbase = tt * kXT;
       if (tt >= t_end || !wave_active || kbase >= kend_w) continue;
       const char *kb = smem + stage(tt) * X::kStage;
-      xtile<KV>(kb, kb + X::kKBytes, kbase, kbase + kXT > wave_min_nvis, nvis, lane, a.scale_log2, qop, oacc,
-                m_run, l_run);
+      xtile<KV>(kb, xop, kbase, kbase + kXT > wave_min_nvis, nvis, lane, a.scale_log2, qop, oacc, m_run, l_run);
     }
   }
 
