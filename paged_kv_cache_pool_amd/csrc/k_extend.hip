@@ -301,7 +301,8 @@ __device__ __forceinline__ void extend_split_body(const ExtendArgs &a, char *sme
   const int wave = uniform(tid >> 6);
   const int g = a.g;
   const int hsel = lane >> 5;                    // which 8-element k group the lane feeds
-  int kvh, col0, ncols, kspan, kc = 0, hist = 0, tok0 = 0;
+  int kvh, col0, ncols, kspan, kc = 0, hist = 0, tok0 = 0, cnew = 0;
+  bool wself = false;                            // the item writes its request's new K/V rows
   const int32_t *btrow;
   if constexpr (PREFIX) {
     const PrefixItem it = a.pitems[blockIdx.x];
@@ -315,6 +316,8 @@ __device__ __forceinline__ void extend_split_body(const ExtendArgs &a, char *sme
   } else {
     const ExtendItem item = a.items[blockIdx.x];
     const int req = uniform(item.req), c = uniform(item.c), L = uniform(item.L);
+    wself = uniform(item.wnew) != 0 && a.knew != nullptr;
+    cnew = c;
     kvh = uniform(item.kvh);
     tok0 = uniform(item.tok0);
     col0 = uniform(item.col0);
@@ -418,6 +421,38 @@ __device__ __forceinline__ void extend_split_body(const ExtendArgs &a, char *sme
     issue(2 * p);
     if (2 * p + 1 < n_tiles) issue(2 * p + 1);
   };
+  // KV update of an item that is the only reader of its request's new rows
+  // (one key-split item per kv head): it writes them into the pool itself,
+  // with the scatter's encoder, before any tile that holds them is copied.
+  if constexpr (!PREFIX) {
+    if (wself) {
+      constexpr int PB = KvTraits<KV>::bytes, E = 16 / PB, NCH = kXD / E;
+      for (int w = tid; w < cnew * NCH; w += 512) {
+        const int t = w / NCH, ch = w - t * NCH;
+        const int pos = hist + t;
+        const int blk = btrow[pos / kBlock];
+        const int off = pos % kBlock;
+        if (ch == 0 && kvh == 0 && a.slots_out) a.slots_out[tok0 + t] = (int64_t)blk * kBlock + off;
+        if (blk < 0 || blk >= a.num_blocks) continue;   // slot outside the pool: not written
+        const int64_t th = (int64_t)(tok0 + t) * a.num_kv_heads + kvh;
+        const KvChunkIn<KV_BF16, KV> in =
+            load_kv_chunk<KV_BF16, KV>((const char *)a.knew + th * kXD * 2, (const char *)a.vnew + th * kXD * 2, ch);
+        const int64_t tile = ((int64_t)blk * a.num_kv_heads + kvh) * X::kTileB;
+        *(uint4 *)((char *)a.k_store + tile + ch * (kBlock * 16) + off * 16) =
+            k_chunk_bits<KV_BF16, KV>(in, a.enc_k_scale);
+        char *vt = (char *)a.v_store + tile;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const uint32_t b = v_elem_bits<KV_BF16, KV>(in, e, a.enc_v_scale);
+          char *pv = vt + ((ch * E + e) * kBlock + off) * PB;
+          if constexpr (PB == 2) *(uint16_t *)pv = (uint16_t)b;
+          else *(uint8_t *)pv = (uint8_t)b;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0);             // every store of this wave has completed
+      __syncthreads();
+    }
+  }
   // Q of the workgroup's 128 columns is copied into the last 32 KB of LDS
   // (for bf16 pools stage 3, not refilled before pair 1 is issued) together
   // with pair 0: row cc (256 bytes) holds column cc's

@@ -416,7 +416,10 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
     // decode unit that holds its last key; every other new token is written
     // by the scatter pass that runs before the attention kernels
     const bool own_write = kv_update && c == 1 && !(ext_ok && c >= ext_min);
-    if (kv_update && !own_write)
+    // a request of one key-split extend item per kv head: the item writes
+    // the request's new rows itself (no other item reads them)
+    const bool ext_self = kv_update && ext_ok && c >= ext_min && (int64_t)c * g <= kExtCols;
+    if (kv_update && !own_write && !ext_self)
       for (int32_t pos = L[i] - c; pos < L[i];) {
         const int32_t end = std::min(L[i], (pos / kBlock + 1) * kBlock);
         plan.wseg.push_back(WriteSeg{i, q[i] + pos - (L[i] - c), pos, end - pos});
@@ -523,8 +526,9 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
     int32_t np = force ? std::max(1, atoi(force)) : 1;
     auto push = [&](int32_t i, int32_t c0, int32_t mode, int32_t k0, int32_t k1, int32_t slot0, int32_t stride) {
       const int32_t c = q[i + 1] - q[i];
+      const int32_t wnew = kv_update && (int64_t)c * g <= kExtCols ? 1 : 0;
       for (int kvh = 0; kvh < Hkv; ++kvh)
-        plan.extw.push_back(ExtendItem{i, kvh, q[i], c, L[i], c0, k0, k1, slot0, stride, mode, 0});
+        plan.extw.push_back(ExtendItem{i, kvh, q[i], c, L[i], c0, k0, k1, slot0, stride, mode, wnew});
     };
     for (const Blk &b0 : fixed_split) push(b0.req, b0.c0, 1, 0, L[b0.req], -1, 0);
     // forced key pieces: per request, np pieces (no more than the shortest block's tiles)
@@ -859,6 +863,15 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
     x.scale_log2 = softmax_scale * log2e * kscale;
     x.k_scale = kscale;
     x.v_scale = vscale;
+    if (kvu) {
+      x.knew = kvu->key;
+      x.vnew = kvu->value;
+      x.slots_out = kvu->slot_mapping;
+      x.k_store = pool->k_cache;
+      x.v_store = pool->v_cache;
+      x.enc_k_scale = kscale;
+      x.enc_v_scale = vscale;
+    }
     e = launch_extend_wide(*pool, x, xs);
     if (e != hipSuccess) return hip_fail(e, "k_extend_wide launch");
   }

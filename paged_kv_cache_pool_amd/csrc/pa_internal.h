@@ -88,7 +88,8 @@ struct ExtendItem {
   int32_t slot0;
   int32_t slot_stride;
   int32_t mode;           // wide kernel: 0 = wide item, 1 = key-split item (kExtCols columns)
-  int32_t pad;
+  int32_t wnew;           // key-split items, attention with the KV update: 1 when this item
+                          // writes its request's new K/V rows of kv head kvh itself
 };
 
 // One workgroup of the shared-prefix (cascade) pass: columns [col0, col0 +
@@ -168,6 +169,14 @@ struct ExtendArgs {
   float scale_log2;
   float k_scale;
   float v_scale;
+  // KV update by items with wnew (null knew: none in this launch)
+  const void *knew;           // [T][Hkv][D] new K rows (bf16)
+  const void *vnew;
+  int64_t *slots_out;         // [T] or null
+  void *k_store;              // the pool arrays, writable
+  void *v_store;
+  float enc_k_scale;          // pool scales for the fp8 encode, 1 otherwise
+  float enc_v_scale;
 };
 
 constexpr int kExtCols = 128;        // columns per extend workgroup (4 x 32, keys split over 2 waves)
