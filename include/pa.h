@@ -86,11 +86,16 @@ typedef enum pa_status {
   PA_ERR_CAPACITY = 6      /* the block pool has too few free blocks               */
 } pa_status;
 
-typedef enum pa_dtype {
+/* Element types.  pa_dtype is a plain 32-bit integer (not an enum type), so
+ * that every value a caller passes is well defined on both sides of the
+ * ABI; the calls reject values other than these constants with
+ * PA_ERR_INVALID_ARG or PA_ERR_UNSUPPORTED. */
+enum {
   PA_F32 = 0,       /* IEEE binary32                                          */
   PA_BF16 = 1,      /* bfloat16                                               */
   PA_FP8_E4M3 = 2   /* OCP FP8 E4M3FN (bias 7, max 448, no inf), pool only    */
-} pa_dtype;
+};
+typedef int32_t pa_dtype;
 
 /* A KV pool ([P1] §6.2: key_cache / value_cache, one per K and V).
  * Supported: block_size 16; head_dim 64 or 128; kv_dtype F32, BF16 or

@@ -195,3 +195,40 @@ def test_empty_calls_are_no_ops(B):
     assert B.lib.pa_write_kv(C.byref(p), None, None, 1, None, 0, None) == 0
     b, keep = _batch(B, [0], [])
     assert _att(B, p, b) == 0
+
+
+def test_planner_random_batches(B, monkeypatch):
+    """The host planner on random ragged batches (runs on the CPU through the
+    workspace size query): decode rows, short and long prefill chunks with
+    history, GQA ratios 1..8, a shared-prefix hint, with and without forced
+    key pieces or the wide layout disabled.  Sizes are positive multiples of
+    256, forced key pieces only add partial slots, and the query is
+    deterministic."""
+    rng = np.random.default_rng(123)
+    for it in range(200):
+        hkv = int(rng.choice([1, 2, 8]))
+        g = int(rng.choice([1, 2, 4, 8]))
+        n = int(rng.integers(1, 12))
+        c = np.where(rng.random(n) < 0.5, 1, rng.integers(2, 700, n)).astype(np.int32)
+        if rng.random() < 0.3:
+            c[0] = int(rng.integers(1000, 5000))
+        hist = rng.integers(0, 3000, n).astype(np.int32)
+        sl = (hist + c).astype(np.int32)
+        qsl = np.concatenate([[0], np.cumsum(c)]).astype(np.int32)
+        stride = int(-(-sl.max() // 16))
+        p = _pool(B, kv="bf16", D=128, H=hkv, nb=stride * n + 64)
+        hint = int(rng.integers(0, 4)) if rng.random() < 0.3 else 0
+        b = B.PaBatch(n, int(qsl[-1]), 0x3000, 0x4000, 0x5000, stride, qsl.ctypes.data, sl.ctypes.data, hint)
+        hq = hkv * g
+        monkeypatch.delenv("PA_WIDE_PIECES", raising=False)
+        monkeypatch.delenv("PA_DISABLE_WIDE", raising=False)
+        n0 = B.lib.pa_attention_workspace_bytes(C.byref(p), C.byref(b), hq)
+        assert n0 > 0 and n0 % 256 == 0, (it, n0)
+        assert B.lib.pa_attention_workspace_bytes(C.byref(p), C.byref(b), hq) == n0
+        monkeypatch.setenv("PA_WIDE_PIECES", "3")
+        n3 = B.lib.pa_attention_workspace_bytes(C.byref(p), C.byref(b), hq)
+        assert n3 >= n0 and n3 % 256 == 0, (it, n0, n3)
+        monkeypatch.delenv("PA_WIDE_PIECES")
+        monkeypatch.setenv("PA_DISABLE_WIDE", "1")
+        nd = B.lib.pa_attention_workspace_bytes(C.byref(p), C.byref(b), hq)
+        assert nd > 0 and nd % 256 == 0, (it, nd)
