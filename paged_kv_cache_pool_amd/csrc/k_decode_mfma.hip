@@ -92,8 +92,10 @@ __device__ __forceinline__ float sum_x32(float x) {
 
 }  // namespace
 
+constexpr int kDecodeWaves = 1;                // waves (work units) per workgroup
+
 template <int KV, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_decode_mfma(const DecodeArgs a) {
+__global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(2))) void k_decode_mfma(const DecodeArgs a) {
   static_assert(KV == KV_BF16 || KV == KV_FP8, "bf16 and fp8 pools");
   constexpr bool F8 = KV == KV_FP8;
   constexpr int PB = KvTraits<KV>::bytes;
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int r = lane & 15;                       // MFMA column (head) / A-operand row
   const int j = lane >> 4;                       // lane group
   const int wave = uniform(threadIdx.x >> 6);
-  const int unit = blockIdx.x * kWavesPerGroup + wave;
+  const int unit = blockIdx.x * kDecodeWaves + wave;
   if (unit >= a.n_items * a.num_kv_heads) return;
   const int item_idx = unit / a.num_kv_heads;
   const int kvh = unit - item_idx * a.num_kv_heads;
@@ -135,16 +137,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   auto qdim = [&](int c) { return F8 ? 64 * (c >> 1) + 16 * j + 8 * (c & 1) : 32 * c + 8 * j; };
 
   // ---- Q^T operand: column r = head qh0 + r (zero past g) ----
+  // (columns past g are cleared with a mask, not a branch: a branch around
+  // a loaded register makes the compiler wait for each load in turn)
   bf16x8_t qop[NS];
   {
     const uint16_t *qrow =
         (const uint16_t *)a.q + ((int64_t)token * a.num_q_heads + qh0 + (r < g ? r : 0)) * D;
+    uint4 v[NS];
 #pragma unroll
-    for (int c = 0; c < NS; ++c) {
-      uint4 v = *(const uint4 *)(qrow + qdim(c));
-      if (r >= g) v = make_uint4(0, 0, 0, 0);
-      qop[c] = as_bf16x8(v);
-    }
+    for (int c = 0; c < NS; ++c) v[c] = *(const uint4 *)(qrow + qdim(c));
+    const uint32_t qm = r < g ? ~0u : 0u;
+#pragma unroll
+    for (int c = 0; c < NS; ++c) qop[c] = as_bf16x8(make_uint4(v[c].x & qm, v[c].y & qm, v[c].z & qm, v[c].w & qm));
   }
 
   // ---- the new key's inputs ----
@@ -443,13 +447,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 
 hipError_t launch_decode_mfma(const pa_kv_pool &p, const DecodeArgs &a, hipStream_t s) {
   const int units = a.n_items * a.num_kv_heads;
-  const dim3 grid((units + kWavesPerGroup - 1) / kWavesPerGroup);
+  const dim3 grid((units + kDecodeWaves - 1) / kDecodeWaves), block(64 * kDecodeWaves);
   if (p.kv_dtype == PA_BF16) {
-    if (p.head_dim == 128) hipLaunchKernelGGL((k_decode_mfma<KV_BF16, 128>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_decode_mfma<KV_BF16, 64>), grid, dim3(256), 0, s, a);
+    if (p.head_dim == 128) hipLaunchKernelGGL((k_decode_mfma<KV_BF16, 128>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_decode_mfma<KV_BF16, 64>), grid, block, 0, s, a);
   } else {
-    if (p.head_dim == 128) hipLaunchKernelGGL((k_decode_mfma<KV_FP8, 128>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_decode_mfma<KV_FP8, 64>), grid, dim3(256), 0, s, a);
+    if (p.head_dim == 128) hipLaunchKernelGGL((k_decode_mfma<KV_FP8, 128>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_decode_mfma<KV_FP8, 64>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }
