@@ -317,6 +317,7 @@ struct Plan {
   std::vector<WriteSeg> wseg;
   int32_t n_slots = 0;
   int32_t part_len = 0;
+  int32_t kstart = 0;                            // first key of the split-K items (the cascade's prefix end)
   size_t off_dec = 0, off_merge = 0, off_extw = 0, off_pre = 0, off_rtok = 0, off_rslot = 0, off_wseg = 0;
   size_t off_ml = 0, off_o = 0, bytes = 0;
 };
@@ -381,6 +382,7 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
   if (prefix_rows == 0) cascade = false;
   if (!cascade) plan.prefix_req = -1;
   const int32_t kstart = cascade ? P : 0;        // first key of the split-K rows' own work
+  plan.kstart = kstart;
 
   // Partition length of the split-K rows (a unit = one token's keys in one
   // partition, for one kv head: one wave).
@@ -446,6 +448,31 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
     n_kc = (P + kc_len - 1) / kc_len;
   }
 
+  // One token's key segments [bnd[r], bnd[r + 1]) -> decode items, their
+  // partial slots and the token's merge entry (outside the cascade a token of
+  // one segment has none: its item writes the output).  own: the segment
+  // that ends at the row's last key also writes the row's new K/V.
+  auto emit_token = [&](int32_t tok, int32_t i, const int32_t *bnd, int32_t nseg, bool own) {
+    auto wpos = [&](int32_t r) { return own && bnd[r + 1] == L[i] ? L[i] - 1 : -1; };
+    if (cascade) {
+      // slots: the prefix chunks, then the segments of keys [P, nvis)
+      plan.row_token.push_back(tok);
+      plan.row_slot0.push_back(plan.n_slots);
+      plan.merge.push_back(MergeItem{tok, plan.n_slots, n_kc + nseg, 0});
+      for (int32_t r = 0; r < nseg; ++r)
+        plan.dec.push_back(DecodeItem{tok, i, bnd[r], bnd[r + 1], plan.n_slots + n_kc + r, wpos(r), {0, 0}});
+      plan.n_slots += n_kc + nseg;
+    } else if (nseg == 1) {
+      plan.dec.push_back(DecodeItem{tok, i, bnd[0], bnd[1], -1, wpos(0), {0, 0}});
+    } else {
+      plan.merge.push_back(MergeItem{tok, plan.n_slots, nseg, 0});
+      for (int32_t r = 0; r < nseg; ++r)
+        plan.dec.push_back(DecodeItem{tok, i, bnd[r], bnd[r + 1], plan.n_slots + r, wpos(r), {0, 0}});
+      plan.n_slots += nseg;
+    }
+  };
+  std::vector<int32_t> bnd;
+
   for (int32_t i = 0; i < b.num_seqs; ++i) {
     const int32_t c = q[i + 1] - q[i];
     if (c == 0) continue;
@@ -462,12 +489,6 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
         plan.wseg.push_back(WriteSeg{i, q[i] + pos - (L[i] - c), pos, end - pos});
         pos = end;
       }
-    const size_t dec0 = plan.dec.size();
-    auto mark_own_write = [&]() {
-      if (!own_write) return;
-      for (size_t k = dec0; k < plan.dec.size(); ++k)
-        if (plan.dec[k].kv_end == L[i]) plan.dec[k].wpos = L[i] - 1;
-    };
     if (ext_ok && c >= ext_min) {
       ext_reqs.push_back(i);
       continue;
@@ -475,32 +496,13 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
     for (int32_t t = 0; t < c; ++t) {
       const int32_t tok = q[i] + t;
       const int32_t nvis = causal ? (L[i] - c + t + 1) : L[i];
-      if (cascade) {
-        // slots: the prefix chunks, then the partitions of keys [P, nvis)
-        const int32_t nparts = (int32_t)((nvis - P + part - 1) / part);
-        plan.row_token.push_back(tok);
-        plan.row_slot0.push_back(plan.n_slots);
-        plan.merge.push_back(MergeItem{tok, plan.n_slots, n_kc + nparts, 0});
-        for (int32_t r = 0; r < nparts; ++r) {
-          const int32_t b0 = (int32_t)(P + r * part), b1 = (int32_t)std::min<int64_t>(nvis, P + (r + 1) * part);
-          plan.dec.push_back(DecodeItem{tok, i, b0, b1, plan.n_slots + n_kc + r, -1, {0, 0}});
-        }
-        plan.n_slots += n_kc + nparts;
-        continue;
-      }
-      const int32_t nparts = (int32_t)((nvis + part - 1) / part);
-      if (nparts <= 1) {
-        plan.dec.push_back(DecodeItem{tok, i, 0, nvis, -1, -1, {0, 0}});
-        continue;
-      }
-      plan.merge.push_back(MergeItem{tok, plan.n_slots, nparts, 0});
-      for (int32_t r = 0; r < nparts; ++r) {
-        const int32_t b0 = (int32_t)(r * part), b1 = (int32_t)std::min<int64_t>(nvis, (r + 1) * part);
-        plan.dec.push_back(DecodeItem{tok, i, b0, b1, plan.n_slots + r, -1, {0, 0}});
-      }
-      plan.n_slots += nparts;
+      // partitions of `part` keys from kstart
+      bnd.clear();
+      for (int64_t k = kstart; k < nvis; k += part) bnd.push_back((int32_t)k);
+      bnd.push_back(nvis);
+      if (bnd.size() == 1 && !cascade) bnd.insert(bnd.begin(), 0);
+      emit_token(tok, i, bnd.data(), (int32_t)bnd.size() - 1, own_write);
     }
-    mark_own_write();
   }
   // Extend items, all run by one launch of the wide kernel.
   //  * A request with at most kExtCols (token, head) columns per kv head is
@@ -680,6 +682,42 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
   plan.bytes = std::max<size_t>(off, 256);
 }
 
+// Host-side consistency of a plan's split-K work (PA_CHECK_PLAN=1, for
+// tests): every item lies inside its row, and each split-K token's items
+// cover its keys [kstart, visible end) once, in order, with distinct partial
+// slots.  Returns null or what is wrong.
+static const char *check_decode_plan(const Plan &plan, const pa_batch &b, int causal) {
+  const int32_t *q = b.query_start_loc_host, *L = b.seq_lens_host;
+  std::vector<std::vector<const DecodeItem *>> by_tok(b.num_tokens);
+  for (const DecodeItem &d : plan.dec) {
+    if (d.req < 0 || d.req >= b.num_seqs || d.token < 0 || d.token >= b.num_tokens) return "item row out of range";
+    if (d.token < q[d.req] || d.token >= q[d.req + 1]) return "item token outside its request";
+    if (d.kv_begin < 0 || d.kv_begin >= d.kv_end || d.kv_end > L[d.req]) return "item keys outside the row";
+    if (d.part >= plan.n_slots || d.part < -1) return "partial slot out of range";
+    if (d.wpos != -1 && (d.wpos != L[d.req] - 1 || d.kv_end != L[d.req])) return "bad own-write position";
+    by_tok[d.token].push_back(&d);
+  }
+  std::vector<char> used(plan.n_slots, 0);
+  for (int32_t t = 0; t < b.num_tokens; ++t) {
+    auto &v = by_tok[t];
+    if (v.empty()) continue;
+    std::sort(v.begin(), v.end(), [](const DecodeItem *x, const DecodeItem *y) { return x->kv_begin < y->kv_begin; });
+    const int32_t i = v[0]->req, c = q[i + 1] - q[i];
+    const int32_t nvis = causal ? L[i] - c + (t - q[i]) + 1 : L[i];
+    if (v.front()->kv_begin != plan.kstart || v.back()->kv_end != nvis) return "a token's items do not cover its keys";
+    for (size_t k = 0; k < v.size(); ++k) {
+      if (k && v[k]->kv_begin != v[k - 1]->kv_end) return "a token's items overlap or leave a gap";
+      const int32_t pt = v[k]->part;
+      if (pt < 0 && (v.size() > 1 || plan.kstart > 0)) return "a split token's item without a partial slot";
+      if (pt >= 0) {
+        if (used[pt]) return "a partial slot used twice";
+        used[pt] = 1;
+      }
+    }
+  }
+  return nullptr;
+}
+
 static pa_status check_attention_args(const pa_kv_pool *pool, const pa_batch *batch,
                                       pa_dtype q_dtype, int32_t Hq, bool need_ptrs) {
   pa_status st = check_pool(pool, need_ptrs);
@@ -767,6 +805,14 @@ size_t pa_attention_workspace_bytes(const pa_kv_pool *pool, const pa_batch *batc
   build_plan(*pool, *batch, num_q_heads, qd, 1, true, plan);
   Plan plan_nc;
   build_plan(*pool, *batch, num_q_heads, qd, 0, true, plan_nc);
+  if (env_flag("PA_CHECK_PLAN")) {
+    const char *why = check_decode_plan(plan, *batch, 1);
+    if (!why) why = check_decode_plan(plan_nc, *batch, 0);
+    if (why) {
+      fail(PA_ERR_VALIDATION, "plan check: %s", why);
+      return 0;
+    }
+  }
   return std::max(plan.bytes, plan_nc.bytes);
 }
 

@@ -203,7 +203,8 @@ def test_planner_random_batches(B, monkeypatch):
     history, GQA ratios 1..8, a shared-prefix hint, with and without forced
     key pieces or the wide layout disabled.  Sizes are positive multiples of
     256, forced key pieces only add partial slots, and the query is
-    deterministic."""
+    deterministic.  The split-K work passes the planner's consistency check
+    (PA_CHECK_PLAN) with the default and with forced partition lengths."""
     rng = np.random.default_rng(123)
     for it in range(200):
         hkv = int(rng.choice([1, 2, 8]))
@@ -232,3 +233,16 @@ def test_planner_random_batches(B, monkeypatch):
         monkeypatch.setenv("PA_DISABLE_WIDE", "1")
         nd = B.lib.pa_attention_workspace_bytes(C.byref(p), C.byref(b), hq)
         assert nd > 0 and nd % 256 == 0, (it, nd)
+        monkeypatch.delenv("PA_DISABLE_WIDE")
+        # the split-K work, default and forced 64- and 192-key partitions,
+        # through the planner's own consistency check
+        monkeypatch.setenv("PA_CHECK_PLAN", "1")
+        for part in [None, "64", "192"]:
+            if part is None:
+                monkeypatch.delenv("PA_PARTITION_KEYS", raising=False)
+            else:
+                monkeypatch.setenv("PA_PARTITION_KEYS", part)
+            nl = B.lib.pa_attention_workspace_bytes(C.byref(p), C.byref(b), hq)
+            assert nl > 0, (it, part, B.lib.pa_last_error().decode())
+        monkeypatch.delenv("PA_CHECK_PLAN")
+        monkeypatch.delenv("PA_PARTITION_KEYS", raising=False)
