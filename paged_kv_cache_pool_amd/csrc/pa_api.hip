@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -436,6 +437,104 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
   if (const char *v = getenv("PA_PARTITION_KEYS")) part = std::max(64, atoi(v) / 64 * 64);
   plan.part_len = (int32_t)part;
 
+  // Paired layout (bf16 and fp8 pools: the matrix-core kernel, two waves per
+  // SIMD).  Measured on MI355X: with 8 one-wave workgroups per compute unit,
+  // workgroups u and u + 4 * CUs land on the same SIMD, and the older wave
+  // takes nearly all of the SIMD's memory issue until it ends, so a SIMD
+  // runs its two units one after the other and ends at a time set by their
+  // sum.  So the split-K tokens' 64-key steps, in token order, are packed
+  // into n_bins = 4 * CUs / Hkv bins of at most T steps and at most two
+  // pieces (a bin ends after its second piece), with the smallest T that
+  // fits.  Bins are numbered two-piece bins first; bin b's first piece is
+  // item b and its second item n_bins + b, so there are no gaps (two-piece
+  // bins are split in two while fewer than n_bins bins are used, so that the
+  // second pieces start at n_bins).  Tokens of several pieces get partials
+  // and a merge.  Used when T is at least 8 steps (shorter units are bound by
+  // their start-up, not by the pairing).  PA_DECODE_PAIRS=0: the partition
+  // form above.
+  int64_t n_bins = 0, pair_T = 0;
+  std::vector<int32_t> tok_steps;
+  auto bins_for = [&](int64_t T, std::vector<std::array<int32_t, 4>> *pieces) {
+    // greedy packing; pieces: (bin, slot, first step, end step) in token order
+    int64_t bins = 0, load = T, np = 2;
+    for (size_t x = 0; x < tok_steps.size(); ++x)
+      for (int64_t o = 0, st = tok_steps[x]; o < st;) {
+        if (np == 2 || load == T) {
+          ++bins;
+          load = 0;
+          np = 0;
+        }
+        const int64_t take = std::min(st - o, T - load);
+        if (pieces) pieces->push_back({(int32_t)(bins - 1), (int32_t)np, (int32_t)o, (int32_t)(o + take)});
+        o += take;
+        load += take;
+        ++np;
+      }
+    return bins;
+  };
+  {
+    const char *penv = getenv("PA_DECODE_PAIRS");
+    const bool want = p.kv_dtype != PA_F32 && !(penv && atoi(penv) <= 0);
+    if (want && (4 * cus) % Hkv == 0 && !tok_keys.empty()) {
+      int64_t S = 0, smax = 0;
+      for (int32_t k : tok_keys) {
+        const int64_t st = (k + kKeysPerIter - 1) / kKeysPerIter;
+        tok_steps.push_back((int32_t)st);
+        S += st;
+        smax = std::max(smax, st);
+      }
+      n_bins = 4 * cus / Hkv;
+      int64_t lo = std::max<int64_t>(1, (S + n_bins - 1) / n_bins), hi = std::max(lo, smax);
+      if (S > 0 && bins_for(hi, nullptr) <= n_bins) {
+        while (lo < hi) {                        // hi stays feasible
+          const int64_t mid = (lo + hi) / 2;
+          if (bins_for(mid, nullptr) <= n_bins) hi = mid;
+          else lo = mid + 1;
+        }
+        if (hi >= 8 || (penv && atoi(penv) > 0)) pair_T = hi;
+      } else {
+        n_bins = 0;
+      }
+    }
+  }
+  const bool paired = pair_T > 0;
+  std::vector<std::array<int32_t, 4>> pieces;
+  if (paired) {
+    const int64_t m = bins_for(pair_T, &pieces);
+    std::vector<int32_t> cnt(m, 0);
+    for (const auto &pc : pieces) ++cnt[pc[0]];
+    // split two-piece bins while bins are short of n_bins
+    int64_t extra = n_bins - m;
+    std::vector<char> split(m, 0);
+    for (int64_t b0 = 0; b0 < m && extra > 0; ++b0)
+      if (cnt[b0] == 2) {
+        split[b0] = 1;
+        --extra;
+      }
+    // final numbering: unsplit two-piece bins, then single pieces
+    std::vector<int32_t> id0(m, -1);
+    int32_t nid = 0;
+    for (int64_t b0 = 0; b0 < m; ++b0)
+      if (cnt[b0] == 2 && !split[b0]) id0[b0] = nid++;
+    std::vector<int32_t> id1(m, -1);          // a split bin's second piece
+    for (int64_t b0 = 0; b0 < m; ++b0) {
+      if (id0[b0] < 0) id0[b0] = nid++;
+      if (split[b0]) id1[b0] = nid++;
+    }
+    const int32_t nb = nid;                   // n_bins, or fewer when every bin holds one piece
+    for (auto &pc : pieces) {
+      const int32_t b0 = pc[0];
+      int64_t pos;
+      if (pc[1] == 0) pos = id0[b0];
+      else if (split[b0]) pos = id1[b0];
+      else pos = (int64_t)nb + id0[b0];
+      pc[0] = (int32_t)pos;                   // item position
+      pc[1] = 0;
+    }
+  }
+  std::vector<int64_t> dec_pos;                  // paired: position of each item
+  size_t piece_next = 0;
+
   // prefix chunks: about one workgroup per compute unit over kv heads x
   // column blocks x chunks (a workgroup costs several microseconds to start
   // and finish, so one round of longer chunks beats two of shorter ones)
@@ -496,10 +595,23 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
     for (int32_t t = 0; t < c; ++t) {
       const int32_t tok = q[i] + t;
       const int32_t nvis = causal ? (L[i] - c + t + 1) : L[i];
-      // partitions of `part` keys from kstart
       bnd.clear();
-      for (int64_t k = kstart; k < nvis; k += part) bnd.push_back((int32_t)k);
-      bnd.push_back(nvis);
+      if (paired) {
+        // this token's pieces (the packing visited the tokens in this
+        // order, with the same step counts)
+        const int64_t st = std::max<int64_t>(0, (int64_t)nvis - kstart + kKeysPerIter - 1) / kKeysPerIter;
+        bnd.push_back(std::min(nvis, kstart));
+        for (int64_t o = 0; o < st && piece_next < pieces.size();) {
+          const auto &pc = pieces[piece_next++];
+          o = pc[3];
+          bnd.push_back((int32_t)std::min<int64_t>(nvis, kstart + (int64_t)kKeysPerIter * o));
+          dec_pos.push_back(pc[0]);
+        }
+      } else {
+        // partitions of `part` keys from kstart
+        for (int64_t k = kstart; k < nvis; k += part) bnd.push_back((int32_t)k);
+        bnd.push_back(nvis);
+      }
       if (bnd.size() == 1 && !cascade) bnd.insert(bnd.begin(), 0);
       emit_token(tok, i, bnd.data(), (int32_t)bnd.size() - 1, own_write);
     }
@@ -627,7 +739,12 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
   // earlier ones finish, so starting the long units first leaves short ones
   // for the tail (longest-processing-time-first list scheduling).  A stable
   // counting sort on the number of 64-key steps keeps this O(n).
-  if (plan.dec.size() > 1) {
+  if (paired) {
+    // items to their bin positions (a permutation: no gaps)
+    std::vector<DecodeItem> arr(plan.dec.size());
+    for (size_t k = 0; k < plan.dec.size(); ++k) arr[(size_t)dec_pos[k]] = plan.dec[k];
+    plan.dec.swap(arr);
+  } else if (plan.dec.size() > 1) {
     auto steps = [](const DecodeItem &d) { return (d.kv_end - d.kv_begin + kKeysPerIter - 1) / kKeysPerIter; };
     int32_t max_steps = 0;
     for (const DecodeItem &d : plan.dec) max_steps = std::max(max_steps, steps(d));

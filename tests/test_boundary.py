@@ -204,7 +204,8 @@ def test_planner_random_batches(B, monkeypatch):
     key pieces or the wide layout disabled.  Sizes are positive multiples of
     256, forced key pieces only add partial slots, and the query is
     deterministic.  The split-K work passes the planner's consistency check
-    (PA_CHECK_PLAN) with the default and with forced partition lengths."""
+    (PA_CHECK_PLAN) in the paired layout (the default) and in the partition
+    form with the default and forced partition lengths."""
     rng = np.random.default_rng(123)
     for it in range(200):
         hkv = int(rng.choice([1, 2, 8]))
@@ -237,12 +238,14 @@ def test_planner_random_batches(B, monkeypatch):
         # the split-K work, default and forced 64- and 192-key partitions,
         # through the planner's own consistency check
         monkeypatch.setenv("PA_CHECK_PLAN", "1")
-        for part in [None, "64", "192"]:
-            if part is None:
-                monkeypatch.delenv("PA_PARTITION_KEYS", raising=False)
-            else:
-                monkeypatch.setenv("PA_PARTITION_KEYS", part)
+        for pairs, part in [(None, None), ("0", None), ("0", "64"), ("0", "192")]:
+            for k, v in [("PA_DECODE_PAIRS", pairs), ("PA_PARTITION_KEYS", part)]:
+                if v is None:
+                    monkeypatch.delenv(k, raising=False)
+                else:
+                    monkeypatch.setenv(k, v)
             nl = B.lib.pa_attention_workspace_bytes(C.byref(p), C.byref(b), hq)
-            assert nl > 0, (it, part, B.lib.pa_last_error().decode())
+            assert nl > 0, (it, pairs, part, B.lib.pa_last_error().decode())
         monkeypatch.delenv("PA_CHECK_PLAN")
         monkeypatch.delenv("PA_PARTITION_KEYS", raising=False)
+        monkeypatch.delenv("PA_DECODE_PAIRS", raising=False)

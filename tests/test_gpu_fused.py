@@ -141,18 +141,21 @@ def test_fused_equals_separate_random(R, seed):
     _check_out(w, sep)
 
 
+@pytest.mark.parametrize("pairs", ["0", "1"])
 @pytest.mark.parametrize("min_rows", ["16", "2"])
 @pytest.mark.parametrize("kv", [W.BF16, W.FP8])
-def test_fused_decode_partitions_and_verify_rows(R, monkeypatch, kv, min_rows):
-    """Decode rows split into 64-key partitions (the newest key is written by
-    the last partition's unit, which may hold that key alone), next to
+def test_fused_decode_partitions_and_verify_rows(R, monkeypatch, kv, min_rows, pairs):
+    """Decode rows split into 64-key partitions or into the paired layout's
+    pieces (the newest key is written by the row's last item, which may hold
+    that key alone), next to
     speculative-verify-sized chunks of 2 to 8 rows and one prefill chunk.  The
     chunks' K/V are written by the scatter pass before the attention kernels
     read them; the verify chunks run on the split-K kernel (threshold 16) or on
     the MFMA extend kernel (threshold 2, the default)."""
     monkeypatch.setenv("PA_PARTITION_KEYS", "64")
+    monkeypatch.setenv("PA_DECODE_PAIRS", pairs)
     monkeypatch.setenv("PA_EXTEND_MIN_ROWS", min_rows)
-    say("fused partitions + verify rows", kv, "extend threshold", min_rows)
+    say("fused partitions + verify rows", kv, "extend threshold", min_rows, "pairs", pairs)
     nc = [64, 0, 127, 128, 300, 5, 64, 200, 40]
     ns = [1, 1, 1, 1, 1, 4, 8, 2, 24]
     w = W.build(f"fused_parts_{kv}", 7, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
@@ -164,11 +167,14 @@ def test_fused_decode_partitions_and_verify_rows(R, monkeypatch, kv, min_rows):
     _check_out(w, fused)
 
 
+@pytest.mark.parametrize("pairs", ["0", "1"])
 @pytest.mark.parametrize("kv", [W.BF16, W.FP8])
-def test_fused_cascade(R, kv):
+def test_fused_cascade(R, monkeypatch, kv, pairs):
     """The shared-prefix pass with the KV update: the decode rows' own keys
-    (written inside the split-K kernel) follow the prefix."""
-    say("fused cascade", kv)
+    (written inside the split-K kernel) follow the prefix; partition form or
+    paired layout."""
+    monkeypatch.setenv("PA_DECODE_PAIRS", pairs)
+    say("fused cascade", kv, "pairs", pairs)
     own = [0, 1, 17, 33, 60, 9, 5]
     w = W.build(f"fused_casc_{kv}", 11, num_q_heads=8, num_kv_heads=2, head_dim=128,
                 block_size=16, num_blocks=80, kv_dtype=kv, io_dtype=W.BF16,

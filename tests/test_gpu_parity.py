@@ -203,10 +203,14 @@ def test_attention_random_small(R, seed):
     _check_attention(w, step)
 
 
-def test_attention_long_and_split(R, monkeypatch):
-    """Several partitions per row (forced short partitions) and long rows."""
+@pytest.mark.parametrize("pairs", ["0", "1"])
+def test_attention_long_and_split(R, monkeypatch, pairs):
+    """Several partials per row and long rows: forced 64-key partitions
+    (pairs "0"), or the paired layout, whose bins (512 for 2 kv heads) cut
+    these rows into pieces of a step or two."""
     monkeypatch.setenv("PA_PARTITION_KEYS", "64")
-    say("attention forced 64-key partitions")
+    monkeypatch.setenv("PA_DECODE_PAIRS", pairs)
+    say("attention split, pairs", pairs)
     w = W.llama8b_decode(seed=3, num_seqs=6, lo=1, hi=700, num_blocks=400)
     step = R.GpuStep(w)
     step.run()
