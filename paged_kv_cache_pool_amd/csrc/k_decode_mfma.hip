@@ -35,6 +35,11 @@
 // have consumed V, so a wave always has one step's K or V in flight while it
 // computes.  Block ids are read two steps ahead.
 //
+// Pairs (PAIR): one wave per SIMD runs two items (token pieces) in turn; the
+// second item's first K/V are read into spare registers at the start, so it
+// begins without a wait.  The kernel then holds up to 512 registers (one
+// wave per SIMD); the single-item form keeps two waves per SIMD.
+//
 // KV update (items with wpos >= 0, the row's own new token at position
 // kv_end - 1): the new key enters the softmax first, with the value the pool
 // will hold (the scatter's own encoding), and its K/V rows are stored into
@@ -94,8 +99,8 @@ __device__ __forceinline__ float sum_x32(float x) {
 
 constexpr int kDecodeWaves = 1;                // waves (work units) per workgroup
 
-template <int KV, int D>
-__global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(2))) void k_decode_mfma(const DecodeArgs a) {
+template <int KV, int D, bool PAIR>
+__global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(PAIR ? 1 : 2))) void k_decode_mfma(const DecodeArgs a) {
   static_assert(KV == KV_BF16 || KV == KV_FP8, "bf16 and fp8 pools");
   constexpr bool F8 = KV == KV_FP8;
   constexpr int PB = KvTraits<KV>::bytes;
@@ -113,20 +118,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   const int j = lane >> 4;                       // lane group
   const int wave = uniform(threadIdx.x >> 6);
   const int unit = blockIdx.x * kDecodeWaves + wave;
-  if (unit >= a.n_items * a.num_kv_heads) return;
-  const int item_idx = unit / a.num_kv_heads;
-  const int kvh = unit - item_idx * a.num_kv_heads;
-  const DecodeItem item = a.items[item_idx];
-  const int token = uniform(item.token), req = uniform(item.req);
-  const int kv_begin = uniform(item.kv_begin), kv_end = uniform(item.kv_end);
-  const int part = uniform(item.part);
-  const int wpos = uniform(item.wpos);
+  // PAIR: wave (bin, kv head) runs item bin, then item pair_stride + bin when
+  // there is one (its first step's K/V read at the start, so the second
+  // item starts without waiting).  Otherwise one item per wave.
+  const int n_first = PAIR ? a.pair_stride : a.n_items;
+  if (unit >= n_first * a.num_kv_heads) return;
+  const int bin = unit / a.num_kv_heads;
+  const int kvh = unit - bin * a.num_kv_heads;
   const int g = a.g;
   const int qh0 = kvh * a.g_total + a.h0;        // head of column 0
-  const bool wnew = wpos >= 0 && a.knew != nullptr;
-  const int kv_last = wnew ? kv_end - 1 : kv_end;   // end of the keys read from the pool
-
-  const int32_t *__restrict__ btrow = a.block_table + (int64_t)req * a.bt_stride;
   const char *__restrict__ kbase = (const char *)a.k_cache + (int64_t)kvh * TILE;
   const char *__restrict__ vbase = (const char *)a.v_cache + (int64_t)kvh * TILE;
   const int64_t bstride = (int64_t)a.num_kv_heads * TILE;   // bytes between blocks
@@ -135,50 +135,6 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   // layout decides it: bf16 reads one 8-dim chunk row per slice, fp8 one
   // 16-dim chunk row per two slices)
   auto qdim = [&](int c) { return F8 ? 64 * (c >> 1) + 16 * j + 8 * (c & 1) : 32 * c + 8 * j; };
-
-  // ---- Q^T operand: column r = head qh0 + r (zero past g) ----
-  // (columns past g are cleared with a mask, not a branch: a branch around
-  // a loaded register makes the compiler wait for each load in turn)
-  bf16x8_t qop[NS];
-  {
-    const uint16_t *qrow =
-        (const uint16_t *)a.q + ((int64_t)token * a.num_q_heads + qh0 + (r < g ? r : 0)) * D;
-    uint4 v[NS];
-#pragma unroll
-    for (int c = 0; c < NS; ++c) v[c] = *(const uint4 *)(qrow + qdim(c));
-    const uint32_t qm = r < g ? ~0u : 0u;
-#pragma unroll
-    for (int c = 0; c < NS; ++c) qop[c] = as_bf16x8(make_uint4(v[c].x & qm, v[c].y & qm, v[c].z & qm, v[c].w & qm));
-  }
-
-  // ---- the new key's inputs ----
-  uint4 kin[NS];
-  uint2 vin[NDG];
-  int wblk = -1;
-  if (wnew) {
-    const int64_t th = (int64_t)token * a.num_kv_heads + kvh;
-    const uint16_t *krow = (const uint16_t *)a.knew + th * D;
-    const uint16_t *vrow = (const uint16_t *)a.vnew + th * D;
-#pragma unroll
-    for (int c = 0; c < NS; ++c) kin[c] = *(const uint4 *)(krow + qdim(c));
-#pragma unroll
-    for (int dg = 0; dg < NDG; ++dg) vin[dg] = *(const uint2 *)(vrow + dg * 16 + 4 * j);
-    wblk = uniform(btrow[wpos / kBlock]);
-  }
-
-  // ---- block ids: lane group j reads block j of a step ----
-  // (the read itself is unconditional, at an index clamped to the row's last
-  // block, so that no branch sits between the step's loads)
-  const int last_bi = kv_last > 0 ? (kv_last - 1) >> 4 : 0;
-  auto ids_of = [&](int itx) {
-    const int bi = (itx >> 4) + j;
-    const int id = btrow[bi < last_bi ? bi : last_bi];
-    return bi <= last_bi ? id : -1;
-  };
-  auto blk = [&](int idv, int t) {
-    const int p = __builtin_amdgcn_readlane(idv, 16 * t);
-    return p < a.num_blocks ? p : -1;            // ids outside the pool: never dereferenced
-  };
 
   // lane-constant parts of the addresses
   const int kofs = j * (kBlock * 16) + (8 * ((r >> 2) & 1) + (r & 3)) * 16;   // + 64 h + 1024 x
@@ -189,7 +145,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   VReg vr[2][NDG];                               // [chunk c][dim group]
   // block of pair c that a lane reads (b0 .. b3: the step's four block ids)
   auto pick = [](int sel, int lo, int hi) { return sel ? hi : lo; };
-  auto issue_k = [&](int b0, int b1, int b2, int b3) {
+  auto issue_k = [&](uint4 (&kd)[4][NKX], int b0, int b1, int b2, int b3) {
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
       const int p = c2 == 0 ? pick(ksel, b0, b1) : pick(ksel, b2, b3);
@@ -198,262 +154,366 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int x = 0; x < NKX; ++x)
-          kr[2 * c2 + h][x] = F8 ? *(const uint4 *)(kp + 64 * h + 1024 * x) : load_stream(kp + 64 * h + 1024 * x);
+          kd[2 * c2 + h][x] = F8 ? *(const uint4 *)(kp + 64 * h + 1024 * x) : load_stream(kp + 64 * h + 1024 * x);
     }
   };
-  auto issue_v = [&](int b0, int b1, int b2, int b3) {
+  auto issue_v = [&](VReg (&vd)[2][NDG], int b0, int b1, int b2, int b3) {
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
       const int p = c2 == 0 ? pick(vsel, b0, b1) : pick(vsel, b2, b3);
       const char *vp = vbase + (int64_t)(p < 0 ? 0 : p) * bstride + vofs;
 #pragma unroll
       for (int dg = 0; dg < NDG; ++dg) {
-        if constexpr (F8) vr[c2][dg] = *(const VReg *)(vp + 16 * VROW * dg);
-        else vr[c2][dg] = load_stream(vp + 16 * VROW * dg);
+        if constexpr (F8) vd[c2][dg] = *(const VReg *)(vp + 16 * VROW * dg);
+        else vd[c2][dg] = load_stream(vp + 16 * VROW * dg);
       }
     }
   };
 
-  float m_run = -INFINITY, l_run = 0.0f;         // head r; l_run: this lane's keys only
-  f32x4_t o[NDG];
-#pragma unroll
-  for (int dg = 0; dg < NDG; ++dg) o[dg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  auto blk = [&](int idv, int t) {
+    const int p = __builtin_amdgcn_readlane(idv, 16 * t);
+    return p < a.num_blocks ? p : -1;            // ids outside the pool: never dereferenced
+  };
 
-  // ---- the new key: first softmax step, then its rows into the pool ----
-  if (wnew && kvh == 0 && lane == 0 && a.slots_out)
-    a.slots_out[token] = (int64_t)wblk * kBlock + wpos % kBlock;
-  if (wnew && wblk >= 0 && wblk < a.num_blocks) {
-    uint32_t kb[NS][8];
-    float sp = 0.0f;
-#pragma unroll
-    for (int c = 0; c < NS; ++c) {
-      const uint32_t w[4] = {kin[c].x, kin[c].y, kin[c].z, kin[c].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t raw = (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-        kb[c][e] = pool_bits<KV_BF16, KV>(raw, a.enc_k_scale);
-        sp = fmaf((float)qop[c][e], pool_value<KV>(kb[c][e]), sp);
-      }
-    }
-    sp = sum_x32(sum_x16(sp));
-    m_run = sp * a.scale_log2;
-    l_run = j == 0 ? 1.0f : 0.0f;
-    uint32_t vb[NDG][4];
-#pragma unroll
-    for (int dg = 0; dg < NDG; ++dg) {
-      const uint32_t w[2] = {vin[dg].x, vin[dg].y};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        vb[dg][i] = pool_bits<KV_BF16, KV>((w[i >> 1] >> (16 * (i & 1))) & 0xffffu, a.enc_v_scale);
-        o[dg][i] = pool_value<KV>(vb[dg][i]);
-      }
-    }
-    // K element d of slot off sits at (d / E) * 256 + off * 16 + (d % E) * PB
-    // of the tile; V element d at (d * 16 + off) * PB
-    const int off = wpos % kBlock;
-    char *kt = (char *)a.k_store + ((int64_t)wblk * a.num_kv_heads + kvh) * TILE;
-    char *vt = (char *)a.v_store + ((int64_t)wblk * a.num_kv_heads + kvh) * TILE;
-#pragma unroll
-    for (int c = 0; c < NS; ++c) {
-      if (r == c) {
-        const int d0 = qdim(c);
-        char *kd = kt + (d0 / E) * (kBlock * 16) + off * 16 + (d0 % E) * PB;
-        if constexpr (F8) {
-          uint2 w;
-          w.x = kb[c][0] | kb[c][1] << 8 | kb[c][2] << 16 | kb[c][3] << 24;
-          w.y = kb[c][4] | kb[c][5] << 8 | kb[c][6] << 16 | kb[c][7] << 24;
-          *(uint2 *)kd = w;
-        } else {
-          uint4 w;
-          w.x = kb[c][0] | kb[c][1] << 16;
-          w.y = kb[c][2] | kb[c][3] << 16;
-          w.z = kb[c][4] | kb[c][5] << 16;
-          w.w = kb[c][6] | kb[c][7] << 16;
-          *(uint4 *)kd = w;
-        }
-      }
-    }
-#pragma unroll
-    for (int dg = 0; dg < NDG; ++dg) {
-      if (r == dg) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          char *vd = vt + ((dg * 16 + 4 * j + i) * kBlock + off) * PB;
-          if constexpr (F8) *(uint8_t *)vd = (uint8_t)vb[dg][i];
-          else *(uint16_t *)vd = (uint16_t)vb[dg][i];
-        }
-      }
-    }
-  }
 
-  // ---- the first step's K/V ----
-  int b0 = -1, b1 = -1, b2 = -1, b3 = -1;
-  int idv_next = -1;
-  if (kv_begin < kv_last) {
-    const int idv = ids_of(kv_begin);
-    b0 = blk(idv, 0), b1 = blk(idv, 1), b2 = blk(idv, 2), b3 = blk(idv, 3);
-    idv_next = ids_of(kv_begin + kKeysPerIter);
-    issue_k(b0, b1, b2, b3);
-    asm volatile("" ::: "memory");              // K before V, as in the loop
-    issue_v(b0, b1, b2, b3);
-    asm volatile("" ::: "memory");
-  }
+  // One item: keys [kv_begin, kv_last) of one token.  pre: its first step's
+  // K/V are already in kr / vr, from the block ids b0 .. b3 (next: idv_next).
+  auto run = [&](const int item_idx, const bool pre, int b0, int b1, int b2, int b3, int idv_next) {
+    const DecodeItem item = a.items[item_idx];
+    const int token = uniform(item.token), req = uniform(item.req);
+    const int kv_begin = uniform(item.kv_begin), kv_end = uniform(item.kv_end);
+    const int part = uniform(item.part);
+    const int wpos = uniform(item.wpos);
+    const bool wnew = wpos >= 0 && a.knew != nullptr;
+    const int kv_last = wnew ? kv_end - 1 : kv_end;   // end of the keys read from the pool
+    const int32_t *__restrict__ btrow = a.block_table + (int64_t)req * a.bt_stride;
+    // ---- Q^T operand: column r = head qh0 + r (zero past g) ----
+    // (columns past g are cleared with a mask, not a branch: a branch around
+    // a loaded register makes the compiler wait for each load in turn)
+    bf16x8_t qop[NS];
+    {
+      const uint16_t *qrow =
+          (const uint16_t *)a.q + ((int64_t)token * a.num_q_heads + qh0 + (r < g ? r : 0)) * D;
+      uint4 v[NS];
+  #pragma unroll
+      for (int c = 0; c < NS; ++c) v[c] = *(const uint4 *)(qrow + qdim(c));
+      const uint32_t qm = r < g ? ~0u : 0u;
+  #pragma unroll
+      for (int c = 0; c < NS; ++c) qop[c] = as_bf16x8(make_uint4(v[c].x & qm, v[c].y & qm, v[c].z & qm, v[c].w & qm));
+    }
 
-  // ---- key loop ----
-  for (int it = kv_begin; it < kv_last; it += kKeysPerIter) {
-    const int idv_next2 = ids_of(it + 2 * kKeysPerIter);
-    const bool slow = it + kKeysPerIter > kv_last || (b0 | b1 | b2 | b3) < 0;
+    // ---- the new key's inputs ----
+    uint4 kin[NS];
+    uint2 vin[NDG];
+    int wblk = -1;
+    if (wnew) {
+      const int64_t th = (int64_t)token * a.num_kv_heads + kvh;
+      const uint16_t *krow = (const uint16_t *)a.knew + th * D;
+      const uint16_t *vrow = (const uint16_t *)a.vnew + th * D;
+  #pragma unroll
+      for (int c = 0; c < NS; ++c) kin[c] = *(const uint4 *)(krow + qdim(c));
+  #pragma unroll
+      for (int dg = 0; dg < NDG; ++dg) vin[dg] = *(const uint2 *)(vrow + dg * 16 + 4 * j);
+      wblk = uniform(btrow[wpos / kBlock]);
+    }
 
-    // S products
-    f32x4_t s[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      s[u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
+    // ---- block ids: lane group j reads block j of a step ----
+    // (the read itself is unconditional, at an index clamped to the row's last
+    // block, so that no branch sits between the step's loads)
+    const int last_bi = kv_last > 0 ? (kv_last - 1) >> 4 : 0;
+    auto ids_of = [&](int itx) {
+      const int bi = (itx >> 4) + j;
+      const int id = btrow[bi < last_bi ? bi : last_bi];
+      return bi <= last_bi ? id : -1;
+    };
+    float m_run = -INFINITY, l_run = 0.0f;         // head r; l_run: this lane's keys only
+    f32x4_t o[NDG];
+  #pragma unroll
+    for (int dg = 0; dg < NDG; ++dg) o[dg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // ---- the new key: first softmax step, then its rows into the pool ----
+    if (wnew && kvh == 0 && lane == 0 && a.slots_out)
+      a.slots_out[token] = (int64_t)wblk * kBlock + wpos % kBlock;
+    if (wnew && wblk >= 0 && wblk < a.num_blocks) {
+      uint32_t kb[NS][8];
+      float sp = 0.0f;
+  #pragma unroll
       for (int c = 0; c < NS; ++c) {
-        bf16x8_t kop;
-        if constexpr (F8) {
-          const uint4 w = kr[u][c >> 1];
-          kop = (c & 1) ? fp8x8_bf16(w.z, w.w) : fp8x8_bf16(w.x, w.y);
-        } else {
-          kop = as_bf16x8(kr[u][c]);
+        const uint32_t w[4] = {kin[c].x, kin[c].y, kin[c].z, kin[c].w};
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t raw = (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+          kb[c][e] = pool_bits<KV_BF16, KV>(raw, a.enc_k_scale);
+          sp = fmaf((float)qop[c][e], pool_value<KV>(kb[c][e]), sp);
         }
-        s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[c], s[u], 0, 0, 0);
       }
-    }
-
-    // the next step's K, into the registers just consumed (after the last
-    // step too, where every id is -1 and block 0 is read: a valid address
-    // already in the caches, and no branch between the loads)
-    const int n0 = blk(idv_next, 0), n1 = blk(idv_next, 1), n2 = blk(idv_next, 2), n3 = blk(idv_next, 3);
-    issue_k(n0, n1, n2, n3);
-
-    // valid keys of this lane: positions it + 32 c + 8 j + e, e < nv[c]
-    int nv[2] = {8, 8};
-    if (slow) {
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        const int p = c2 == 0 ? pick(vsel, b0, b1) : pick(vsel, b2, b3);
-        const int lim = kv_last - (it + 32 * c2 + 8 * j);
-        nv[c2] = p < 0 ? 0 : lim < 0 ? 0 : lim > 8 ? 8 : lim;
+      sp = sum_x32(sum_x16(sp));
+      m_run = sp * a.scale_log2;
+      l_run = j == 0 ? 1.0f : 0.0f;
+      uint32_t vb[NDG][4];
+  #pragma unroll
+      for (int dg = 0; dg < NDG; ++dg) {
+        const uint32_t w[2] = {vin[dg].x, vin[dg].y};
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          vb[dg][i] = pool_bits<KV_BF16, KV>((w[i >> 1] >> (16 * (i & 1))) & 0xffffu, a.enc_v_scale);
+          o[dg][i] = pool_value<KV>(vb[dg][i]);
+        }
       }
-    }
-
-    // online softmax (log2 units); S element i of product 2c + h is key 4h + i of chunk c
-    float sc[4][4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = s[u][i] * a.scale_log2;
-        if (slow && 4 * (u & 1) + i >= nv[u >> 1]) v = -INFINITY;
-        sc[u][i] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = max_x32(max_x16(mx));
-    const float mn = fmaxf(m_run, mx);
-    const float mu = mn == -INFINITY ? 0.0f : mn;   // no key yet: every p and alpha is 0
-    const float alpha = __builtin_amdgcn_exp2f(m_run - mu);
-    float psum = 0.0f;
-    bf16x8_t pop[2];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = __builtin_amdgcn_exp2f(sc[u][i] - mu);
-        psum += p;
-        pop[u >> 1][4 * (u & 1) + i] = (__bf16)p;
-      }
-    l_run = l_run * alpha + psum;
-    m_run = mn;
-#pragma unroll
-    for (int dg = 0; dg < NDG; ++dg) o[dg] *= alpha;
-
-    // PV products (keys past the end or in invalid blocks: V zeroed, since
-    // unwritten slots may hold anything)
-    if (slow) {
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        if constexpr (F8) {
-          const uint64_t m8 = nv[c2] >= 8 ? ~0ull : ((1ull << (8 * nv[c2])) - 1);
-#pragma unroll
-          for (int dg = 0; dg < NDG; ++dg) {
-            vr[c2][dg].x &= (uint32_t)m8;
-            vr[c2][dg].y &= (uint32_t)(m8 >> 32);
+      // K element d of slot off sits at (d / E) * 256 + off * 16 + (d % E) * PB
+      // of the tile; V element d at (d * 16 + off) * PB
+      const int off = wpos % kBlock;
+      char *kt = (char *)a.k_store + ((int64_t)wblk * a.num_kv_heads + kvh) * TILE;
+      char *vt = (char *)a.v_store + ((int64_t)wblk * a.num_kv_heads + kvh) * TILE;
+  #pragma unroll
+      for (int c = 0; c < NS; ++c) {
+        if (r == c) {
+          const int d0 = qdim(c);
+          char *kd = kt + (d0 / E) * (kBlock * 16) + off * 16 + (d0 % E) * PB;
+          if constexpr (F8) {
+            uint2 w;
+            w.x = kb[c][0] | kb[c][1] << 8 | kb[c][2] << 16 | kb[c][3] << 24;
+            w.y = kb[c][4] | kb[c][5] << 8 | kb[c][6] << 16 | kb[c][7] << 24;
+            *(uint2 *)kd = w;
+          } else {
+            uint4 w;
+            w.x = kb[c][0] | kb[c][1] << 16;
+            w.y = kb[c][2] | kb[c][3] << 16;
+            w.z = kb[c][4] | kb[c][5] << 16;
+            w.w = kb[c][6] | kb[c][7] << 16;
+            *(uint4 *)kd = w;
           }
-        } else {
-          uint32_t mw[4];
-#pragma unroll
-          for (int w = 0; w < 4; ++w)
-            mw[w] = (2 * w < nv[c2] ? 0xffffu : 0u) | (2 * w + 1 < nv[c2] ? 0xffff0000u : 0u);
-#pragma unroll
-          for (int dg = 0; dg < NDG; ++dg) {
-            vr[c2][dg].x &= mw[0];
-            vr[c2][dg].y &= mw[1];
-            vr[c2][dg].z &= mw[2];
-            vr[c2][dg].w &= mw[3];
+        }
+      }
+  #pragma unroll
+      for (int dg = 0; dg < NDG; ++dg) {
+        if (r == dg) {
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            char *vd = vt + ((dg * 16 + 4 * j + i) * kBlock + off) * PB;
+            if constexpr (F8) *(uint8_t *)vd = (uint8_t)vb[dg][i];
+            else *(uint16_t *)vd = (uint16_t)vb[dg][i];
           }
         }
       }
     }
+
+    // ---- the first step's K/V ----
+    if (!pre && kv_begin < kv_last) {
+      const int idv = ids_of(kv_begin);
+      b0 = blk(idv, 0), b1 = blk(idv, 1), b2 = blk(idv, 2), b3 = blk(idv, 3);
+      idv_next = ids_of(kv_begin + kKeysPerIter);
+      issue_k(kr, b0, b1, b2, b3);
+      asm volatile("" ::: "memory");              // K before V, as in the loop
+      issue_v(vr, b0, b1, b2, b3);
+      asm volatile("" ::: "memory");
+    }
+
+    // ---- key loop ----
+    for (int it = kv_begin; it < kv_last; it += kKeysPerIter) {
+      const int idv_next2 = ids_of(it + 2 * kKeysPerIter);
+      const bool slow = it + kKeysPerIter > kv_last || (b0 | b1 | b2 | b3) < 0;
+
+      // S products
+      f32x4_t s[4];
+  #pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        s[u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  #pragma unroll
+        for (int c = 0; c < NS; ++c) {
+          bf16x8_t kop;
+          if constexpr (F8) {
+            const uint4 w = kr[u][c >> 1];
+            kop = (c & 1) ? fp8x8_bf16(w.z, w.w) : fp8x8_bf16(w.x, w.y);
+          } else {
+            kop = as_bf16x8(kr[u][c]);
+          }
+          s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[c], s[u], 0, 0, 0);
+        }
+      }
+
+      // the next step's K, into the registers just consumed (after the last
+      // step too, where every id is -1 and block 0 is read: a valid address
+      // already in the caches, and no branch between the loads)
+      const int n0 = blk(idv_next, 0), n1 = blk(idv_next, 1), n2 = blk(idv_next, 2), n3 = blk(idv_next, 3);
+      issue_k(kr, n0, n1, n2, n3);
+
+      // valid keys of this lane: positions it + 32 c + 8 j + e, e < nv[c]
+      int nv[2] = {8, 8};
+      if (slow) {
+  #pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          const int p = c2 == 0 ? pick(vsel, b0, b1) : pick(vsel, b2, b3);
+          const int lim = kv_last - (it + 32 * c2 + 8 * j);
+          nv[c2] = p < 0 ? 0 : lim < 0 ? 0 : lim > 8 ? 8 : lim;
+        }
+      }
+
+      // online softmax (log2 units); S element i of product 2c + h is key 4h + i of chunk c
+      float sc[4][4];
+      float mx = -INFINITY;
+  #pragma unroll
+      for (int u = 0; u < 4; ++u)
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = s[u][i] * a.scale_log2;
+          if (slow && 4 * (u & 1) + i >= nv[u >> 1]) v = -INFINITY;
+          sc[u][i] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = max_x32(max_x16(mx));
+      const float mn = fmaxf(m_run, mx);
+      const float mu = mn == -INFINITY ? 0.0f : mn;   // no key yet: every p and alpha is 0
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mu);
+      float psum = 0.0f;
+      bf16x8_t pop[2];
+  #pragma unroll
+      for (int u = 0; u < 4; ++u)
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = __builtin_amdgcn_exp2f(sc[u][i] - mu);
+          psum += p;
+          pop[u >> 1][4 * (u & 1) + i] = (__bf16)p;
+        }
+      l_run = l_run * alpha + psum;
+      m_run = mn;
+  #pragma unroll
+      for (int dg = 0; dg < NDG; ++dg) o[dg] *= alpha;
+
+      // PV products (keys past the end or in invalid blocks: V zeroed, since
+      // unwritten slots may hold anything)
+      if (slow) {
+  #pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          if constexpr (F8) {
+            const uint64_t m8 = nv[c2] >= 8 ? ~0ull : ((1ull << (8 * nv[c2])) - 1);
+  #pragma unroll
+            for (int dg = 0; dg < NDG; ++dg) {
+              vr[c2][dg].x &= (uint32_t)m8;
+              vr[c2][dg].y &= (uint32_t)(m8 >> 32);
+            }
+          } else {
+            uint32_t mw[4];
+  #pragma unroll
+            for (int w = 0; w < 4; ++w)
+              mw[w] = (2 * w < nv[c2] ? 0xffffu : 0u) | (2 * w + 1 < nv[c2] ? 0xffff0000u : 0u);
+  #pragma unroll
+            for (int dg = 0; dg < NDG; ++dg) {
+              vr[c2][dg].x &= mw[0];
+              vr[c2][dg].y &= mw[1];
+              vr[c2][dg].z &= mw[2];
+              vr[c2][dg].w &= mw[3];
+            }
+          }
+        }
+      }
+  #pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+  #pragma unroll
+        for (int dg = 0; dg < NDG; ++dg) {
+          bf16x8_t vop;
+          if constexpr (F8) vop = fp8x8_bf16(vr[c2][dg].x, vr[c2][dg].y);
+          else vop = as_bf16x8(vr[c2][dg]);
+          o[dg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[c2], o[dg], 0, 0, 0);
+        }
+
+      // the next step's V.  (The empty asm with a memory clobber keeps the
+      // compiler from merging these reads with the first step's into one read
+      // at the top of the loop, which would issue V only when it is needed.)
+      issue_v(vr, n0, n1, n2, n3);
+      asm volatile("" ::: "memory");
+      b0 = n0, b1 = n1, b2 = n2, b3 = n3;
+      idv_next = idv_next2;
+    }
+
+    // ---- totals and output: lane (r, j) holds dims 16 dg + 4 j + i of head r ----
+    const float l_tot = sum_x32(sum_x16(l_run));
+    if (r >= g) return;
+    const int qh = qh0 + r;
+    if (part < 0) {
+      const float f = a.v_scale / l_tot;
+      uint16_t *orow = (uint16_t *)a.out + ((int64_t)token * a.num_q_heads + qh) * D + 4 * j;
+  #pragma unroll
+      for (int dg = 0; dg < NDG; ++dg) {
+        uint2 w;
+        w.x = pack_bf16x2(o[dg][0] * f, o[dg][1] * f);
+        w.y = pack_bf16x2(o[dg][2] * f, o[dg][3] * f);
+        *(uint2 *)(orow + 16 * dg) = w;
+      }
+    } else {
+      float *po = a.part_o + ((int64_t)part * a.num_q_heads + qh) * D + 4 * j;
+  #pragma unroll
+      for (int dg = 0; dg < NDG; ++dg) {
+        const f32x4_t v = o[dg] * a.v_scale;
+        *(float4 *)(po + 16 * dg) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+      if (j == 0) {
+        float *pml = a.part_ml + ((int64_t)part * a.num_q_heads + qh) * 2;
+        pml[0] = m_run;
+        pml[1] = l_tot;
+      }
+    }
+  };
+
+  // the second item's first step, read now (PAIR)
+  uint4 kr2[4][NKX];
+  VReg vr2[2][NDG];
+  const int item_b = PAIR && a.pair_stride + bin < a.n_items ? a.pair_stride + bin : -1;
+  int pb0 = -1, pb1 = -1, pb2 = -1, pb3 = -1, pidv = -1;
+  if (PAIR && item_b >= 0) {
+    const DecodeItem ib = a.items[item_b];
+    const int req = uniform(ib.req), kv_begin = uniform(ib.kv_begin), kv_end = uniform(ib.kv_end);
+    const int kv_last = uniform(ib.wpos) >= 0 && a.knew != nullptr ? kv_end - 1 : kv_end;
+    const int32_t *__restrict__ btrow = a.block_table + (int64_t)req * a.bt_stride;
+    // ---- block ids: lane group j reads block j of a step ----
+    // (the read itself is unconditional, at an index clamped to the row's last
+    // block, so that no branch sits between the step's loads)
+    const int last_bi = kv_last > 0 ? (kv_last - 1) >> 4 : 0;
+    auto ids_of = [&](int itx) {
+      const int bi = (itx >> 4) + j;
+      const int id = btrow[bi < last_bi ? bi : last_bi];
+      return bi <= last_bi ? id : -1;
+    };
+    if (kv_begin < kv_last) {
+      const int idv = ids_of(kv_begin);
+      pb0 = blk(idv, 0), pb1 = blk(idv, 1), pb2 = blk(idv, 2), pb3 = blk(idv, 3);
+      pidv = ids_of(kv_begin + kKeysPerIter);
+      issue_k(kr2, pb0, pb1, pb2, pb3);
+      asm volatile("" ::: "memory");
+      issue_v(vr2, pb0, pb1, pb2, pb3);
+      asm volatile("" ::: "memory");
+    }
+  }
+  run(bin, false, -1, -1, -1, -1, -1);
+  if (PAIR && item_b >= 0) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int x = 0; x < NKX; ++x) kr[u][x] = kr2[u][x];
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-      for (int dg = 0; dg < NDG; ++dg) {
-        bf16x8_t vop;
-        if constexpr (F8) vop = fp8x8_bf16(vr[c2][dg].x, vr[c2][dg].y);
-        else vop = as_bf16x8(vr[c2][dg]);
-        o[dg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[c2], o[dg], 0, 0, 0);
-      }
-
-    // the next step's V.  (The empty asm with a memory clobber keeps the
-    // compiler from merging these reads with the first step's into one read
-    // at the top of the loop, which would issue V only when it is needed.)
-    issue_v(n0, n1, n2, n3);
-    asm volatile("" ::: "memory");
-    b0 = n0, b1 = n1, b2 = n2, b3 = n3;
-    idv_next = idv_next2;
-  }
-
-  // ---- totals and output: lane (r, j) holds dims 16 dg + 4 j + i of head r ----
-  const float l_tot = sum_x32(sum_x16(l_run));
-  if (r >= g) return;
-  const int qh = qh0 + r;
-  if (part < 0) {
-    const float f = a.v_scale / l_tot;
-    uint16_t *orow = (uint16_t *)a.out + ((int64_t)token * a.num_q_heads + qh) * D + 4 * j;
-#pragma unroll
-    for (int dg = 0; dg < NDG; ++dg) {
-      uint2 w;
-      w.x = pack_bf16x2(o[dg][0] * f, o[dg][1] * f);
-      w.y = pack_bf16x2(o[dg][2] * f, o[dg][3] * f);
-      *(uint2 *)(orow + 16 * dg) = w;
-    }
-  } else {
-    float *po = a.part_o + ((int64_t)part * a.num_q_heads + qh) * D + 4 * j;
-#pragma unroll
-    for (int dg = 0; dg < NDG; ++dg) {
-      const f32x4_t v = o[dg] * a.v_scale;
-      *(float4 *)(po + 16 * dg) = make_float4(v[0], v[1], v[2], v[3]);
-    }
-    if (j == 0) {
-      float *pml = a.part_ml + ((int64_t)part * a.num_q_heads + qh) * 2;
-      pml[0] = m_run;
-      pml[1] = l_tot;
-    }
+      for (int dg = 0; dg < NDG; ++dg) vr[c2][dg] = vr2[c2][dg];
+    run(item_b, true, pb0, pb1, pb2, pb3, pidv);
   }
 }
 
 hipError_t launch_decode_mfma(const pa_kv_pool &p, const DecodeArgs &a, hipStream_t s) {
-  const int units = a.n_items * a.num_kv_heads;
+  const bool pair = a.pair_stride > 0;
+  const int units = (pair ? a.pair_stride : a.n_items) * a.num_kv_heads;
   const dim3 grid((units + kDecodeWaves - 1) / kDecodeWaves), block(64 * kDecodeWaves);
-  if (p.kv_dtype == PA_BF16) {
-    if (p.head_dim == 128) hipLaunchKernelGGL((k_decode_mfma<KV_BF16, 128>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_decode_mfma<KV_BF16, 64>), grid, block, 0, s, a);
+  if (p.kv_dtype == PA_BF16 && p.head_dim == 128) {
+    if (pair) hipLaunchKernelGGL((k_decode_mfma<KV_BF16, 128, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_decode_mfma<KV_BF16, 128, false>), grid, block, 0, s, a);
+  } else if (p.kv_dtype == PA_BF16) {
+    if (pair) hipLaunchKernelGGL((k_decode_mfma<KV_BF16, 64, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_decode_mfma<KV_BF16, 64, false>), grid, block, 0, s, a);
+  } else if (p.head_dim == 128) {
+    if (pair) hipLaunchKernelGGL((k_decode_mfma<KV_FP8, 128, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_decode_mfma<KV_FP8, 128, false>), grid, block, 0, s, a);
   } else {
-    if (p.head_dim == 128) hipLaunchKernelGGL((k_decode_mfma<KV_FP8, 128>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_decode_mfma<KV_FP8, 64>), grid, block, 0, s, a);
+    if (pair) hipLaunchKernelGGL((k_decode_mfma<KV_FP8, 64, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_decode_mfma<KV_FP8, 64, false>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }

@@ -319,6 +319,7 @@ struct Plan {
   int32_t n_slots = 0;
   int32_t part_len = 0;
   int32_t kstart = 0;                            // first key of the split-K items (the cascade's prefix end)
+  int32_t pair_stride = 0;                       // paired layout: items b and pair_stride + b share a wave
   size_t off_dec = 0, off_merge = 0, off_extw = 0, off_pre = 0, off_rtok = 0, off_rslot = 0, off_wseg = 0;
   size_t off_ml = 0, off_o = 0, bytes = 0;
 };
@@ -437,21 +438,22 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
   if (const char *v = getenv("PA_PARTITION_KEYS")) part = std::max(64, atoi(v) / 64 * 64);
   plan.part_len = (int32_t)part;
 
-  // Paired layout (bf16 and fp8 pools: the matrix-core kernel, two waves per
-  // SIMD).  Measured on MI355X: with 8 one-wave workgroups per compute unit,
-  // workgroups u and u + 4 * CUs land on the same SIMD, and the older wave
-  // takes nearly all of the SIMD's memory issue until it ends, so a SIMD
-  // runs its two units one after the other and ends at a time set by their
-  // sum.  So the split-K tokens' 64-key steps, in token order, are packed
-  // into n_bins = 4 * CUs / Hkv bins of at most T steps and at most two
-  // pieces (a bin ends after its second piece), with the smallest T that
-  // fits.  Bins are numbered two-piece bins first; bin b's first piece is
-  // item b and its second item n_bins + b, so there are no gaps (two-piece
-  // bins are split in two while fewer than n_bins bins are used, so that the
-  // second pieces start at n_bins).  Tokens of several pieces get partials
-  // and a merge.  Used when T is at least 8 steps (shorter units are bound by
-  // their start-up, not by the pairing).  PA_DECODE_PAIRS=0: the partition
-  // form above.
+  // Paired layout (bf16 and fp8 pools: the matrix-core kernel).  Measured on
+  // MI355X: with two waves per SIMD (8 one-wave workgroups per compute unit)
+  // workgroups u and u + 4 * CUs share a SIMD, and the older wave takes
+  // nearly all of the SIMD's memory issue until it ends, so the two run one
+  // after the other and the SIMD ends at a time set by their sum.  So the
+  // split-K tokens' 64-key steps, in token order, are packed into at most
+  // n_bins = 4 * CUs / Hkv bins of at most T steps and at most two pieces (a
+  // bin ends after its second piece), with the smallest T that fits, and one
+  // wave per SIMD runs a bin's two pieces in turn (pair_stride: bin b's pieces
+  // are items b and pair_stride + b; two-piece bins are numbered first, so
+  // the items have no gaps).  The wave reads its second piece's first K/V at
+  // the start, so the second piece starts without a wait.  Tokens of several
+  // pieces get partials and a merge.  Used when T is at least 8 steps
+  // (shorter units are bound by their start-up).  PA_DECODE_PAIRS=2: the same
+  // bins as two waves of one SIMD (each piece its own wave; bins split until
+  // there are n_bins); 0: the partition form above.
   int64_t n_bins = 0, pair_T = 0;
   std::vector<int32_t> tok_steps;
   auto bins_for = [&](int64_t T, std::vector<std::array<int32_t, 4>> *pieces) {
@@ -498,13 +500,15 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
     }
   }
   const bool paired = pair_T > 0;
+  const bool pair_waves = getenv("PA_DECODE_PAIRS") && atoi(getenv("PA_DECODE_PAIRS")) == 2;
   std::vector<std::array<int32_t, 4>> pieces;
   if (paired) {
     const int64_t m = bins_for(pair_T, &pieces);
     std::vector<int32_t> cnt(m, 0);
     for (const auto &pc : pieces) ++cnt[pc[0]];
-    // split two-piece bins while bins are short of n_bins
-    int64_t extra = n_bins - m;
+    // split two-piece bins while bins are short of n_bins (the form with two
+    // waves per SIMD, PA_DECODE_PAIRS=2: each piece its own wave)
+    int64_t extra = pair_waves ? n_bins - m : 0;
     std::vector<char> split(m, 0);
     for (int64_t b0 = 0; b0 < m && extra > 0; ++b0)
       if (cnt[b0] == 2) {
@@ -521,7 +525,8 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
       if (id0[b0] < 0) id0[b0] = nid++;
       if (split[b0]) id1[b0] = nid++;
     }
-    const int32_t nb = nid;                   // n_bins, or fewer when every bin holds one piece
+    const int32_t nb = nid;                   // bins (n_bins in the two-wave form, unless every bin holds one piece)
+    plan.pair_stride = !pair_waves && (int64_t)pieces.size() > nb ? nb : 0;
     for (auto &pc : pieces) {
       const int32_t b0 = pc[0];
       int64_t pos;
@@ -1107,6 +1112,7 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
     a.v_cache = pool->v_cache;
     a.block_table = batch->block_table;
     a.items = (const DecodeItem *)(items + plan.off_dec);
+    a.pair_stride = plan.pair_stride;
     a.part_ml = (float *)(ws + plan.off_ml);
     a.part_o = (float *)(ws + plan.off_o);
     a.n_items = (int32_t)plan.dec.size();

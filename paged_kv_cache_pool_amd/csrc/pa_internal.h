@@ -112,6 +112,9 @@ struct DecodeArgs {
   const void *v_cache;
   const int32_t *block_table;
   const DecodeItem *items;
+  // > 0 (matrix-core kernel): wave (b, kv head), b < pair_stride, runs item b
+  // and then item pair_stride + b when it exists; 0: one item per wave
+  int32_t pair_stride;
   float *part_ml;         // [slots][Hq][2]  (m in log2 units, l)
   float *part_o;          // [slots][Hq][D]
   int32_t n_items;

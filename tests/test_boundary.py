@@ -238,7 +238,7 @@ def test_planner_random_batches(B, monkeypatch):
         # the split-K work, default and forced 64- and 192-key partitions,
         # through the planner's own consistency check
         monkeypatch.setenv("PA_CHECK_PLAN", "1")
-        for pairs, part in [(None, None), ("0", None), ("0", "64"), ("0", "192")]:
+        for pairs, part in [(None, None), ("2", None), ("0", None), ("0", "64"), ("0", "192")]:
             for k, v in [("PA_DECODE_PAIRS", pairs), ("PA_PARTITION_KEYS", part)]:
                 if v is None:
                     monkeypatch.delenv(k, raising=False)

@@ -141,13 +141,13 @@ def test_fused_equals_separate_random(R, seed):
     _check_out(w, sep)
 
 
-@pytest.mark.parametrize("pairs", ["0", "1"])
+@pytest.mark.parametrize("pairs", ["0", "1", "2"])
 @pytest.mark.parametrize("min_rows", ["16", "2"])
 @pytest.mark.parametrize("kv", [W.BF16, W.FP8])
 def test_fused_decode_partitions_and_verify_rows(R, monkeypatch, kv, min_rows, pairs):
     """Decode rows split into 64-key partitions or into the paired layout's
-    pieces (the newest key is written by the row's last item, which may hold
-    that key alone), next to
+    pieces, one wave per bin or per piece (the newest key is written by the
+    row's last item, which may hold that key alone), next to
     speculative-verify-sized chunks of 2 to 8 rows and one prefill chunk.  The
     chunks' K/V are written by the scatter pass before the attention kernels
     read them; the verify chunks run on the split-K kernel (threshold 16) or on
@@ -167,12 +167,12 @@ def test_fused_decode_partitions_and_verify_rows(R, monkeypatch, kv, min_rows, p
     _check_out(w, fused)
 
 
-@pytest.mark.parametrize("pairs", ["0", "1"])
+@pytest.mark.parametrize("pairs", ["0", "1", "2"])
 @pytest.mark.parametrize("kv", [W.BF16, W.FP8])
 def test_fused_cascade(R, monkeypatch, kv, pairs):
     """The shared-prefix pass with the KV update: the decode rows' own keys
     (written inside the split-K kernel) follow the prefix; partition form or
-    paired layout."""
+    paired layout (one wave per bin or per piece)."""
     monkeypatch.setenv("PA_DECODE_PAIRS", pairs)
     say("fused cascade", kv, "pairs", pairs)
     own = [0, 1, 17, 33, 60, 9, 5]

@@ -203,10 +203,11 @@ def test_attention_random_small(R, seed):
     _check_attention(w, step)
 
 
-@pytest.mark.parametrize("pairs", ["0", "1"])
+@pytest.mark.parametrize("pairs", ["0", "1", "2"])
 def test_attention_long_and_split(R, monkeypatch, pairs):
     """Several partials per row and long rows: forced 64-key partitions
-    (pairs "0"), or the paired layout, whose bins (512 for 2 kv heads) cut
+    (pairs "0"), or the paired layout (one wave runs a bin's two pieces, "1";
+    or each piece its own wave, "2"), whose bins (512 for 2 kv heads) cut
     these rows into pieces of a step or two."""
     monkeypatch.setenv("PA_PARTITION_KEYS", "64")
     monkeypatch.setenv("PA_DECODE_PAIRS", pairs)
