@@ -184,13 +184,19 @@ def test_attention_full_size_sampled(R, cfg, n):
     _check_attention(w, step, tokens=_sample_tokens(w, n, seed=cfg))
 
 
+@pytest.mark.parametrize("pairs", [None, "1"])
 @pytest.mark.parametrize("seed", range(24))
-def test_attention_random_small(R, seed):
+def test_attention_random_small(R, monkeypatch, seed, pairs):
+    """Random small batches over pool dtypes, GQA ratios and head dims, in
+    the planner's own decode form and with the paired form forced (its
+    matrix-core kernel for both head dims; fp32 pools keep their kernel)."""
+    if pairs:
+        monkeypatch.setenv("PA_DECODE_PAIRS", pairs)
     kv = [W.F32, W.BF16, W.FP8][seed % 3]
     io = W.F32 if kv == W.F32 else W.BF16
     g = [1, 2, 4, 8][(seed // 3) % 4]
     D = [64, 128][(seed // 12) % 2]
-    say("attention random", seed, kv, "g", g, "D", D)
+    say("attention random", seed, kv, "g", g, "D", D, "pairs", pairs)
     w = W.random_small(seed, max_seqs=5, max_len=300, num_q_heads=2 * g, num_kv_heads=2,
                        head_dim=D, kv_dtype=kv, io_dtype=io, spare_blocks=4)
     if kv == W.FP8:
