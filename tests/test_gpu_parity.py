@@ -225,6 +225,20 @@ def test_attention_long_and_split(R, monkeypatch, pairs):
     _check_attention(w, step)
 
 
+@pytest.mark.parametrize("n,lo,hi", [(200, 512, 1500), (300, 16, 400)])
+def test_attention_many_decode_rows(R, n, lo, hi):
+    """Many decode rows on the Llama-3-8B layer shape: 200 rows of 512-1500
+    keys fit the paired layout (128 bins of two pieces), 300 rows do not
+    (more rows than two per bin) and take the partition form.  Sampled rows
+    against the oracle."""
+    say("attention", n, "decode rows")
+    w = W.llama8b_decode(seed=5, num_seqs=n, lo=lo, hi=hi, num_blocks=n * (hi // 16 + 2) + 64)
+    step = R.GpuStep(w, fused=True)
+    step.run()
+    torch.cuda.synchronize()
+    _check_attention(w, step, tokens=_sample_tokens(w, 40, seed=n))
+
+
 def test_attention_zero_token_requests_and_noncausal(R):
     say("attention c=0 requests + non-causal")
     w = W.build("zeros", 5, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
