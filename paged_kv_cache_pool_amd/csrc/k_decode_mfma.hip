@@ -1,6 +1,7 @@
 // Token-parallel split-K attention on the matrix cores, for bf16 and fp8
-// pools: the same computation and the same work items as k_decode (one wave
-// per (item, kv head), all g <= 16 query heads of the kv head over keys
+// pools: the same computation and the same work items as k_decode (a wave
+// per (item, kv head), or per pair of items below; all g <= 16 query heads
+// of the kv head over keys
 // [kv_begin, kv_end) walked through the block table, online softmax in log2
 // units, partial (m, l, o) for split rows; "vLLM 源码完全拆解（十六）", third
 // walk-through path), with the dot products moved from the vector ALUs to
