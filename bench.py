@@ -2,16 +2,26 @@
 
     python bench.py [--steps K] [--warmup W] [--config N] [--gpus 1]
 
-A step is the whole hot path on one batch: slot derivation (pa_slot_mapping),
-KV scatter (pa_write_kv) and attention (pa_attention: host plan + split-K
-decode + merge + MFMA extend), with every input already in HBM.  The default
-workload is the Llama-3-8B-shaped decode layer: 64 requests, 32 q / 8 kv
-heads, head_dim 128, block 16, bf16 KV, context U[512, 4096], 40k-block pool.
+A step is the whole hot path on one batch: slot derivation, KV scatter and
+attention (host plan + split-K decode + merge + MFMA extend), run as the one
+call with the KV update (pa_write_kv_attention; --separate: the three calls
+pa_slot_mapping, pa_write_kv, pa_attention), with every input already in
+HBM.  The default workload is the largest single-GPU configuration, the
+mixed continuous-batching step with a 2048-token budget: 48 decode rows
+(context U[256, 8192]) + a 512-token prefill chunk + a 1488-token chunk
+after 1536 cached tokens; 32 q / 8 kv heads, head_dim 128, block 16, bf16,
+40k-block pool.  It runs every kernel of the path.
 
-Prints one JSON line: tokens/s (whole step), the dominant kernel's
-bandwidth against the HBM roofline (HIP events recorded around every launch
-of that kernel on its own stream during the timed steps), and the CPU oracle
-timed on this host on the same workload.
+Timing: each of the K timed steps starts with cold caches (a 1 GiB read
+before the step, outside its HIP events, evicts L2 and the 256 MB Infinity
+Cache); ms_per_step is their median, with p10 / p90.  The same K steps back
+to back with warm caches are reported beside it.
+
+Prints one JSON line: tokens/s (whole step), the dominant kernel against its
+roofline (HIP events recorded around every launch on the stream it runs on,
+over K more cold steps), the extend kernel against the bf16 MFMA peak when
+the step has prefill rows, and the CPU oracle timed on this host on the same
+workload.
 """
 import argparse
 import json
@@ -34,7 +44,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--config", type=int, default=2,
+    ap.add_argument("--config", type=int, default=3,
                     help="workload: 1-5 the reference configurations, 6 speculative verify, 7 long prefill")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -54,9 +64,6 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured once into a HIP graph and replayed "
                          "(same batch every replay)")
-    ap.add_argument("--cold", action="store_true",
-                    help="also time steps that start with cold caches (a 1 GiB scratch read "
-                         "before each step, outside the timed events)")
     return ap.parse_args()
 
 
@@ -277,17 +284,37 @@ def main():
         step.run()
     torch.cuda.synchronize()
 
-    # timed region: K steps back to back, bracketed by synchronisations, with
-    # HIP events around every kernel launch on the step's stream
+    # A 1 GiB read before a cold step evicts L2 and the 256 MB Infinity Cache
+    # (clean lines: no write-back is left for the step to pay); it runs before
+    # the step's first event, so only the step is between its events.
+    scratch = torch.ones(1 << 27, dtype=torch.int64, device="cuda")
+
+    def cold_steps(n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for e0, e1 in evs:
+            scratch.max()
+            e0.record(stream)
+            step.run()
+            e1.record(stream)
+        return evs
+
+    # timed region: K cold steps, bracketed by synchronisations
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    evs = cold_steps(a.steps)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    per_step = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+    ms_per_step = float(np.median(per_step))
+    spread = {"p10": round(float(np.percentile(per_step, 10)), 5),
+              "p50": round(ms_per_step, 5),
+              "p90": round(float(np.percentile(per_step, 90)), 5)}
+
+    # K more cold steps with HIP events around every kernel launch on the
+    # stream it runs on (the library records them): the kernels' durations
     B.profile_enable(True)
+    cold_steps(a.steps)
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(a.steps):
-        step.run()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms_instr = ev0.elapsed_time(ev1) / a.steps
     kernels = {}
     for name in ("k_slot_mapping", "k_write_kv", "k_write_new", "k_prefix", "k_decode", "k_merge",
                  "k_extend"):
@@ -296,7 +323,8 @@ def main():
             kernels[name] = {"launches": n, "avg_us": 1000.0 * ms / n}
     B.profile_enable(False)
 
-    # the same K steps without the per-kernel events (reported step time)
+    # the same K steps back to back with warm caches (inputs of the previous
+    # identical step partly cached), beside the cold figure
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -304,39 +332,24 @@ def main():
         step.run()
     e1.record(stream)
     torch.cuda.synchronize()
-    ms_per_step = e0.elapsed_time(e1) / a.steps
-    # K more steps with an event after each, for the per-step spread (the
-    # events add a little time of their own, so this pass is not the figure)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
-    evs[0].record(stream)
-    for k in range(a.steps):
-        step.run()
-        evs[k + 1].record(stream)
-    torch.cuda.synchronize()
-    per_step = np.array([evs[k].elapsed_time(evs[k + 1]) for k in range(a.steps)])
-    spread = {"p10": round(float(np.percentile(per_step, 10)), 5),
-              "p50": round(float(np.percentile(per_step, 50)), 5),
-              "p90": round(float(np.percentile(per_step, 90)), 5)}
+    ms_warm = e0.elapsed_time(e1) / a.steps
     # the other form of the step on the same pool and inputs (the KV write is
-    # idempotent), for comparison
+    # idempotent), for comparison (cold steps, median)
     other = None
     if a.compare:
         step.fused = a.separate
         for _ in range(a.warmup):
             step.run()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(a.steps):
-            step.run()
-        e1.record(stream)
+        evo = cold_steps(a.steps)
         torch.cuda.synchronize()
-        other = round(e0.elapsed_time(e1) / a.steps, 5)
+        other = round(float(np.median([x0.elapsed_time(x1) for x0, x1 in evo])), 5)
         step.fused = not a.separate
 
     graph_ms = None
     if a.graph:
-        # the step captured on a side stream, then replayed on the step's stream
+        # the step captured on a side stream, then replayed on the step's
+        # stream: warm back-to-back replays, against the warm eager figure
         gs = torch.cuda.Stream()
         gs.wait_stream(stream)
         step.stream = gs
@@ -359,26 +372,7 @@ def main():
         torch.cuda.synchronize()
         graph_ms = round(e0.elapsed_time(e1) / a.steps, 5)
         del g
-
-    cold = None
-    if a.cold:
-        # each step starts after a 1 GiB read, so L2 and the 256 MB Infinity
-        # Cache hold none of its inputs (clean lines: no write-back is left
-        # for the step to pay); only the step is between its events
-        scratch = torch.ones(1 << 27, dtype=torch.int64, device="cuda")
-        times = []
-        for _ in range(a.steps):
-            scratch.max()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            step.run()
-            e1.record(stream)
-            e1.synchronize()
-            times.append(e0.elapsed_time(e1))
-        cold = {"p10": round(float(np.percentile(times, 10)), 5),
-                "p50": round(float(np.percentile(times, 50)), 5),
-                "p90": round(float(np.percentile(times, 90)), 5)}
-        del scratch
+    del scratch
 
     T = w.num_tokens
     tokens_per_s = T / (ms_per_step / 1000.0)
@@ -415,6 +409,17 @@ def main():
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": load_traffic(dom, w.name),
                 "algorithmic_flops_per_launch": ext_flops}
+
+    # the extend kernel against the bf16 MFMA peak whenever the step has
+    # prefill rows (its flops: visible (query, key) pairs only)
+    roof_ext = None
+    if ext_flops and "k_extend" in kernels:
+        achieved = ext_flops / (kernels["k_extend"]["avg_us"] * 1e-6) / 1e12
+        roof_ext = {"kernel": "k_extend", "bound": "mfma", "achieved": round(achieved, 1),
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "traffic": load_traffic("k_extend", w.name),
+                    "algorithmic_flops_per_launch": ext_flops}
 
     cpu = None
     if a.cpu_seconds > 0:
@@ -455,18 +460,20 @@ def main():
                    "num_blocks": w.num_blocks, "context_total": int(sl.sum()),
                    "context_min": int(sl.min()), "context_max": int(sl.max()), "seed": a.seed},
         "roofline": roof,
+        **({"roofline_extend": roof_ext} if roof_ext is not None and dom != "k_extend" else {}),
         "cpu_baseline": cpu,
+        "timing": "cold caches: a 1 GiB read before each step, outside its events; median of the "
+                  "steps' HIP-event times",
+        "ms_per_step_spread": spread,
+        "ms_per_step_warm": round(ms_warm, 5),
+        "timed_region_wall_s": round(t_wall, 4),
         "kernels_us": {k: round(v["avg_us"], 2) for k, v in kernels.items()},
         "step_form": "separate calls" if a.separate else "one call with the KV update",
         **({("ms_per_step_one_call" if a.separate else "ms_per_step_separate_calls"): other}
            if other is not None else {}),
-        **({"ms_per_step_graph_replay": graph_ms} if graph_ms is not None else {}),
-        "ms_per_step_with_kernel_events": round(ms_instr, 5),
-        "ms_per_step_spread": spread,
+        **({"ms_per_step_graph_replay_warm": graph_ms} if graph_ms is not None else {}),
         "decode_kv_gbps": roof["achieved"] if dom == "k_decode" else None,
     }
-    if cold is not None:
-        out["ms_per_step_cold"] = cold
     if dom == "k_decode":
         uniq = unique_kv_bytes(w, sl, qsl, prefix)
         out["decode_kv_bytes_logical"] = dec_bytes

@@ -29,9 +29,13 @@
  *   pa_attention on one stream attends over the freshly written rows, as
  *   [P1] §6.1 orders them).
  * - Errors are reported through pa_status only; nothing is thrown across
- *   the ABI.  On any status other than PA_OK the call has enqueued no work
- *   and pa_last_error() (per thread) describes the problem.  PA_ERR_HIP means
- *   a HIP runtime call failed.
+ *   the ABI.  On any status other than PA_OK and PA_ERR_HIP the call has
+ *   enqueued no work, and pa_last_error() (per thread) describes the
+ *   problem.  PA_ERR_HIP means a HIP runtime call failed; when a call
+ *   launches several kernels and a later launch fails, the kernels queued
+ *   before it stay queued (for pa_write_kv_attention this can be part of
+ *   the KV update).  Every argument and workspace check is done before the
+ *   first launch.
  * - The library is thread-compatible: concurrent calls on different streams
  *   are allowed; the workspace passed to pa_attention must not be shared by
  *   calls that may run concurrently.
@@ -186,7 +190,13 @@ pa_status pa_write_kv(const pa_kv_pool *pool, const void *key, const void *value
 
 /* Device workspace pa_attention and pa_write_kv_attention need for this
  * batch (bytes), or 0 when the arguments are invalid (pa_last_error() says
- * why). */
+ * why).  The attention backend plans a batch on the host and runs it in a
+ * caller-provided workspace ([P5] fourth walk-through path: the backend's
+ * metadata builder prepares the plan and workspace before the kernels run);
+ * the size depends only on the pool's shape and the batch's host mirrors
+ * (the split-K partial results (m, l, o) of the rows whose keys are cut
+ * into several pieces, plus room for the work lists), so the query and the
+ * call always agree.  Host only: launches nothing. */
 size_t pa_attention_workspace_bytes(const pa_kv_pool *pool, const pa_batch *batch,
                                     int32_t num_q_heads);
 

@@ -165,13 +165,20 @@ class KVPool:
     def elem_offset(self, which: int, block: int, offset: int, head: int, dim: int) -> int:
         return int(lib.pa_kv_elem_offset(C.byref(self.struct()), which, block, offset, head, dim))
 
-    def logical(self, which: str) -> np.ndarray:
+    def logical(self, which: str, blocks: Optional[np.ndarray] = None) -> np.ndarray:
         """Copy of K or V in logical [num_blocks][block_size][num_kv_heads][head_dim]
-        order, as raw element values (float32, uint16 bf16 bits, or uint8 codes)."""
-        raw = (self.k_cache if which == "k" else self.v_cache).cpu().numpy()
+        order, as raw element values (float32, uint16 bf16 bits, or uint8 codes).
+        With `blocks`, only those blocks, in that order ([len(blocks)][...])."""
+        dev = self.k_cache if which == "k" else self.v_cache
+        nb = self.num_blocks
+        if blocks is not None:
+            idx = torch.as_tensor(np.asarray(blocks, dtype=np.int64), device=dev.device)
+            dev = dev.view(nb, -1).index_select(0, idx)
+            nb = int(idx.numel())
+        raw = dev.cpu().numpy().reshape(-1)
         npd = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[self.kv_dtype]
         el = raw.view(npd)
-        nb, S, H, D = self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim
+        S, H, D = self.block_size, self.num_kv_heads, self.head_dim
         if which == "k":
             E = 16 // el.itemsize
             return el.reshape(nb, H, D // E, S, E).transpose(0, 3, 1, 2, 4).reshape(nb, S, H, D).copy()

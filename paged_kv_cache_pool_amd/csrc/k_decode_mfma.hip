@@ -25,7 +25,8 @@
 // fp8 pools: K and V codes become bf16 in registers (exact: every E4M3 value
 // is a bf16 value); the K scale is folded into the score scale, the V scale is
 // applied to the output, as in k_decode.  The probabilities are rounded to
-// bf16 for the PV product; l sums them in fp32.
+// bf16 for the PV product, and l sums the rounded values, so the output is
+// normalised by exactly the weights it is made of.
 //
 // Loads: bf16 K/V tiles are read non-temporally (each byte is read once per
 // row); measured faster on the bf16 decode workloads (up to 6 % when prefill
@@ -366,15 +367,23 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
       const float mn = fmaxf(m_run, mx);
       const float mu = mn == -INFINITY ? 0.0f : mn;   // no key yet: every p and alpha is 0
       const float alpha = __builtin_amdgcn_exp2f(m_run - mu);
+      // P is rounded to bf16 for the PV product, and l sums those rounded
+      // values (v_dot2 with (1, 1) per pair), so the output is normalised by
+      // exactly the weights it is made of
+      constexpr uint32_t kOnes = 0x3F803F80u;    // (1.0, 1.0) in bf16
       float psum = 0.0f;
       bf16x8_t pop[2];
   #pragma unroll
       for (int u = 0; u < 4; ++u)
   #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(sc[u][i] - mu);
-          psum += p;
-          pop[u >> 1][4 * (u & 1) + i] = (__bf16)p;
+        for (int i = 0; i < 4; i += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(sc[u][i] - mu);
+          const float p1 = __builtin_amdgcn_exp2f(sc[u][i + 1] - mu);
+          const uint32_t pw = pack_bf16x2(p0, p1);
+          psum = dot2_bf16(pw, kOnes, psum);
+          const bf16x2_t pb = __builtin_bit_cast(bf16x2_t, pw);
+          pop[u >> 1][4 * (u & 1) + i] = pb[0];
+          pop[u >> 1][4 * (u & 1) + i + 1] = pb[1];
         }
       l_run = l_run * alpha + psum;
       m_run = mn;

@@ -370,9 +370,15 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
   // blocks for every request; their attention over them is computed once per
   // kv head by the MFMA prefix pass and merged with the rest.  Used when
   // every split-K request holds the prefix wholly in its history.
-  const int32_t P = b.num_common_prefix_blocks * kBlock;
-  bool cascade = P > 0 && extend_supported(p, q_dtype) && !env_flag("PA_DISABLE_CASCADE") &&
+  // (in int64: a hint of any int32 value is compared with the histories,
+  // never wrapped; one longer than INT32_MAX keys or beyond bt_stride cannot
+  // lie in any request's history, so it is ignored)
+  const int64_t P64 = (int64_t)b.num_common_prefix_blocks * kBlock;
+  bool cascade = P64 > 0 && P64 <= INT32_MAX && b.num_common_prefix_blocks <= b.bt_stride &&
+                 extend_supported(p, q_dtype) &&
+                 !env_flag("PA_DISABLE_CASCADE") &&
                  (int64_t)b.num_tokens * Hq * p.head_dim * 2 < ((int64_t)1 << 32);
+  const int32_t P = cascade ? (int32_t)P64 : 0;
   int32_t prefix_rows = 0;
   for (int32_t i = 0; i < b.num_seqs && cascade; ++i) {
     const int32_t c = q[i + 1] - q[i];
@@ -1016,6 +1022,14 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
   const float kscale = pool->kv_dtype == PA_FP8_E4M3 ? pool->k_scale : 1.0f;
   const float vscale = pool->kv_dtype == PA_FP8_E4M3 ? pool->v_scale : 1.0f;
 
+  // Every check and set-up that can fail without a HIP launch error is done
+  // before the first launch, so that such a failure leaves the pool as it was.
+  hipStream_t xs = s;
+  SideStream *side = nullptr;
+  // (not with key pieces: their partials are merged on the caller's stream)
+  const bool fork = !plan.extw.empty() && plan.merge.empty() && !plan.dec.empty() && env_flag("PA_OVERLAP");
+  if (fork && (st = side_stream(&side)) != PA_OK) return st;
+
   hipError_t e = hipSuccess;
   // KV update, first part: the new rows no decode unit writes itself (slots
   // derived on the fly), before any kernel that may read them
@@ -1038,12 +1052,7 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
     if (e != hipSuccess) return hip_fail(e, "k_write_new launch");
   }
   // the extend kernel goes to the side stream when decode work runs beside it
-  hipStream_t xs = s;
-  SideStream *side = nullptr;
-  // (not with key pieces: their partials are merged on the caller's stream)
-  const bool fork = !plan.extw.empty() && plan.merge.empty() && !plan.dec.empty() && env_flag("PA_OVERLAP");
   if (fork) {
-    if ((st = side_stream(&side)) != PA_OK) return st;
     if ((e = hipEventRecord(side->fork, s)) != hipSuccess) return hip_fail(e, "fork record");
     if ((e = hipStreamWaitEvent(side->stream, side->fork, 0)) != hipSuccess) return hip_fail(e, "fork wait");
     xs = side->stream;

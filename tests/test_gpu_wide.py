@@ -7,6 +7,7 @@ key ranges are cut into pieces whose partial (m, l, o) the merge kernel
 combines.  PA_WIDE_PIECES forces the number of pieces, so small batches cover
 the piece path; PA_DISABLE_WIDE routes the same rows to the key-split kernel.
 """
+import dataclasses
 import sys
 
 import numpy as np
@@ -56,15 +57,19 @@ def _err(w, step, causal=True):
     return float(np.abs(got - ref).max())
 
 
+# (g, c, hist): every case has more than 128 (token, head) columns, so it
+# reaches the wide kernel (g = 1 takes longer chunks for that)
+WIDE_CASES = [(g, c, h) for g in (1, 4, 8, 16)
+              for c, h in ([(140, 0), (200, 37)] if g == 1 else [(40, 0), (100, 37)]) + [(257, 300), (600, 1000)]]
+
+
 @pytest.mark.parametrize("pieces", ["1", "2", "3"])
-@pytest.mark.parametrize("g", [1, 4, 8])
-@pytest.mark.parametrize("c,hist", [(40, 0), (100, 37), (257, 300), (600, 1000)])
+@pytest.mark.parametrize("g,c,hist", WIDE_CASES)
 def test_wide_chunks(R, monkeypatch, pieces, g, c, hist):
     """Causal chunks with history on the wide kernel, whole key range or cut
     into 2 / 3 pieces, with ragged column blocks (c * g not a multiple of
     256) and a decode row in the same batch."""
-    if c * g <= 128:
-        pytest.skip("fits one key-split item")
+    assert c * g > 128
     monkeypatch.setenv("PA_WIDE_PIECES", pieces)
     say("wide g", g, "c", c, "hist", hist, "pieces", pieces)
     w = _chunk_batch(f"wide_{g}_{c}_{hist}", g, c, hist, W.BF16)
@@ -74,7 +79,7 @@ def test_wide_chunks(R, monkeypatch, pieces, g, c, hist):
 
 
 @pytest.mark.parametrize("pieces", ["1", "2"])
-@pytest.mark.parametrize("g", [4, 8])
+@pytest.mark.parametrize("g", [4, 8, 16])
 @pytest.mark.parametrize("c,hist", [(100, 37), (600, 1000)])
 def test_wide_chunks_fp8(R, monkeypatch, pieces, g, c, hist):
     """The same over an fp8 pool (k_scale folded into the scores, v_scale
@@ -167,8 +172,9 @@ def test_wide_default_large_prefill(R, monkeypatch):
 def test_wide_pieces_graph_capture(R, monkeypatch, fused):
     """A step with wide items cut into two key pieces (so the merge runs too),
     captured into a HIP graph: every replay equals the eager step bit for bit,
-    with an eager step of another batch between replays, and a replay reads
-    new query contents."""
+    with an eager step of another batch between replays, and matches the
+    oracle; a replay reads new query contents and matches the oracle for
+    them."""
     monkeypatch.setenv("PA_WIDE_PIECES", "2")
     w = _chunk_batch("wide_graph", 4, 600, 1000, W.BF16)
     s = torch.cuda.Stream()
@@ -177,6 +183,7 @@ def test_wide_pieces_graph_capture(R, monkeypatch, fused):
         step.run()
     s.synchronize()
     eager = step.out.clone()
+    assert _err(w, step) <= TOL
     other = R.GpuStep(_chunk_batch("wide_graph_other", 8, 257, 300, W.BF16), fused=True)
     g = torch.cuda.CUDAGraph()
     step.out.zero_()
@@ -195,6 +202,11 @@ def test_wide_pieces_graph_capture(R, monkeypatch, fused):
     g.replay()
     torch.cuda.synchronize()
     replayed = step.out.clone()
+    # halving is exact in bf16 for these values: the oracle gets the same query
+    half = dataclasses.replace(w, query=W.f32_to_bf16_bits(W.to_f32(w.query, W.BF16) * np.float32(0.5)))
+    err = _err(half, step)
+    say("replay after the query change, max_abs_err", err)
+    assert err <= TOL
     with torch.cuda.stream(s):
         step.run()
     s.synchronize()
