@@ -55,7 +55,13 @@ def parse():
                     help="turn four rocprofv3 --pmc output folders (FETCH_SIZE and WRITE_SIZE of "
                          "this workload, then of --copy-calibration) into the traffic record of "
                          "the dominant kernel under profiles/, and exit")
-    ap.add_argument("--kernel", default="k_decode", help="kernel for --traffic-ingest")
+    ap.add_argument("--kernel", default="k_decode", help="kernel for --traffic-ingest / --counters-ingest")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("TRACE_DIR", "BENCH_OUT"),
+                    help="turn a rocprofv3 --kernel-trace --stats folder of a bench.py run and that run's "
+                         "output (its JSON line) into profiles/<kernel>_<workload>.md, and exit")
+    ap.add_argument("--counters-ingest", nargs="+", metavar="DIR",
+                    help="turn rocprofv3 --pmc output folders (one pass each) into the counter record "
+                         "of --kernel on this workload under profiles/, and exit")
     ap.add_argument("--separate", action="store_true",
                     help="time the step as three calls (slot derivation, KV write, attention) "
                          "instead of the one call that includes the KV update")
@@ -162,6 +168,140 @@ def traffic_ingest(a):
     print(json.dumps(rec), flush=True)
 
 
+def counters_ingest(a):
+    """Write the counter record of a kernel on a workload: the mean per
+    dispatch of every counter found in the given --pmc passes, the kernel's
+    mean duration from the same runs, and the derived figures:
+    * MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 * 1024):
+      the busy counter is summed over all 1024 SIMDs (32 cycles per
+      32x32x16 MFMA), and GRBM_GUI_ACTIVE as reported is summed over the 8
+      XCDs, each counting its own active cycles, so GRBM_GUI_ACTIVE / 8 is a
+      SIMD's cycles during the dispatch;
+    * clock = GRBM_GUI_ACTIVE / 8 / the dispatch's duration;
+    * wave wait share = SQ_WAIT_ANY / SQ_WAVE_CYCLES, and busy-issue share =
+      SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (waves that cannot issue)."""
+    import csv
+    import glob
+    from paged_kv_cache_pool_amd import workloads as W
+    vals, durs = {}, []
+    for folder in a.counters_ingest:
+        files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {folder}")
+        for f in files:
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if a.kernel in r["Kernel_Name"]:
+                        vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                        if "End_Timestamp" in r and r.get("Start_Timestamp"):
+                            durs.append(float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
+    if not vals:
+        raise SystemExit(f"no counters for '{a.kernel}'")
+    mean = {k: sum(v) / len(v) for k, v in vals.items()}
+    n = {k: len(v) for k, v in vals.items()}
+    simds, xcds = 4 * 256, 8
+    derived = {}
+    dur_us = sum(durs) / len(durs) / 1e3 if durs else None
+    if dur_us:
+        derived["duration_us"] = dur_us
+    if "GRBM_GUI_ACTIVE" in mean and dur_us:
+        derived["clock_ghz"] = mean["GRBM_GUI_ACTIVE"] / xcds / (dur_us * 1e3)
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and "GRBM_GUI_ACTIVE" in mean:
+        derived["mfma_busy"] = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (mean["GRBM_GUI_ACTIVE"] / xcds * simds)
+    if "SQ_INSTS_MFMA" in mean:
+        derived["mfma_flops"] = mean["SQ_INSTS_MFMA"] * 32 * 32 * 16 * 2
+    if "SQ_WAIT_ANY" in mean and "SQ_WAVE_CYCLES" in mean:
+        derived["wave_wait_share"] = mean["SQ_WAIT_ANY"] / mean["SQ_WAVE_CYCLES"]
+    if "SQ_WAIT_INST_ANY" in mean and "SQ_WAVE_CYCLES" in mean:
+        derived["wave_no_issue_share"] = mean["SQ_WAIT_INST_ANY"] / mean["SQ_WAVE_CYCLES"]
+    if "SQ_INSTS_LDS" in mean and "SQ_INSTS_VALU" in mean:
+        derived["lds_per_valu"] = mean["SQ_INSTS_LDS"] / mean["SQ_INSTS_VALU"]
+    w = W.make(a.config, a.seed)
+    src_kernel = "k_extend" if a.kernel in ("k_extend_wide", "k_extend") else "k_decode"
+    rec = {"kernel": a.kernel, "workload": w.name, "source_sha": source_hash(src_kernel),
+           "counters_mean_per_dispatch": {k: round(v, 1) for k, v in sorted(mean.items())},
+           "dispatches": n, "derived": {k: round(v, 4) for k, v in derived.items()}}
+    cmd = f"python bench.py --config {a.config} --steps 5 --warmup 2 --cpu-seconds 0"
+    text = [f"# Hardware counters of {a.kernel}, workload {w.name}", "",
+            "One rocprofv3 --pmc pass per counter group, on the GPU box, from the repository root:", "",
+            "```",
+            f"rocprofv3 --pmc <counters of one pass> -d <pass folder> -o run --output-format csv -- {cmd}",
+            f"python bench.py --config {a.config} --kernel {a.kernel} --counters-ingest <pass folders>",
+            "```", "",
+            "Derived: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs) (the "
+            "busy counter is summed over the SIMDs, GRBM_GUI_ACTIVE over the XCDs); clock = GRBM_GUI_ACTIVE "
+            "/ 8 / duration; mfma_flops = SQ_INSTS_MFMA x 32768 (32x32x16 MFMAs); wave wait share = "
+            "SQ_WAIT_ANY / SQ_WAVE_CYCLES; no-issue share = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES.",
+            "The record holds the hash of the kernel's sources it was taken on.", "",
+            "| counter | mean per dispatch |", "|---|---|"]
+    text += [f"| {k} | {v:,.0f} |" for k, v in sorted(mean.items())]
+    text += ["", "| derived | value |", "|---|---|"]
+    text += [f"| {k} | {v:.4f} |" for k, v in derived.items()]
+    text += ["", "```json", json.dumps(rec), "```", ""]
+    path = os.path.join(ROOT, "profiles", f"counters_{a.kernel}_{w.name}.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(text))
+    print(json.dumps(rec), flush=True)
+
+
+def trace_summary(a):
+    """Summary of a traced bench.py run: rocprofv3's per-kernel statistics over
+    every launch, the average over the launches of the cold profiled pass
+    (bench.py's roofline pass: launches W + K .. W + 2K - 1 of each step
+    kernel), and the run's own JSON line."""
+    import csv
+    trace_dir, bench_out = a.trace_summary
+    res = None
+    with open(bench_out) as fh:
+        for line in fh:
+            if line.startswith("{") and '"metric"' in line:
+                res = json.loads(line)
+    if res is None:
+        raise SystemExit(f"no JSON line in {bench_out}")
+    stats = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
+    trace = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))))
+    W_, K_ = res["warmup"], res["steps"]
+    by_kernel = {}
+    for r in sorted(trace, key=lambda r: int(r["Start_Timestamp"])):
+        by_kernel.setdefault(r["Kernel_Name"], []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    wl = res["config"]["workload"]
+    dom = res["roofline"]["kernel"]
+    cmd = (f"rocprofv3 --kernel-trace --stats -d <trace_dir> -o run --output-format csv -- python3 bench.py "
+           f"--config {a.config} --steps {K_} --warmup {W_} --cpu-seconds 0 > <bench_out>")
+    text = [f"# Kernel trace of one step of workload {wl} (seed {res['config']['seed']}), "
+            f"{res['step_form']}", "",
+            "Commands (repository root on the MI355X box):", "", "```", cmd,
+            f"python bench.py --config {a.config} --trace-summary <trace_dir> <bench_out>", "```", "",
+            f"The run does {W_} warm-up steps, then {K_} cold timed steps, {K_} cold steps with the "
+            f"library's per-launch HIP events (the roofline pass), then {K_} warm steps: "
+            f"{W_ + 3 * K_} launches of each kernel of the step.  A cold step starts after a 1 GiB read "
+            "that evicts L2 and the Infinity Cache.", "",
+            "| kernel | launches | avg us (all) | min us | max us | avg us (roofline pass) |",
+            "|---|---|---|---|---|---|"]
+    for r in stats:
+        name = r["Name"]
+        d = by_kernel.get(name, [])
+        rp = d[W_ + K_: W_ + 2 * K_] if len(d) >= W_ + 2 * K_ else []
+        rp_s = f"{sum(rp) / len(rp):.2f}" if rp else "-"
+        text.append(f"| `{name[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {rp_s} |")
+    text += ["", "bench.py's own figures in the same run (HIP events on the launching stream):", "",
+             f"- kernels_us: {res.get('kernels_us')}",
+             f"- roofline ({dom}): achieved {res['roofline']['achieved']} {res['roofline']['unit']} = "
+             f"{100 * res['roofline']['frac']:.1f}% of {res['roofline']['peak']}"]
+    if res.get("roofline_extend"):
+        re_ = res["roofline_extend"]
+        text.append(f"- roofline_extend: {re_['achieved']} {re_['unit']} = {100 * re_['frac']:.1f}% of {re_['peak']}")
+    text += [f"- ms_per_step {res['ms_per_step']} (cold median; p10/p90 {res['ms_per_step_spread']['p10']} / "
+             f"{res['ms_per_step_spread']['p90']}), warm {res.get('ms_per_step_warm')}; "
+             f"{res['value']} tokens/s", ""]
+    path = os.path.join(ROOT, "profiles", f"{dom}_{wl}.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(text))
+    print(path)
+
+
 def load_traffic(kernel, workload):
     """Measured HBM bytes per launch, or None when absent or taken on other sources."""
     path = traffic_record_path(kernel, workload)
@@ -250,6 +390,12 @@ def main():
     a = parse()
     if a.traffic_ingest:
         traffic_ingest(a)
+        return
+    if a.counters_ingest:
+        counters_ingest(a)
+        return
+    if a.trace_summary:
+        trace_summary(a)
         return
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
