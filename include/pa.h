@@ -247,6 +247,32 @@ pa_status pa_write_kv_attention(const pa_kv_pool *pool, const pa_batch *batch, c
                                 int64_t *slot_mapping, void *output, void *workspace,
                                 size_t workspace_bytes, pa_stream_t stream);
 
+/* pa_write_kv_attention for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, result, pool bytes and errors as
+ * pa_write_kv_attention, without the workspace: the call's work lists and
+ * split-K partials live in a static device array of the library
+ * (pa_noalloc_scratch_bytes() bytes, 32 MiB; each device the library runs
+ * on holds its own copy until the process ends).  The call allocates no
+ * device, pinned or managed memory and creates no stream (its host-side
+ * plan uses ordinary host memory); the work lists reach the array through
+ * kernels that carry them as arguments.  A batch whose plan needs more than
+ * the array returns PA_ERR_WORKSPACE before anything is launched (all five
+ * reference workloads fit; the largest, 128 decode rows over a shared
+ * prefix, needs about 20 MiB).  No part of the array needs to start at zero:
+ * every byte a kernel reads was written earlier in the same call.  Every
+ * call on one device shares that device's array and it keeps the last
+ * call's contents, so calls that may overlap on one device (other streams,
+ * other threads) race and give undefined results; serialise them. */
+pa_status pa_write_kv_attention_noalloc(const pa_kv_pool *pool, const pa_batch *batch,
+                                        const void *query, const void *key, const void *value,
+                                        pa_dtype q_dtype, int32_t num_q_heads, float softmax_scale,
+                                        int32_t causal, int64_t *slot_mapping, void *output,
+                                        pa_stream_t stream);
+
+/* Bytes of the static scratch pa_write_kv_attention_noalloc uses per device. */
+size_t pa_noalloc_scratch_bytes(void);
+
 /* ---------------------------------------------------------------------- */
 /* Host block pool (the KV-cache manager on either side of the step).
  *

@@ -27,7 +27,8 @@ STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED", 3: "PA_E
 
 # Every symbol include/pa.h declares.
 EXPORTS = ["pa_prepare_metadata", "pa_slot_mapping", "pa_write_kv", "pa_attention_workspace_bytes",
-           "pa_attention", "pa_write_kv_attention", "pa_kv_cache_bytes", "pa_kv_elem_offset",
+           "pa_attention", "pa_write_kv_attention", "pa_write_kv_attention_noalloc",
+           "pa_noalloc_scratch_bytes", "pa_kv_cache_bytes", "pa_kv_elem_offset",
            "pa_status_string",
            "pa_last_error", "pa_profile_enable", "pa_profile_read",
            "pa_kv_manager_create", "pa_kv_manager_destroy", "pa_kv_manager_num_free_blocks",
@@ -70,6 +71,8 @@ def _load():
         "pa_attention": (i32, [pool_p, batch_p, P, i32, i32, f32, i32, P, P, C.c_size_t, P]),
         "pa_write_kv_attention": (i32, [pool_p, batch_p, P, P, P, i32, i32, f32, i32, P, P, P,
                                         C.c_size_t, P]),
+        "pa_write_kv_attention_noalloc": (i32, [pool_p, batch_p, P, P, P, i32, i32, f32, i32, P, P, P]),
+        "pa_noalloc_scratch_bytes": (C.c_size_t, []),
         "pa_kv_cache_bytes": (C.c_size_t, [pool_p]),
         "pa_kv_elem_offset": (i64, [pool_p, i32, i64, i32, i32, i32]),
         "pa_status_string": (C.c_char_p, [i32]),
@@ -294,6 +297,29 @@ def write_kv_attention(pool: KVPool, batch: Batch, query: torch.Tensor, key: tor
                                      int(causal), _ptr(slots), _ptr(out), _ptr(workspace),
                                      workspace.numel(), _stream(stream)))
     return out
+
+
+def write_kv_attention_noalloc(pool: KVPool, batch: Batch, query: torch.Tensor, key: torch.Tensor,
+                               value: torch.Tensor, num_q_heads: int, softmax_scale: float,
+                               causal: bool = True, out: Optional[torch.Tensor] = None,
+                               slots: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """pa_write_kv_attention_noalloc: the one call with the KV update, its
+    scratch in the library's static device array (no workspace)."""
+    assert query.is_contiguous() and key.is_contiguous() and value.is_contiguous()
+    assert key.dtype == query.dtype and value.dtype == query.dtype
+    assert slots is None or (slots.dtype == torch.int64 and slots.is_contiguous())
+    if out is None:
+        out = torch.empty_like(query)
+    p, b = pool.struct(), batch.struct()
+    _check(lib.pa_write_kv_attention_noalloc(C.byref(p), C.byref(b), _ptr(query), _ptr(key),
+                                             _ptr(value), torch_dtype_code(query), num_q_heads,
+                                             softmax_scale, int(causal), _ptr(slots), _ptr(out),
+                                             _stream(stream)))
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(lib.pa_noalloc_scratch_bytes())
 
 
 class KVManager:

@@ -179,6 +179,38 @@ struct StageGuard {
   }
 };
 
+// ------------------------------------------------------------ static scratch --
+// Scratch of pa_write_kv_attention_noalloc (for callers that cannot allocate):
+// the call's work lists and split-K partials live in this array instead of a
+// caller's workspace.  Each device holds its own copy from the time the
+// library's code object is loaded on it until the process ends.  In host code
+// `scratch` names a host-side stand-in, never the device array: its device
+// address is looked up once per device (hipGetSymbolAddress, with that device
+// current) and only that address is handed to kernels.
+
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void *g_scratch_dev[kMaxDevices];           // device address of `scratch`, per device
+
+static pa_status static_scratch(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(PA_ERR_UNSUPPORTED, "device %d beyond the %d the library supports", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void *ptr = nullptr;
+    if ((e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess) return hip_fail(e, "scratch address");
+    if (!ptr) return fail(PA_ERR_HIP, "scratch address is NULL");
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return PA_OK;
+}
+
 // ------------------------------------------------------------- side stream --
 // Prefill rows (MFMA) and decode rows (HBM-bound) of one step are
 // independent; with PA_OVERLAP=1 the extend kernel runs on a second stream,
@@ -955,10 +987,15 @@ struct KvUpdate {
   int64_t *slot_mapping;   // may be null
 };
 
+// no_alloc: the call's scratch is the library's static device array (the
+// workspace arguments are ignored), the work lists are copied into it by
+// kernels that carry them as arguments, and nothing is allocated (no
+// staging ring, no side stream).
 static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, const void *query,
                                 pa_dtype q_dtype, int32_t num_q_heads, float softmax_scale,
                                 int32_t causal, void *output, void *workspace,
-                                size_t workspace_bytes, hipStream_t s, const KvUpdate *kvu) {
+                                size_t workspace_bytes, hipStream_t s, const KvUpdate *kvu,
+                                bool no_alloc = false) {
   pa_status st = check_attention_args(pool, batch, q_dtype, num_q_heads, true);
   if (st != PA_OK) return st;
   if (batch->num_tokens > 0 && (!query || !output)) return fail(PA_ERR_INVALID_ARG, "NULL query/output");
@@ -973,6 +1010,13 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
 
   Plan plan;
   build_plan(*pool, *batch, num_q_heads, q_dtype, causal ? 1 : 0, kvu != nullptr, plan);
+  if (no_alloc) {
+    if (plan.bytes > kStaticScratchBytes)
+      return fail(PA_ERR_WORKSPACE, "batch needs %zu bytes of scratch, more than the %zu of the static scratch "
+                  "(pa_write_kv_attention with a workspace has no such limit)", plan.bytes, kStaticScratchBytes);
+    if ((st = static_scratch(&workspace)) != PA_OK) return st;
+    workspace_bytes = kStaticScratchBytes;
+  }
   if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL");
   if (((uintptr_t)workspace & 255) != 0) return fail(PA_ERR_WORKSPACE, "workspace not 256-byte aligned");
   if (workspace_bytes < plan.bytes)
@@ -998,7 +1042,7 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
     }
     if (!plan.wseg.empty()) memcpy(host + plan.off_wseg, plan.wseg.data(), plan.wseg.size() * sizeof(WriteSeg));
   };
-  if (plan_bytes && graph) {
+  if (plan_bytes && (graph || no_alloc)) {
     std::vector<char> host(plan_bytes);
     fill(host.data());
     hipError_t ce = launch_plan_copy(workspace, host.data(), plan_bytes, s);
@@ -1027,7 +1071,8 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
   hipStream_t xs = s;
   SideStream *side = nullptr;
   // (not with key pieces: their partials are merged on the caller's stream)
-  const bool fork = !plan.extw.empty() && plan.merge.empty() && !plan.dec.empty() && env_flag("PA_OVERLAP");
+  const bool fork = !no_alloc && !plan.extw.empty() && plan.merge.empty() && !plan.dec.empty() &&
+                    env_flag("PA_OVERLAP");
   if (fork && (st = side_stream(&side)) != PA_OK) return st;
 
   hipError_t e = hipSuccess;
@@ -1192,6 +1237,18 @@ pa_status pa_write_kv_attention(const pa_kv_pool *pool, const pa_batch *batch, c
   return attention_impl(pool, batch, query, q_dtype, num_q_heads, softmax_scale, causal, output,
                         workspace, workspace_bytes, (hipStream_t)stream, &kvu);
 }
+
+pa_status pa_write_kv_attention_noalloc(const pa_kv_pool *pool, const pa_batch *batch,
+                                        const void *query, const void *key, const void *value,
+                                        pa_dtype q_dtype, int32_t num_q_heads, float softmax_scale,
+                                        int32_t causal, int64_t *slot_mapping, void *output,
+                                        pa_stream_t stream) {
+  const KvUpdate kvu{key, value, slot_mapping};
+  return attention_impl(pool, batch, query, q_dtype, num_q_heads, softmax_scale, causal, output,
+                        nullptr, 0, (hipStream_t)stream, &kvu, true);
+}
+
+size_t pa_noalloc_scratch_bytes(void) { return kStaticScratchBytes; }
 
 pa_status pa_zero_blocks(const pa_kv_pool *pool, const int32_t *block_ids, int32_t num_ids,
                          pa_stream_t stream) {
