@@ -40,8 +40,12 @@
  *   are allowed; the workspace passed to pa_attention must not be shared by
  *   calls that may run concurrently.
  * - HIP graphs: every launching call may be captured into a HIP graph
- *   (stream capture).  pa_attention and pa_write_kv_attention then write
- *   their work lists into the workspace from inside the graph, so a replay
+ *   (stream capture).  pa_attention and pa_write_kv_attention then store
+ *   their work lists at capture in a pinned host arena of the library (8 MiB
+ *   per device, created by the first call on the device made outside
+ *   capture, never reused, kept until the process ends) that the graph's
+ *   kernels read at every replay; without room there, the lists are written
+ *   into the workspace by copy kernels inside the graph.  A replay
  *   recomputes the captured batch on the current contents of the device
  *   buffers.  The batch's shape (the host mirrors, num_tokens and the hint)
  *   is fixed at capture; the device arrays, the pool, query/key/value and

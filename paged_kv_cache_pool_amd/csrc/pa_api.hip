@@ -179,6 +179,64 @@ struct StageGuard {
   }
 };
 
+// -------------------------------------------------------- captured plans --
+// Work lists of calls captured into a HIP graph: written once, at capture,
+// into a pinned, device-mapped host arena that is never reused, so the
+// graph's kernels read them at every replay exactly as eager launches read
+// the staging ring (no copy nodes in the graph).  One arena per device,
+// created by the first call on that device made outside capture (allocation
+// is avoided while capturing), kept until the process ends; captured calls
+// take space from it until it is full, then fall back to copy kernels that
+// carry the lists as arguments into the workspace.
+
+constexpr size_t kArenaBytes = (size_t)8 << 20;
+
+struct PlanArena {
+  char *host = nullptr;
+  char *dev = nullptr;
+  size_t used = 0;
+  bool failed = false;                           // allocation failed once: do not retry
+};
+
+static std::mutex g_arena_mu;
+static PlanArena g_arena[64];
+
+// Outside capture: create this device's arena if it does not exist yet.
+static void arena_ensure() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return;
+  std::lock_guard<std::mutex> lk(g_arena_mu);
+  PlanArena &a = g_arena[dev];
+  if (a.host || a.failed) return;
+  void *h = nullptr, *d = nullptr;
+  if (hipHostMalloc(&h, kArenaBytes, hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess) {
+    a.failed = true;
+    return;
+  }
+  if (hipHostGetDevicePointer(&d, h, 0) != hipSuccess) {
+    (void)hipHostFree(h);
+    a.failed = true;
+    return;
+  }
+  a.host = (char *)h;
+  a.dev = (char *)d;
+}
+
+// Under capture: bytes of the arena for one call's lists (host and device
+// addresses), or false when there is no arena or no room.
+static bool arena_take(size_t bytes, char **host, const char **dev) {
+  int d = 0;
+  if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= 64) return false;
+  std::lock_guard<std::mutex> lk(g_arena_mu);
+  PlanArena &a = g_arena[d];
+  const size_t need = (bytes + 255) & ~(size_t)255;
+  if (!a.host || a.used + need > kArenaBytes) return false;
+  *host = a.host + a.used;
+  *dev = a.dev + a.used;
+  a.used += need;
+  return true;
+}
+
 // ------------------------------------------------------------ static scratch --
 // Scratch of pa_write_kv_attention_noalloc (for callers that cannot allocate):
 // the call's work lists and split-K partials live in this array instead of a
@@ -1024,8 +1082,10 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
 
   // the work lists: written into a staging slot that the kernels read
   // directly, or (PA_PLAN_UPLOAD=1) copied into the workspace.  Under graph
-  // capture they are written into the workspace by captured copy kernels
-  // that carry them as arguments, so the graph owns its plan.
+  // capture they are written once into the captured-plan arena, which the
+  // graph's kernels read at every replay (PA_GRAPH_PLAN_COPY=1, a full or
+  // absent arena, and the call that allocates nothing: copied into the
+  // workspace by captured copy kernels that carry them as arguments).
   const size_t plan_bytes = plan.off_ml;
   StageSlot *slot = nullptr;
   StageGuard guard;
@@ -1042,7 +1102,14 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
     }
     if (!plan.wseg.empty()) memcpy(host + plan.off_wseg, plan.wseg.data(), plan.wseg.size() * sizeof(WriteSeg));
   };
-  if (plan_bytes && (graph || no_alloc)) {
+  if (!graph && !no_alloc) arena_ensure();
+  char *arena_host = nullptr;
+  const char *arena_dev = nullptr;
+  if (plan_bytes && graph && !no_alloc && !env_flag("PA_GRAPH_PLAN_COPY") &&
+      arena_take(plan_bytes, &arena_host, &arena_dev)) {
+    fill(arena_host);                            // read by every replay of the graph
+    items = arena_dev;
+  } else if (plan_bytes && (graph || no_alloc)) {
     std::vector<char> host(plan_bytes);
     fill(host.data());
     hipError_t ce = launch_plan_copy(workspace, host.data(), plan_bytes, s);

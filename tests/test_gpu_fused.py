@@ -238,15 +238,19 @@ def test_spec_verify_workload(R, monkeypatch, min_rows):
 
 # ------------------------------------------------------------- HIP graphs --
 
+@pytest.mark.parametrize("plan_copy", ["", "1"])
 @pytest.mark.parametrize("cfg,fused", [(1, True), (1, False), (2, True), (6, True)])
-def test_graph_capture_replays(R, cfg, fused):
+def test_graph_capture_replays(R, monkeypatch, cfg, fused, plan_copy):
     """A step captured into a HIP graph (torch's stream capture around the
     library's calls) replays the same batch: every replay equals the eager
     step bit for bit, with unrelated eager steps of another batch (other
     pool, own plans) run between the replays, and both match the oracle; new
     query contents written between replays are read by the next replay, whose
-    output matches the oracle's for the new query."""
-    say("graph capture config", cfg, "fused", fused)
+    output matches the oracle's for the new query.  The captured work lists
+    live in the library's captured-plan arena, or (plan_copy) are copied
+    into the workspace by kernels inside the graph."""
+    monkeypatch.setenv("PA_GRAPH_PLAN_COPY", plan_copy)
+    say("graph capture config", cfg, "fused", fused, "plan copy", plan_copy)
     w = W.make(cfg)
     s = torch.cuda.Stream()
     step = R.GpuStep(w, stream=s, fused=fused)

@@ -168,14 +168,16 @@ def test_wide_default_large_prefill(R, monkeypatch):
     assert np.isfinite(got).all() and err <= TOL
 
 
+@pytest.mark.parametrize("plan_copy", ["", "1"])
 @pytest.mark.parametrize("fused", [True, False])
-def test_wide_pieces_graph_capture(R, monkeypatch, fused):
+def test_wide_pieces_graph_capture(R, monkeypatch, fused, plan_copy):
     """A step with wide items cut into two key pieces (so the merge runs too),
     captured into a HIP graph: every replay equals the eager step bit for bit,
     with an eager step of another batch between replays, and matches the
     oracle; a replay reads new query contents and matches the oracle for
     them."""
     monkeypatch.setenv("PA_WIDE_PIECES", "2")
+    monkeypatch.setenv("PA_GRAPH_PLAN_COPY", plan_copy)
     w = _chunk_batch("wide_graph", 4, 600, 1000, W.BF16)
     s = torch.cuda.Stream()
     step = R.GpuStep(w, stream=s, fused=fused)
