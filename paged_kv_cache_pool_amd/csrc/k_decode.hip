@@ -33,6 +33,7 @@ namespace pa {
 
 template <int KV, int D, int G>
 __global__ __launch_bounds__(256) void k_decode(const DecodeArgs a) {
+  const StagingRelease staging_release{a.release};
   constexpr int PB = KvTraits<KV>::bytes;     // pool element bytes
   constexpr int E = 16 / PB;                  // elements per 16-byte vector
   constexpr int NCH = D / E;                  // K chunks per key row

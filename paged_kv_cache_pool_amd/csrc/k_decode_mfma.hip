@@ -103,6 +103,7 @@ constexpr int kDecodeWaves = 1;                // waves (work units) per workgro
 
 template <int KV, int D, bool PAIR>
 __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(PAIR ? 1 : 2))) void k_decode_mfma(const DecodeArgs a) {
+  const StagingRelease staging_release{a.release};
   static_assert(KV == KV_BF16 || KV == KV_FP8, "bf16 and fp8 pools");
   constexpr bool F8 = KV == KV_FP8;
   constexpr int PB = KvTraits<KV>::bytes;

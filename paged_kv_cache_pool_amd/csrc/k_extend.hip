@@ -599,6 +599,7 @@ __device__ __forceinline__ void extend_split_body(const ExtendArgs &a, char *sme
 
 template <int KV, bool PREFIX>
 __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
+  const StagingRelease staging_release{a.release};
   extern __shared__ __attribute__((aligned(16))) char smem[];
   extend_split_body<KV, PREFIX>(a, smem);
 }
@@ -621,6 +622,7 @@ __global__ __launch_bounds__(512, 1) void k_extend(const ExtendArgs a) {
 // path: partitions of the key range merged by their maxima).
 template <int KV>
 __global__ __launch_bounds__(512, 1) void k_extend_wide(const ExtendArgs a) {
+  const StagingRelease staging_release{a.release};
   using X = XLayout<KV>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;

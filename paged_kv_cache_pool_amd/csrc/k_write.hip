@@ -100,6 +100,7 @@ __global__ __launch_bounds__(256) void k_write_kv(const void *__restrict__ key,
 // Used by the attention call that includes the KV update.
 template <int IN, int KV, int D>
 __global__ __launch_bounds__(256) void k_write_new(const WriteArgs a) {
+  const StagingRelease staging_release{a.release};
   constexpr int IB = KvTraits<IN>::bytes;
   constexpr int PB = KvTraits<KV>::bytes;
   constexpr int E = 16 / PB;                // elements per 16 bytes of the pool

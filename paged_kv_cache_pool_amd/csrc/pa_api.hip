@@ -108,42 +108,71 @@ static void prof_reset_locked() {
 // The plan of a step (work lists) is built on the host.  It is written into
 // a pinned, device-mapped host buffer that the kernels read directly (one
 // small read per wave or workgroup), so no copy is queued between the
-// caller's previous kernel and ours.  A buffer is reused only after the last
-// kernel that reads it has completed (checked with an event).  With
-// PA_PLAN_UPLOAD=1 the plan is instead copied into the caller's workspace.
-// One ring per device (events belong to the device they were created on).
+// caller's previous kernel and ours.  A buffer is reused only after every
+// kernel that reads it has completed.  No event is recorded per call (an
+// event between steps measured 3-5 us per step): the first kernel of the next
+// call on the same stream stores a release flag for the previous call's
+// buffer when it starts, and by then every earlier kernel of that stream has
+// completed.  A buffer whose stream saw no later call before the buffer is
+// needed again is waited for with a device synchronisation.  One ring of 16
+// buffers per device.  With PA_PLAN_UPLOAD=1 the plan is instead copied into
+// the caller's workspace.
+
+constexpr int kDevMax = 64;
+constexpr int kStageSlots = 16;
 
 struct StageSlot {
   void *host = nullptr;
   void *dev = nullptr;                           // device address of `host`
   size_t cap = 0;
-  hipEvent_t done = nullptr;
-  bool pending = false;
+  hipStream_t stream = nullptr;                  // stream of the call that used it last
+  bool pending = false;                          // that call's kernels may still read it
+  bool superseded = false;                       // a later call on that stream has been issued
+};
+
+struct StageRing {
+  StageSlot slot[kStageSlots];
+  unsigned next = 0;
+  volatile int32_t *flags = nullptr;             // pinned words, one per slot: 1 once released
+  int32_t *flags_dev = nullptr;                  // their device addresses
+  std::vector<std::pair<hipStream_t, int>> last; // stream -> the slot its last call used
 };
 
 static std::mutex g_stage_mu;
-static std::vector<std::vector<StageSlot>> g_stage;   // per device: 8 slots
-static std::vector<unsigned> g_stage_next;
+static StageRing g_stage[kDevMax];
 
-// A free slot of at least `bytes`; the caller fills slot->host, launches the
-// kernels that read slot->dev, then calls stage_release.
-static pa_status stage_acquire(size_t bytes, StageSlot **out) {
+// A free slot of at least `bytes` for a call on stream s.  *release: the
+// device address of the release flag of the previous call's slot on s
+// (null if there is none), which the call's first kernel must store 1 to.
+static pa_status stage_acquire(size_t bytes, hipStream_t s, StageSlot **out, int32_t **release) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kDevMax) return fail(PA_ERR_UNSUPPORTED, "device %d beyond the %d the library supports", dev, kDevMax);
   std::lock_guard<std::mutex> lk(g_stage_mu);
-  if ((int)g_stage.size() <= dev) {
-    g_stage.resize(dev + 1);
-    g_stage_next.resize(dev + 1, 0);
+  StageRing &R = g_stage[dev];
+  if (!R.flags) {
+    void *h = nullptr, *d = nullptr;
+    if ((e = hipHostMalloc(&h, kStageSlots * sizeof(int32_t), hipHostMallocMapped | hipHostMallocCoherent)) != hipSuccess)
+      return hip_fail(e, "staging flags");
+    if ((e = hipHostGetDevicePointer(&d, h, 0)) != hipSuccess) return hip_fail(e, "staging flags map");
+    memset(h, 0, kStageSlots * sizeof(int32_t));
+    R.flags = (volatile int32_t *)h;
+    R.flags_dev = (int32_t *)d;
   }
-  if (g_stage[dev].empty()) g_stage[dev].resize(8);
-  StageSlot &slot = g_stage[dev][g_stage_next[dev]++ % g_stage[dev].size()];
+  const int k = (int)(R.next++ % kStageSlots);
+  StageSlot &slot = R.slot[k];
   if (slot.pending) {
-    if ((e = hipEventSynchronize(slot.done)) != hipSuccess) return hip_fail(e, "staging wait");
+    bool released = R.flags[k] != 0;
+    if (!released && slot.superseded) {
+      // the next call on its stream has been issued: its first kernel sets
+      // the flag when it starts (bounded wait; the device synchronisation
+      // below covers a call whose launch failed)
+      for (int spin = 0; spin < (1 << 22) && !released; ++spin) released = R.flags[k] != 0;
+    }
+    if (!released && (e = hipDeviceSynchronize()) != hipSuccess) return hip_fail(e, "staging wait");
     slot.pending = false;
   }
-  if (!slot.done && (e = hipEventCreateWithFlags(&slot.done, hipEventDisableTiming)) != hipSuccess)
-    return hip_fail(e, "staging event");
   if (slot.cap < bytes) {
     if (slot.host) hipHostFree(slot.host);
     slot.host = slot.dev = nullptr;
@@ -156,28 +185,31 @@ static pa_status stage_acquire(size_t bytes, StageSlot **out) {
     if ((e = hipHostGetDevicePointer(&slot.dev, slot.host, 0)) != hipSuccess) return hip_fail(e, "staging map");
     slot.cap = cap;
   }
+  // the previous slot of this stream is released by this call's first kernel
+  *release = nullptr;
+  bool found = false;
+  for (auto &entry : R.last) {
+    if (entry.first != s) continue;
+    StageSlot &prev = R.slot[entry.second];
+    if (entry.second != k && prev.pending && !prev.superseded && prev.stream == s) {
+      prev.superseded = true;
+      *release = R.flags_dev + entry.second;
+    }
+    entry.second = k;
+    found = true;
+    break;
+  }
+  if (!found) {
+    if (R.last.size() >= 64) R.last.erase(R.last.begin());
+    R.last.push_back({s, k});
+  }
+  R.flags[k] = 0;
+  slot.stream = s;
+  slot.pending = true;
+  slot.superseded = false;
   *out = &slot;
   return PA_OK;
 }
-
-// Marks the slot busy until the work queued on `s` so far has completed
-// (recorded when the guard leaves scope, i.e. after every launch of the call,
-// on every return path).
-struct StageGuard {
-  StageSlot *slot = nullptr;
-  hipStream_t s = nullptr;
-  ~StageGuard() {
-    if (!slot) return;
-    std::lock_guard<std::mutex> lk(g_stage_mu);
-    if (hipEventRecord(slot->done, s) == hipSuccess) {
-      slot->pending = true;
-    } else {
-      // the event could not be queued: wait for the stream instead, so the
-      // buffer is not reused while kernels may still read it
-      (void)hipStreamSynchronize(s);
-    }
-  }
-};
 
 // -------------------------------------------------------- captured plans --
 // Work lists of calls captured into a HIP graph: written once, at capture,
@@ -199,12 +231,12 @@ struct PlanArena {
 };
 
 static std::mutex g_arena_mu;
-static PlanArena g_arena[64];
+static PlanArena g_arena[kDevMax];
 
 // Outside capture: create this device's arena if it does not exist yet.
 static void arena_ensure() {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevMax) return;
   std::lock_guard<std::mutex> lk(g_arena_mu);
   PlanArena &a = g_arena[dev];
   if (a.host || a.failed) return;
@@ -226,7 +258,7 @@ static void arena_ensure() {
 // addresses), or false when there is no arena or no room.
 static bool arena_take(size_t bytes, char **host, const char **dev) {
   int d = 0;
-  if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= 64) return false;
+  if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= kDevMax) return false;
   std::lock_guard<std::mutex> lk(g_arena_mu);
   PlanArena &a = g_arena[d];
   const size_t need = (bytes + 255) & ~(size_t)255;
@@ -247,7 +279,7 @@ static bool arena_take(size_t bytes, char **host, const char **dev) {
 // current) and only that address is handed to kernels.
 
 constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
-constexpr int kMaxDevices = 64;
+constexpr int kMaxDevices = kDevMax;
 static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 static std::mutex g_scratch_mu;
@@ -1088,7 +1120,7 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
   // workspace by captured copy kernels that carry them as arguments).
   const size_t plan_bytes = plan.off_ml;
   StageSlot *slot = nullptr;
-  StageGuard guard;
+  int32_t *release = nullptr;                    // set by the call's first kernel (staging ring)
   const char *items = (const char *)workspace;
   auto fill = [&](char *host) {
     memset(host, 0, plan_bytes);
@@ -1115,9 +1147,7 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
     hipError_t ce = launch_plan_copy(workspace, host.data(), plan_bytes, s);
     if (ce != hipSuccess) return hip_fail(ce, "plan copy launch");
   } else if (plan_bytes) {
-    if ((st = stage_acquire(plan_bytes, &slot)) != PA_OK) return st;
-    guard.slot = slot;
-    guard.s = s;
+    if ((st = stage_acquire(plan_bytes, s, &slot, &release)) != PA_OK) return st;
     char *host = (char *)slot->host;
     fill(host);
     if (env_flag("PA_PLAN_UPLOAD")) {
@@ -1160,6 +1190,8 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
     w.num_kv_heads = pool->num_kv_heads;
     w.k_scale = kscale;
     w.v_scale = vscale;
+    w.release = release;                         // the call's first kernel
+    release = nullptr;
     e = launch_write_new(*pool, q_dtype, w, s);
     if (e != hipSuccess) return hip_fail(e, "k_write_new launch");
   }
@@ -1198,6 +1230,8 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
       x.enc_k_scale = kscale;
       x.enc_v_scale = vscale;
     }
+    x.release = release;
+    release = nullptr;
     e = launch_extend_wide(*pool, x, xs);
     if (e != hipSuccess) return hip_fail(e, "k_extend_wide launch");
   }
@@ -1222,6 +1256,8 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
     x.scale_log2 = softmax_scale * log2e * kscale;
     x.k_scale = kscale;
     x.v_scale = vscale;
+    x.release = release;
+    release = nullptr;
     e = launch_prefix(*pool, x, s);
     if (e != hipSuccess) return hip_fail(e, "k_prefix launch");
   }
@@ -1260,6 +1296,8 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
       a.h0 = h0;
       a.g = std::min(g_max, g_total - h0);
       const int g_tmpl = a.g <= 1 ? 1 : a.g <= 2 ? 2 : a.g <= 4 ? 4 : a.g <= 8 ? 8 : 16;
+      a.release = release;
+      release = nullptr;
       e = launch_decode(*pool, q_dtype, a, g_tmpl, s);
       if (e != hipSuccess) return hip_fail(e, "k_decode launch");
       a.knew = a.vnew = nullptr;                  // rows written by the first launch

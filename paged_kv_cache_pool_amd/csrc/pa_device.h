@@ -6,6 +6,21 @@
 
 namespace pa {
 
+// The first kernel a call launches releases the staging buffer of the
+// previous call on its stream: while any of its workgroups runs, every
+// earlier kernel of the stream has completed.  The lanes of wave 0 of
+// workgroup 0 store the flag when they leave the kernel (the same value, a
+// wave-uniform condition; a vector store to pinned host memory at system
+// scope).  At the exit no load follows the store, so the compiler keeps
+// loading the kernel's uniform metadata through the scalar path.
+struct StagingRelease {
+  int32_t *flag;
+  __device__ __forceinline__ ~StagingRelease() {
+    if (flag != nullptr && blockIdx.x == 0 && __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0)
+      __hip_atomic_store(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+};
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 

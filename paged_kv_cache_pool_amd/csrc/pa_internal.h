@@ -56,6 +56,7 @@ struct WriteArgs {
   int32_t num_kv_heads;
   float k_scale;          // pool scales (fp8 encode), 1 otherwise
   float v_scale;
+  int32_t *release;       // or null: release flag of the stream's previous staging buffer
 };
 
 // Merge of the partials of one token: slots [first, first + count).
@@ -136,6 +137,7 @@ struct DecodeArgs {
   void *v_store;
   float enc_k_scale;      // pool scales for the fp8 encode, 1 otherwise
   float enc_v_scale;
+  int32_t *release;       // or null: release flag of the stream's previous staging buffer
 };
 
 struct MergeArgs {
@@ -180,6 +182,7 @@ struct ExtendArgs {
   void *v_store;
   float enc_k_scale;          // pool scales for the fp8 encode, 1 otherwise
   float enc_v_scale;
+  int32_t *release;           // or null: release flag of the stream's previous staging buffer
 };
 
 constexpr int kExtCols = 128;        // columns per extend workgroup (4 x 32, keys split over 2 waves)

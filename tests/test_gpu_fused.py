@@ -302,3 +302,38 @@ def test_graph_capture_rejects_validation(R, monkeypatch):
             step.run()
     assert e.value.status == 2
     torch.cuda.synchronize()
+
+
+def test_staging_ring_across_streams(R):
+    """The plan's staging buffers are reused after 16 calls: 48 calls that
+    alternate between two streams (two batches, the decode layer and a mixed
+    batch) and a third stream used once, with every call's output equal to
+    the same batch's first output bit for bit.  A buffer is released by the
+    next call on its own stream; the buffer of the stream used once is waited
+    for by a device synchronisation."""
+    say("staging ring across streams")
+    wa = W.llama8b_decode(seed=2, num_seqs=40, lo=100, hi=1500, num_blocks=4200)
+    wb = W.build("ring_b", 4, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                 num_blocks=90, kv_dtype=W.BF16, io_dtype=W.BF16, num_computed=[300, 40, 0, 77],
+                 num_scheduled=[1, 1, 120, 9])
+    sa, sb, sc = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    a = R.GpuStep(wa, stream=sa, fused=True)
+    b = R.GpuStep(wb, stream=sb, fused=True)
+    c = R.GpuStep(wb, stream=sc, fused=True)
+    a.run()
+    b.run()
+    c.run()
+    torch.cuda.synchronize()
+    ref_a, ref_b = a.out.clone(), b.out.clone()
+    assert torch.equal(c.out.view(torch.uint8), ref_b.view(torch.uint8))
+    _check_out(wa, a)
+    _check_out(wb, b)
+    for k in range(48):
+        (a if k % 2 == 0 else b).run()
+        if k % 8 == 7:
+            torch.cuda.synchronize()
+            assert torch.equal(a.out.view(torch.uint8), ref_a.view(torch.uint8)), k
+            assert torch.equal(b.out.view(torch.uint8), ref_b.view(torch.uint8)), k
+    torch.cuda.synchronize()
+    assert torch.equal(a.out.view(torch.uint8), ref_a.view(torch.uint8))
+    assert torch.equal(b.out.view(torch.uint8), ref_b.view(torch.uint8))
