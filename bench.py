@@ -587,6 +587,13 @@ def main():
         cpu = {"value": round(n_rows * reps / t_cpu, 2), "unit": "tokens/s", "cores": O.num_threads(),
                "kind": "oracle", "sample": f"{what}, {reps} repetition(s), {t_cpu:.1f}s, fp64"}
 
+    # dispatch placement the planners rely on (diagnostic, after the timed
+    # region): a fraction below 1 costs speed, never exactness
+    try:
+        placement = B.placement_check()
+    except B.PaError as e:
+        placement = {"error": str(e)}
+
     out = {
         "metric": "tokens/s per paged-attn step + decode KV GB/s (% of HBM peak), 1 MI355X",
         "value": round(tokens_per_s, 1),
@@ -619,6 +626,7 @@ def main():
            if other is not None else {}),
         **({"ms_per_step_graph_replay_warm": graph_ms} if graph_ms is not None else {}),
         "decode_kv_gbps": roof["achieved"] if dom == "k_decode" else None,
+        "placement": placement,
     }
     if dom == "k_decode":
         uniq = unique_kv_bytes(w, sl, qsl, prefix)

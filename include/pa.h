@@ -380,6 +380,34 @@ const char *pa_last_error(void);
 pa_status pa_profile_enable(int32_t enable);
 pa_status pa_profile_read(const char *kernel, int32_t *launches, double *total_ms);
 
+/* Placement check (diagnostic, for measurement; allocates, launches on the
+ * null stream and waits for the device).  The planners rely on dispatch
+ * placements that HIP does not promise; when one fails the results stay
+ * exact and only the speed suffers.  Three probe launches, shaped like the
+ * library's own, record each workgroup's hardware ids on the current device:
+ *   one_wave_alone:   4 x CUs one-wave workgroups using over 256 registers
+ *                     per lane (the matrix-core decode kernel's paired form,
+ *                     sized for one wave on every SIMD): fraction of them
+ *                     alone on their SIMD;
+ *   two_wave_paired:  8 x CUs one-wave workgroups of two waves per SIMD (its
+ *                     two-wave form): fraction of u < 4 x CUs whose partner
+ *                     u + 4 x CUs runs on u's SIMD;
+ *   xcd_round_robin:  2 x CUs 512-thread workgroups holding 160 KB of LDS
+ *                     (the extend kernels): fraction of workgroups b on XCD
+ *                     b % 8.
+ * compute_units and xcds (distinct XCD ids seen) describe the device.
+ * out: host struct, filled on PA_OK.  Errors: PA_ERR_INVALID_ARG (NULL out),
+ * PA_ERR_HIP (no device, or a launch or copy failed). */
+typedef struct pa_placement {
+  int32_t compute_units;
+  int32_t xcds;
+  float one_wave_alone;
+  float two_wave_paired;
+  float xcd_round_robin;
+} pa_placement;
+
+pa_status pa_placement_check(pa_placement *out);
+
 #ifdef __cplusplus
 }
 #endif

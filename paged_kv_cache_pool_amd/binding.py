@@ -34,7 +34,7 @@ EXPORTS = ["pa_prepare_metadata", "pa_slot_mapping", "pa_write_kv", "pa_attentio
            "pa_kv_manager_create", "pa_kv_manager_destroy", "pa_kv_manager_num_free_blocks",
            "pa_kv_manager_get_computed_blocks", "pa_kv_manager_allocate_slots",
            "pa_kv_manager_cache_blocks", "pa_kv_manager_free", "pa_kv_manager_block_ids",
-           "pa_kv_manager_ref_count", "pa_zero_blocks"]
+           "pa_kv_manager_ref_count", "pa_zero_blocks", "pa_placement_check"]
 
 
 class PaError(RuntimeError):
@@ -55,6 +55,11 @@ class PaBatch(C.Structure):
                 ("block_table", C.c_void_p), ("bt_stride", C.c_int32),
                 ("query_start_loc_host", C.c_void_p), ("seq_lens_host", C.c_void_p),
                 ("num_common_prefix_blocks", C.c_int32)]
+
+
+class PaPlacement(C.Structure):
+    _fields_ = [("compute_units", C.c_int32), ("xcds", C.c_int32), ("one_wave_alone", C.c_float),
+                ("two_wave_paired", C.c_float), ("xcd_round_robin", C.c_float)]
 
 
 def _load():
@@ -89,6 +94,7 @@ def _load():
         "pa_kv_manager_block_ids": (i32, [P, i64, P, i32, C.POINTER(i32)]),
         "pa_kv_manager_ref_count": (i32, [P, i32, C.POINTER(i32)]),
         "pa_zero_blocks": (i32, [pool_p, P, i32, P]),
+        "pa_placement_check": (i32, [C.POINTER(PaPlacement)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -402,6 +408,17 @@ def profile_read(kernel: str):
     ms = C.c_double(0)
     _check(lib.pa_profile_read(kernel.encode(), C.byref(n), C.byref(ms)))
     return int(n.value), float(ms.value)
+
+
+def placement_check() -> dict:
+    """Dispatch placement on the current device (pa_placement_check): the
+    fractions of probe workgroups placed as the planners assume."""
+    r = PaPlacement()
+    _check(lib.pa_placement_check(C.byref(r)))
+    return {"compute_units": int(r.compute_units), "xcds": int(r.xcds),
+            "one_wave_alone": round(float(r.one_wave_alone), 4),
+            "two_wave_paired": round(float(r.two_wave_paired), 4),
+            "xcd_round_robin": round(float(r.xcd_round_robin), 4)}
 
 
 def status_string(code: int) -> str:

@@ -15,7 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(OUT_DIR, "libpa.so")
-SOURCES = ["pa_api.hip", "k_write.hip", "k_decode.hip", "k_decode_mfma.hip", "k_extend.hip", "kv_manager.cpp"]
+SOURCES = ["pa_api.hip", "k_write.hip", "k_decode.hip", "k_decode_mfma.hip", "k_extend.hip", "k_probe.hip",
+           "kv_manager.cpp"]
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
 

@@ -11,7 +11,9 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <map>
 #include <mutex>
+#include <set>
 #include <string>
 #include <vector>
 
@@ -1421,6 +1423,51 @@ pa_status pa_profile_read(const char *kernel, int32_t *launches, double *total_m
   }
   *launches = n;
   *total_ms = ms;
+  return PA_OK;
+}
+
+pa_status pa_placement_check(pa_placement *out) {
+  if (!out) return fail(PA_ERR_INVALID_ARG, "NULL argument");
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "placement check: device");
+  if (cus <= 0) return fail(PA_ERR_HIP, "placement check: no compute units");
+  const size_t n_one = 4 * (size_t)cus, n_two = 8 * (size_t)cus, n_wide = 2 * (size_t)cus;
+  const size_t n_all = 2 * (n_one + n_two + n_wide);
+  uint32_t *ids = nullptr;
+  if ((e = hipMalloc((void **)&ids, n_all * sizeof(uint32_t))) != hipSuccess) return hip_fail(e, "placement check: alloc");
+  std::vector<uint32_t> h(n_all);
+  uint32_t *one = ids, *two = one + 2 * n_one, *wide = two + 2 * n_two;
+  e = launch_placement_probe(cus, one, two, wide, nullptr);
+  if (e == hipSuccess) e = hipMemcpy(h.data(), ids, n_all * sizeof(uint32_t), hipMemcpyDeviceToHost);
+  hipFree(ids);
+  if (e != hipSuccess) return hip_fail(e, "placement check: probe");
+  // a SIMD: XCD id, and HW_ID's SIMD (bits 5:4) and CU / array / engine
+  // fields (bits 15:8); the wave slot and queue pipe fields are left out
+  auto simd = [&](const uint32_t *r, size_t u) -> uint64_t {
+    const uint32_t hw = r[2 * u], xcc = r[2 * u + 1] & 0xF;
+    return ((uint64_t)xcc << 16) | (((hw >> 8) & 0xFF) << 2) | ((hw >> 4) & 3);
+  };
+  std::map<uint64_t, int> per_simd;
+  for (size_t u = 0; u < n_one; ++u) ++per_simd[simd(h.data() + 0, u)];
+  size_t alone = 0;
+  for (size_t u = 0; u < n_one; ++u) alone += per_simd[simd(h.data(), u)] == 1;
+  const uint32_t *h2 = h.data() + 2 * n_one, *hw3 = h2 + 2 * n_two;
+  size_t paired = 0;
+  for (size_t u = 0; u < n_one; ++u) paired += simd(h2, u) == simd(h2, u + n_one);
+  size_t rr = 0;
+  std::set<uint32_t> xcds;
+  for (size_t b = 0; b < n_wide; ++b) {
+    const uint32_t x = hw3[2 * b + 1] & 0xF;
+    xcds.insert(x);
+    rr += x == b % 8;
+  }
+  out->compute_units = cus;
+  out->xcds = (int32_t)xcds.size();
+  out->one_wave_alone = (float)alone / (float)n_one;
+  out->two_wave_paired = (float)paired / (float)n_one;
+  out->xcd_round_robin = (float)rr / (float)n_wide;
   return PA_OK;
 }
 

@@ -208,6 +208,11 @@ hipError_t launch_prefix(const pa_kv_pool &p, const ExtendArgs &a, hipStream_t s
 // Records the error detail for pa_last_error() and returns `st`.
 pa_status pa_set_error(pa_status st, const char *fmt, ...);
 
+// Placement probe: 4 x cus, 8 x cus and 2 x cus workgroups, each writing its
+// (HW_ID, XCC_ID) pair at ids[2 * workgroup].
+hipError_t launch_placement_probe(int cus, uint32_t *one_ids, uint32_t *two_ids, uint32_t *wide_ids,
+                                  hipStream_t s);
+
 hipError_t launch_zero_blocks(const pa_kv_pool &p, const int32_t *block_ids, int32_t n, hipStream_t s);
 
 // Kernel timing hooks (no-ops unless profiling is enabled).
