@@ -3,12 +3,13 @@
 Each step follows the scheduler and model-runner passes of "vLLM 推理流程分析":
   * schedule (§4.2-4.3): running requests first, each with its next tokens
     (one for a decode, the rest of the prompt up to the token budget for a
-    chunked prefill), through allocate_slots; when the pool is short of
-    blocks the most recently admitted running request is preempted (its
-    blocks freed, its progress dropped) and the allocation retried.  Then
-    waiting requests, each looked up in the prefix cache
-    (get_computed_blocks) and admitted while the token budget and the pool
-    allow;
+    chunked prefill), through allocate_slots.  Then waiting requests, each
+    looked up in the prefix cache (get_computed_blocks) and admitted while
+    the token budget and the pool allow.  A request is admitted only when
+    the free blocks cover its whole length (prompt and new tokens) on top of
+    what the running requests may still take, so a running request's
+    allocation never fails and no request is ever preempted (preemption is
+    control plane, left out);
   * execute (§5.1.1-5.1.3, §6): the newly allocated blocks are zeroed, the
     batch metadata (query_start_loc, seq_lens, the block table) is built on
     the host and copied to the device, and the one-call step writes the new
@@ -59,7 +60,6 @@ class Request:
     num_computed: int = 0
     generated: int = 0
     status: str = "waiting"
-    preemptions: int = 0
 
     def __post_init__(self):
         if not self.tokens:
@@ -83,7 +83,6 @@ class StepPlan:
     block_table: np.ndarray       # [N][width], -1 past each request's blocks
     new_blocks: List[int]         # new_block_ids_to_zero
     prefix_hits: Dict[int, int]   # request -> hit blocks, for requests admitted this step
-    preempted: List[int]
     query: np.ndarray             # [T][Hq][D] io dtype (bf16 bits or float32)
     key: np.ndarray               # [T][Hkv][D]
     value: np.ndarray
@@ -110,9 +109,13 @@ class ServingLoop:
         self.running: List[int] = []
         self.finished: List[int] = []
         self.steps = 0
+        self.admission_waits = 0      # steps whose admission stopped for want of blocks
 
     # ------------------------------------------------------------ requests --
     def add_request(self, req: Request) -> None:
+        if self._total_blocks(req) > self.pool.num_blocks:
+            raise ValueError(f"request {req.req_id} needs {self._total_blocks(req)} blocks, "
+                             f"the pool has {self.pool.num_blocks}")
         self.requests[req.req_id] = req
         self.waiting.append(req.req_id)
 
@@ -133,14 +136,15 @@ class ServingLoop:
         return q, k, v
 
     # ------------------------------------------------------------ schedule --
-    def _preempt(self, rid: int, preempted: List[int]) -> None:
-        req = self.requests[rid]
-        self.manager.free(rid)
-        self.running.remove(rid)
-        req.status, req.num_computed = "waiting", 0
-        req.preemptions += 1
-        self.waiting.insert(0, rid)
-        preempted.append(rid)
+    def _total_blocks(self, req: Request) -> int:
+        # blocks of the request's whole length (an upper bound: the last new
+        # token is never computed)
+        return -(-(len(req.prompt) + req.max_new_tokens) // self.S)
+
+    def _outstanding(self) -> int:
+        # blocks the running requests may still allocate
+        return sum(max(0, self._total_blocks(self.requests[r]) - len(self.manager.block_ids(r)))
+                   for r in self.running)
 
     def schedule(self) -> Optional[StepPlan]:
         budget = self.budget
@@ -148,7 +152,6 @@ class ServingLoop:
         nsched: Dict[int, int] = {}
         new_blocks: List[int] = []
         hits_of: Dict[int, int] = {}
-        preempted: List[int] = []
         # running requests (decodes and unfinished chunked prefills)
         i = 0
         while i < len(self.running) and budget > 0:
@@ -158,31 +161,29 @@ class ServingLoop:
             if n <= 0:
                 i += 1
                 continue
-            while True:
-                new = self.manager.allocate_slots(rid, req.num_computed + n)
-                if new is not None:
-                    break
-                victim = self.running[-1]
-                self._preempt(victim, preempted)
-                if victim == rid:
-                    break
-            if rid not in self.running:
-                break
+            new = self.manager.allocate_slots(rid, req.num_computed + n)
+            if new is None:
+                raise RuntimeError(f"request {rid}: no free block although its blocks were reserved")
             new_blocks += new
             sched.append(rid)
             nsched[rid] = n
             budget -= n
             i += 1
-        # waiting requests (new, or preempted and recomputed from the start)
-        while self.waiting and budget > 0 and len(self.running) < self.max_num_seqs and not preempted:
+        # waiting requests, admitted while their whole length fits (hit
+        # blocks counted as new: a hit on a free cached block takes it from
+        # the free queue)
+        while self.waiting and budget > 0 and len(self.running) < self.max_num_seqs:
             rid = self.waiting[0]
             req = self.requests[rid]
+            if self._total_blocks(req) > self.manager.num_free_blocks() - self._outstanding():
+                self.admission_waits += 1
+                break
             hits = self.manager.get_computed_blocks(req.tokens, req.extra_key) if self.prefix_cache else []
             computed = len(hits) * self.S
             n = min(len(req.tokens) - computed, budget)
             new = self.manager.allocate_slots(rid, computed + n, hits)
             if new is None:
-                break
+                raise RuntimeError(f"request {rid}: no free block although the admission check passed")
             self.waiting.pop(0)
             self.running.append(rid)
             req.status, req.num_computed = "running", computed
@@ -193,9 +194,9 @@ class ServingLoop:
             budget -= n
         if not sched:
             return None
-        return self._build(sched, nsched, new_blocks, hits_of, preempted)
+        return self._build(sched, nsched, new_blocks, hits_of)
 
-    def _build(self, sched, nsched, new_blocks, hits_of, preempted) -> StepPlan:
+    def _build(self, sched, nsched, new_blocks, hits_of) -> StepPlan:
         nc = np.array([self.requests[r].num_computed for r in sched], np.int32)
         ns = np.array([nsched[r] for r in sched], np.int32)
         qsl, sl = B.prepare_metadata(nc, ns)
@@ -211,8 +212,7 @@ class ServingLoop:
         q, k, v = (np.concatenate(x) for x in (qs, ks, vs))
         if self.io_dtype == BF16:
             q, k, v = (f32_to_bf16_bits(x) for x in (q, k, v))
-        return StepPlan(list(sched), nc, ns, qsl, sl, bt, list(new_blocks), dict(hits_of),
-                        list(preempted), q, k, v)
+        return StepPlan(list(sched), nc, ns, qsl, sl, bt, list(new_blocks), dict(hits_of), q, k, v)
 
     # ------------------------------------------------------------- execute --
     def _dev(self, a: np.ndarray) -> torch.Tensor:

@@ -1,7 +1,8 @@
 """A shared continuous-batching scenario for the serving-loop tests: twelve
 requests built on three system prompts (so later requests hit the prefix
 cache), two extra keys, prompts of 18..130 tokens, 2..10 new tokens each,
-a 30-block pool of 16-token blocks (small enough to force preemption), a
+a 30-block pool of 16-token blocks (too small to admit every request at
+once, so admission waits for blocks), a
 128-token budget and at most 8 running requests."""
 import numpy as np
 

@@ -1,8 +1,10 @@
 """The continuous-batching loop's host side (scheduling, the block pool,
 metadata), dry-run on the CPU: every step's batch passes the oracle's
 metadata checks, new tokens go to distinct slots in their own request's
-blocks, the token budget and the running-request cap hold, prefix hits and
-preemptions happen, and every request finishes with all blocks returned."""
+blocks, the token budget and the running-request cap hold, prefix hits
+happen, admission waits for blocks (the pool cannot hold every request at
+once) without any running request running out, and every request finishes
+with all blocks returned."""
 import numpy as np
 import pytest
 
@@ -19,7 +21,7 @@ def test_dry_run_scenario():
     loop = serve.ServingLoop(pool, device="cpu", **SC.LOOP)
     for r in SC.requests():
         loop.add_request(r)
-    hits = preempts = steps = 0
+    hits = steps = 0
     while not loop.done():
         plan = loop.schedule()
         assert plan is not None, "nothing schedulable while requests remain"
@@ -38,14 +40,21 @@ def test_dry_run_scenario():
                 assert int(s) // 16 in own
         assert plan.query.shape == (T, SC.LOOP["num_q_heads"], 128)
         hits += sum(plan.prefix_hits.values())
-        preempts += len(plan.preempted)
         loop.commit(plan)
     assert sorted(loop.finished) == list(range(12))
     assert loop.manager.num_free_blocks() == SC.POOL["num_blocks"]
-    assert hits > 0 and preempts > 0, (hits, preempts)
+    assert hits > 0 and loop.admission_waits > 0, (hits, loop.admission_waits)
     for r in loop.requests.values():
         assert r.generated == r.max_new_tokens
         assert len(r.tokens) == len(r.prompt) + r.max_new_tokens
+
+
+def test_request_longer_than_pool_refused():
+    pool = B.KVPool.allocate(4, 16, 2, 64, "bf16", device="cpu")
+    loop = serve.ServingLoop(pool, num_q_heads=4, device="cpu")
+    with pytest.raises(ValueError):
+        loop.add_request(serve.Request(0, list(range(60)), 5))
+    loop.add_request(serve.Request(1, list(range(59)), 5))
 
 
 def test_same_prefix_same_rows():
