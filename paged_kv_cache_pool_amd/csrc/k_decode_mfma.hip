@@ -101,11 +101,19 @@ __device__ __forceinline__ float sum_x32(float x) {
 
 constexpr int kDecodeWaves = 1;                // waves (work units) per workgroup
 
-template <int KV, int D, bool PAIR>
-__global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(PAIR ? 1 : 2))) void k_decode_mfma(const DecodeArgs a) {
+// NH: column halves.  A launch whose items have at most 16 (row, head)
+// columns runs NH = 1; items of up to 32 columns (kind 1) run NH = 2, where
+// every K and V operand feeds two products (columns 0-15 and 16-31) and each
+// half keeps its own softmax state.  (With NH = 2 the paired form does not
+// pre-read the second item's first step: the registers go to the second
+// half.)
+template <int KV, int D, bool PAIR, int NH>
+__global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(PAIR || NH == 2 ? 1 : 2))) void k_decode_mfma(const DecodeArgs a) {
   const StagingRelease staging_release{a.release};
   static_assert(KV == KV_BF16 || KV == KV_FP8, "bf16 and fp8 pools");
+  static_assert(NH == 1 || NH == 2, "one or two column halves");
   constexpr bool F8 = KV == KV_FP8;
+  constexpr bool PREFETCH = PAIR && NH == 1;     // the second item's first step read at the start
   constexpr int PB = KvTraits<KV>::bytes;
   constexpr int E = 16 / PB;                     // elements per 16-byte K chunk row
   constexpr int TILE = D * kBlock * PB;          // bytes per (block, head) tile
@@ -117,19 +125,18 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   static_assert(NS >= 2 && NKX >= 1, "head_dim 64 or 128");
 
   const int lane = threadIdx.x & 63;
-  const int r = lane & 15;                       // MFMA column (head) / A-operand row
+  const int r = lane & 15;                       // MFMA column within a half / A-operand row
   const int j = lane >> 4;                       // lane group
   const int wave = uniform(threadIdx.x >> 6);
   const int unit = blockIdx.x * kDecodeWaves + wave;
   // PAIR: wave (bin, kv head) runs item bin, then item pair_stride + bin when
-  // there is one (its first step's K/V read at the start, so the second
-  // item starts without waiting).  Otherwise one item per wave.
+  // there is one.  Otherwise one item per wave.
   const int n_first = PAIR ? a.pair_stride : a.n_items;
   if (unit >= n_first * a.num_kv_heads) return;
   const int bin = unit / a.num_kv_heads;
   const int kvh = unit - bin * a.num_kv_heads;
   const int g = a.g;
-  const int qh0 = kvh * a.g_total + a.h0;        // head of column 0
+  const int qh0 = kvh * a.g_total + a.h0;        // q head of a column with head index 0
   const char *__restrict__ kbase = (const char *)a.k_cache + (int64_t)kvh * TILE;
   const char *__restrict__ vbase = (const char *)a.v_cache + (int64_t)kvh * TILE;
   const int64_t bstride = (int64_t)a.num_kv_heads * TILE;   // bytes between blocks
@@ -179,33 +186,55 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   };
 
 
-  // One item: keys [kv_begin, kv_last) of one token.  pre: its first step's
+  // One item: keys [kv_begin, kv_last) of its rows.  pre: its first step's
   // K/V are already in kr / vr, from the block ids b0 .. b3 (next: idv_next).
   auto run = [&](const int item_idx, const bool pre, int b0, int b1, int b2, int b3, int idv_next) {
     const DecodeItem item = a.items[item_idx];
     const int token = uniform(item.token), req = uniform(item.req);
     const int kv_begin = uniform(item.kv_begin), kv_end = uniform(item.kv_end);
     const int part = uniform(item.part);
-    const int wpos = uniform(item.wpos);
+    const int aux = uniform(item.wpos);
+    const int kind = uniform((int)item.kind);
+    const int ntok = kind == 0 ? 1 : uniform((int)item.ntok);
+    const int stride = uniform(item.stride);
+    const int wpos = kind == 0 ? aux : -1;
     const bool wnew = wpos >= 0 && a.knew != nullptr;
     const int kv_last = wnew ? kv_end - 1 : kv_end;   // end of the keys read from the pool
     const int32_t *__restrict__ btrow = a.block_table + (int64_t)req * a.bt_stride;
-    // ---- Q^T operand: column r = head qh0 + r (zero past g) ----
-    // (columns past g are cleared with a mask, not a branch: a branch around
+    // ---- columns: lane column 16 hf + r of half hf is (row ct, head ch) ----
+    const bool rows_causal = kind == 1 && a.causal != 0;
+    int ct[NH], ch[NH], clim[NH];
+    bool cval[NH];
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf) {
+      const int n = 16 * hf + r;
+      const int t = n / g;
+      cval[hf] = t < ntok;
+      ct[hf] = cval[hf] ? t : 0;
+      ch[hf] = cval[hf] ? n - t * g : 0;
+      // key limit of the column's row (exclusive)
+      clim[hf] = rows_causal ? aux - (ntok - 1 - ct[hf]) : kv_last;
+    }
+    // keys from which some column can be cut off (the masked steps start there)
+    const int cut = rows_causal ? min(kv_last, aux - (ntok - 1)) : kv_last;
+    // ---- Q^T operand of each half: column r = (row ct, head ch) (zero when invalid) ----
+    // (invalid columns are cleared with a mask, not a branch: a branch around
     // a loaded register makes the compiler wait for each load in turn)
-    bf16x8_t qop[NS];
-    {
+    bf16x8_t qop[NH][NS];
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf) {
       const uint16_t *qrow =
-          (const uint16_t *)a.q + ((int64_t)token * a.num_q_heads + qh0 + (r < g ? r : 0)) * D;
+          (const uint16_t *)a.q + ((int64_t)(token + ct[hf]) * a.num_q_heads + qh0 + ch[hf]) * D;
       uint4 v[NS];
-  #pragma unroll
+#pragma unroll
       for (int c = 0; c < NS; ++c) v[c] = *(const uint4 *)(qrow + qdim(c));
-      const uint32_t qm = r < g ? ~0u : 0u;
-  #pragma unroll
-      for (int c = 0; c < NS; ++c) qop[c] = as_bf16x8(make_uint4(v[c].x & qm, v[c].y & qm, v[c].z & qm, v[c].w & qm));
+      const uint32_t qm = cval[hf] ? ~0u : 0u;
+#pragma unroll
+      for (int c = 0; c < NS; ++c)
+        qop[hf][c] = as_bf16x8(make_uint4(v[c].x & qm, v[c].y & qm, v[c].z & qm, v[c].w & qm));
     }
 
-    // ---- the new key's inputs ----
+    // ---- the new key's inputs (kind 0) ----
     uint4 kin[NS];
     uint2 vin[NDG];
     int wblk = -1;
@@ -213,9 +242,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
       const int64_t th = (int64_t)token * a.num_kv_heads + kvh;
       const uint16_t *krow = (const uint16_t *)a.knew + th * D;
       const uint16_t *vrow = (const uint16_t *)a.vnew + th * D;
-  #pragma unroll
+#pragma unroll
       for (int c = 0; c < NS; ++c) kin[c] = *(const uint4 *)(krow + qdim(c));
-  #pragma unroll
+#pragma unroll
       for (int dg = 0; dg < NDG; ++dg) vin[dg] = *(const uint2 *)(vrow + dg * 16 + 4 * j);
       wblk = uniform(btrow[wpos / kBlock]);
     }
@@ -229,38 +258,43 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
       const int id = btrow[bi < last_bi ? bi : last_bi];
       return bi <= last_bi ? id : -1;
     };
-    float m_run = -INFINITY, l_run = 0.0f;         // head r; l_run: this lane's keys only
-    f32x4_t o[NDG];
-  #pragma unroll
-    for (int dg = 0; dg < NDG; ++dg) o[dg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    float m_run[NH], l_run[NH];                    // per half, column r; l_run: this lane's keys only
+    f32x4_t o[NH][NDG];
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf) {
+      m_run[hf] = -INFINITY;
+      l_run[hf] = 0.0f;
+#pragma unroll
+      for (int dg = 0; dg < NDG; ++dg) o[hf][dg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
 
-    // ---- the new key: first softmax step, then its rows into the pool ----
+    // ---- the new key (kind 0, half 0): first softmax step, then its rows into the pool ----
     if (wnew && kvh == 0 && lane == 0 && a.slots_out)
       a.slots_out[token] = (int64_t)wblk * kBlock + wpos % kBlock;
     if (wnew && wblk >= 0 && wblk < a.num_blocks) {
       uint32_t kb[NS][8];
       float sp = 0.0f;
-  #pragma unroll
+#pragma unroll
       for (int c = 0; c < NS; ++c) {
         const uint32_t w[4] = {kin[c].x, kin[c].y, kin[c].z, kin[c].w};
-  #pragma unroll
+#pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint32_t raw = (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
           kb[c][e] = pool_bits<KV_BF16, KV>(raw, a.enc_k_scale);
-          sp = fmaf((float)qop[c][e], pool_value<KV>(kb[c][e]), sp);
+          sp = fmaf((float)qop[0][c][e], pool_value<KV>(kb[c][e]), sp);
         }
       }
       sp = sum_x32(sum_x16(sp));
-      m_run = sp * a.scale_log2;
-      l_run = j == 0 ? 1.0f : 0.0f;
+      m_run[0] = sp * a.scale_log2;
+      l_run[0] = j == 0 ? 1.0f : 0.0f;
       uint32_t vb[NDG][4];
-  #pragma unroll
+#pragma unroll
       for (int dg = 0; dg < NDG; ++dg) {
         const uint32_t w[2] = {vin[dg].x, vin[dg].y};
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 4; ++i) {
           vb[dg][i] = pool_bits<KV_BF16, KV>((w[i >> 1] >> (16 * (i & 1))) & 0xffffu, a.enc_v_scale);
-          o[dg][i] = pool_value<KV>(vb[dg][i]);
+          o[0][dg][i] = pool_value<KV>(vb[dg][i]);
         }
       }
       // K element d of slot off sits at (d / E) * 256 + off * 16 + (d % E) * PB
@@ -268,7 +302,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
       const int off = wpos % kBlock;
       char *kt = (char *)a.k_store + ((int64_t)wblk * a.num_kv_heads + kvh) * TILE;
       char *vt = (char *)a.v_store + ((int64_t)wblk * a.num_kv_heads + kvh) * TILE;
-  #pragma unroll
+#pragma unroll
       for (int c = 0; c < NS; ++c) {
         if (r == c) {
           const int d0 = qdim(c);
@@ -288,10 +322,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
           }
         }
       }
-  #pragma unroll
+#pragma unroll
       for (int dg = 0; dg < NDG; ++dg) {
         if (r == dg) {
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < 4; ++i) {
             char *vd = vt + ((dg * 16 + 4 * j + i) * kBlock + off) * PB;
             if constexpr (F8) *(uint8_t *)vd = (uint8_t)vb[dg][i];
@@ -299,6 +333,30 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
           }
         }
       }
+    }
+
+    // ---- kind 1, attention with the KV update: the piece holding the rows'
+    // own keys (positions aux - ntok .. aux - 1; the plan puts all of them in
+    // the last piece, which ends at aux) stores the rows' K/V into the pool
+    // first, and its key loop then reads them like any other key.  No other
+    // wave reads those slots in this launch.
+    if (kind == 1 && a.knew != nullptr && kv_end == aux) {
+      constexpr int NCH = D / E;                 // 16-byte pool chunks per row
+      for (int w = lane; w < ntok * NCH; w += 64) {
+        const int t = w / NCH, chn = w - t * NCH;
+        const int pos = aux - ntok + t;
+        const int wb = btrow[pos / kBlock];
+        const int off = pos % kBlock;
+        if (chn == 0 && kvh == 0 && a.slots_out) a.slots_out[token + t] = (int64_t)wb * kBlock + off;
+        if (wb < 0 || wb >= a.num_blocks) continue;   // slot outside the pool: not written
+        const int64_t th = (int64_t)(token + t) * a.num_kv_heads + kvh;
+        const KvChunkIn<KV_BF16, KV> in =
+            load_kv_chunk<KV_BF16, KV>((const char *)a.knew + th * D * 2, (const char *)a.vnew + th * D * 2, chn);
+        store_kv_chunk<KV_BF16, KV, D>(in, a.k_store, a.v_store, ((int64_t)wb * a.num_kv_heads + kvh) * TILE, off, chn,
+                                       a.enc_k_scale, a.enc_v_scale);
+      }
+      __builtin_amdgcn_s_waitcnt(0);             // every store of this wave has completed
+      asm volatile("" ::: "memory");             // and no read below moves above them
     }
 
     // ---- the first step's K/V ----
@@ -315,14 +373,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     // ---- key loop ----
     for (int it = kv_begin; it < kv_last; it += kKeysPerIter) {
       const int idv_next2 = ids_of(it + 2 * kKeysPerIter);
-      const bool slow = it + kKeysPerIter > kv_last || (b0 | b1 | b2 | b3) < 0;
+      const bool slow = it + kKeysPerIter > cut || (b0 | b1 | b2 | b3) < 0;
 
-      // S products
-      f32x4_t s[4];
-  #pragma unroll
+      // S products (each K operand feeds every half)
+      f32x4_t s[NH][4];
+#pragma unroll
       for (int u = 0; u < 4; ++u) {
-        s[u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  #pragma unroll
+#pragma unroll
+        for (int hf = 0; hf < NH; ++hf) s[hf][u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
         for (int c = 0; c < NS; ++c) {
           bf16x8_t kop;
           if constexpr (F8) {
@@ -331,7 +390,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
           } else {
             kop = as_bf16x8(kr[u][c]);
           }
-          s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[c], s[u], 0, 0, 0);
+#pragma unroll
+          for (int hf = 0; hf < NH; ++hf)
+            s[hf][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[hf][c], s[hf][u], 0, 0, 0);
         }
       }
 
@@ -342,73 +403,84 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
       issue_k(kr, n0, n1, n2, n3);
 
       // valid keys of this lane: positions it + 32 c + 8 j + e, e < nv[c]
+      // (and, per column, e < cl[hf][c]: the row's causal limit)
       int nv[2] = {8, 8};
+      int cl[NH][2];
+#pragma unroll
+      for (int hf = 0; hf < NH; ++hf) cl[hf][0] = cl[hf][1] = 8;
       if (slow) {
-  #pragma unroll
+#pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
           const int p = c2 == 0 ? pick(vsel, b0, b1) : pick(vsel, b2, b3);
           const int lim = kv_last - (it + 32 * c2 + 8 * j);
           nv[c2] = p < 0 ? 0 : lim < 0 ? 0 : lim > 8 ? 8 : lim;
+#pragma unroll
+          for (int hf = 0; hf < NH; ++hf) cl[hf][c2] = clim[hf] - (it + 32 * c2 + 8 * j);
         }
       }
 
-      // online softmax (log2 units); S element i of product 2c + h is key 4h + i of chunk c
-      float sc[4][4];
-      float mx = -INFINITY;
-  #pragma unroll
-      for (int u = 0; u < 4; ++u)
-  #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = s[u][i] * a.scale_log2;
-          if (slow && 4 * (u & 1) + i >= nv[u >> 1]) v = -INFINITY;
-          sc[u][i] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = max_x32(max_x16(mx));
-      const float mn = fmaxf(m_run, mx);
-      const float mu = mn == -INFINITY ? 0.0f : mn;   // no key yet: every p and alpha is 0
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mu);
+      // online softmax (log2 units), per half; S element i of product 2c + h is key 4h + i of chunk c.
       // P is rounded to bf16 for the PV product, and l sums those rounded
       // values (v_dot2 with (1, 1) per pair), so the output is normalised by
       // exactly the weights it is made of
       constexpr uint32_t kOnes = 0x3F803F80u;    // (1.0, 1.0) in bf16
-      float psum = 0.0f;
-      bf16x8_t pop[2];
-  #pragma unroll
-      for (int u = 0; u < 4; ++u)
-  #pragma unroll
-        for (int i = 0; i < 4; i += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(sc[u][i] - mu);
-          const float p1 = __builtin_amdgcn_exp2f(sc[u][i + 1] - mu);
-          const uint32_t pw = pack_bf16x2(p0, p1);
-          psum = dot2_bf16(pw, kOnes, psum);
-          const bf16x2_t pb = __builtin_bit_cast(bf16x2_t, pw);
-          pop[u >> 1][4 * (u & 1) + i] = pb[0];
-          pop[u >> 1][4 * (u & 1) + i + 1] = pb[1];
-        }
-      l_run = l_run * alpha + psum;
-      m_run = mn;
-  #pragma unroll
-      for (int dg = 0; dg < NDG; ++dg) o[dg] *= alpha;
+      bf16x8_t pop[NH][2];
+#pragma unroll
+      for (int hf = 0; hf < NH; ++hf) {
+        float sc[4][4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float v = s[hf][u][i] * a.scale_log2;
+            const int e = 4 * (u & 1) + i;
+            if (slow && (e >= nv[u >> 1] || e >= cl[hf][u >> 1])) v = -INFINITY;
+            sc[u][i] = v;
+            mx = fmaxf(mx, v);
+          }
+        mx = max_x32(max_x16(mx));
+        const float mn = fmaxf(m_run[hf], mx);
+        const float mu = mn == -INFINITY ? 0.0f : mn;   // no key yet: every p and alpha is 0
+        const float alpha = __builtin_amdgcn_exp2f(m_run[hf] - mu);
+        float psum = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; i += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(sc[u][i] - mu);
+            const float p1 = __builtin_amdgcn_exp2f(sc[u][i + 1] - mu);
+            const uint32_t pw = pack_bf16x2(p0, p1);
+            psum = dot2_bf16(pw, kOnes, psum);
+            const bf16x2_t pb = __builtin_bit_cast(bf16x2_t, pw);
+            pop[hf][u >> 1][4 * (u & 1) + i] = pb[0];
+            pop[hf][u >> 1][4 * (u & 1) + i + 1] = pb[1];
+          }
+        l_run[hf] = l_run[hf] * alpha + psum;
+        m_run[hf] = mn;
+#pragma unroll
+        for (int dg = 0; dg < NDG; ++dg) o[hf][dg] *= alpha;
+      }
 
       // PV products (keys past the end or in invalid blocks: V zeroed, since
-      // unwritten slots may hold anything)
+      // unwritten slots may hold anything; keys cut by a row's causal limit
+      // are valid rows with p = 0)
       if (slow) {
-  #pragma unroll
+#pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
           if constexpr (F8) {
             const uint64_t m8 = nv[c2] >= 8 ? ~0ull : ((1ull << (8 * nv[c2])) - 1);
-  #pragma unroll
+#pragma unroll
             for (int dg = 0; dg < NDG; ++dg) {
               vr[c2][dg].x &= (uint32_t)m8;
               vr[c2][dg].y &= (uint32_t)(m8 >> 32);
             }
           } else {
             uint32_t mw[4];
-  #pragma unroll
+#pragma unroll
             for (int w = 0; w < 4; ++w)
               mw[w] = (2 * w < nv[c2] ? 0xffffu : 0u) | (2 * w + 1 < nv[c2] ? 0xffff0000u : 0u);
-  #pragma unroll
+#pragma unroll
             for (int dg = 0; dg < NDG; ++dg) {
               vr[c2][dg].x &= mw[0];
               vr[c2][dg].y &= mw[1];
@@ -418,14 +490,16 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
           }
         }
       }
-  #pragma unroll
+#pragma unroll
       for (int c2 = 0; c2 < 2; ++c2)
-  #pragma unroll
+#pragma unroll
         for (int dg = 0; dg < NDG; ++dg) {
           bf16x8_t vop;
           if constexpr (F8) vop = fp8x8_bf16(vr[c2][dg].x, vr[c2][dg].y);
           else vop = as_bf16x8(vr[c2][dg]);
-          o[dg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[c2], o[dg], 0, 0, 0);
+#pragma unroll
+          for (int hf = 0; hf < NH; ++hf)
+            o[hf][dg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[hf][c2], o[hf][dg], 0, 0, 0);
         }
 
       // the next step's V.  (The empty asm with a memory clobber keeps the
@@ -437,44 +511,56 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
       idv_next = idv_next2;
     }
 
-    // ---- totals and output: lane (r, j) holds dims 16 dg + 4 j + i of head r ----
-    const float l_tot = sum_x32(sum_x16(l_run));
-    if (r >= g) return;
-    const int qh = qh0 + r;
-    if (part < 0) {
-      const float f = a.v_scale / l_tot;
-      uint16_t *orow = (uint16_t *)a.out + ((int64_t)token * a.num_q_heads + qh) * D + 4 * j;
-  #pragma unroll
-      for (int dg = 0; dg < NDG; ++dg) {
-        uint2 w;
-        w.x = pack_bf16x2(o[dg][0] * f, o[dg][1] * f);
-        w.y = pack_bf16x2(o[dg][2] * f, o[dg][3] * f);
-        *(uint2 *)(orow + 16 * dg) = w;
-      }
-    } else {
-      float *po = a.part_o + ((int64_t)part * a.num_q_heads + qh) * D + 4 * j;
-  #pragma unroll
-      for (int dg = 0; dg < NDG; ++dg) {
-        const f32x4_t v = o[dg] * a.v_scale;
-        *(float4 *)(po + 16 * dg) = make_float4(v[0], v[1], v[2], v[3]);
-      }
-      if (j == 0) {
-        float *pml = a.part_ml + ((int64_t)part * a.num_q_heads + qh) * 2;
-        pml[0] = m_run;
-        pml[1] = l_tot;
+    // ---- totals and output: lane (r, j) holds dims 16 dg + 4 j + i of its column ----
+    float l_tot[NH];
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf) l_tot[hf] = sum_x32(sum_x16(l_run[hf]));   // every lane takes part
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf) {
+      if (!cval[hf]) continue;
+      const int row = token + ct[hf];
+      const int qh = qh0 + ch[hf];
+      if (part < 0) {
+        const float f = a.v_scale / l_tot[hf];
+        uint16_t *orow = (uint16_t *)a.out + ((int64_t)row * a.num_q_heads + qh) * D + 4 * j;
+#pragma unroll
+        for (int dg = 0; dg < NDG; ++dg) {
+          uint2 w;
+          w.x = pack_bf16x2(o[hf][dg][0] * f, o[hf][dg][1] * f);
+          w.y = pack_bf16x2(o[hf][dg][2] * f, o[hf][dg][3] * f);
+          *(uint2 *)(orow + 16 * dg) = w;
+        }
+      } else {
+        const int slot = part + ct[hf] * stride;
+        float *po = a.part_o + ((int64_t)slot * a.num_q_heads + qh) * D + 4 * j;
+#pragma unroll
+        for (int dg = 0; dg < NDG; ++dg) {
+          const f32x4_t v = o[hf][dg] * a.v_scale;
+          *(float4 *)(po + 16 * dg) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+        if (j == 0) {
+          float *pml = a.part_ml + ((int64_t)slot * a.num_q_heads + qh) * 2;
+          pml[0] = m_run[hf];
+          pml[1] = l_tot[hf];
+        }
       }
     }
   };
 
-  // the second item's first step, read now (PAIR)
-  uint4 kr2[4][NKX];
-  VReg vr2[2][NDG];
+  // the second item's first step, read now (PREFETCH)
+  uint4 kr2[PREFETCH ? 4 : 1][NKX];
+  VReg vr2[PREFETCH ? 2 : 1][NDG];
   const int item_b = PAIR && a.pair_stride + bin < a.n_items ? a.pair_stride + bin : -1;
   int pb0 = -1, pb1 = -1, pb2 = -1, pb3 = -1, pidv = -1;
-  if (PAIR && item_b >= 0) {
+  bool pre_b = false;                            // the second item's first step was read ahead
+  if (PREFETCH && item_b >= 0) {
     const DecodeItem ib = a.items[item_b];
     const int req = uniform(ib.req), kv_begin = uniform(ib.kv_begin), kv_end = uniform(ib.kv_end);
-    const int kv_last = uniform(ib.wpos) >= 0 && a.knew != nullptr ? kv_end - 1 : kv_end;
+    const int ikind = uniform((int)ib.kind), iaux = uniform(ib.wpos);
+    const bool own = ikind == 0 && iaux >= 0 && a.knew != nullptr;
+    const int kv_last = own ? kv_end - 1 : kv_end;
+    // a kind-1 piece that stores its rows' K/V first is not read ahead
+    const bool stores_rows = ikind == 1 && a.knew != nullptr && kv_end == iaux;
     const int32_t *__restrict__ btrow = a.block_table + (int64_t)req * a.bt_stride;
     // ---- block ids: lane group j reads block j of a step ----
     // (the read itself is unconditional, at an index clamped to the row's last
@@ -485,47 +571,59 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
       const int id = btrow[bi < last_bi ? bi : last_bi];
       return bi <= last_bi ? id : -1;
     };
-    if (kv_begin < kv_last) {
+    if (kv_begin < kv_last && !stores_rows) {
+      pre_b = true;
       const int idv = ids_of(kv_begin);
       pb0 = blk(idv, 0), pb1 = blk(idv, 1), pb2 = blk(idv, 2), pb3 = blk(idv, 3);
       pidv = ids_of(kv_begin + kKeysPerIter);
-      issue_k(kr2, pb0, pb1, pb2, pb3);
-      asm volatile("" ::: "memory");
-      issue_v(vr2, pb0, pb1, pb2, pb3);
-      asm volatile("" ::: "memory");
+      if constexpr (PREFETCH) {
+        issue_k(kr2, pb0, pb1, pb2, pb3);
+        asm volatile("" ::: "memory");
+        issue_v(vr2, pb0, pb1, pb2, pb3);
+        asm volatile("" ::: "memory");
+      }
     }
   }
   run(bin, false, -1, -1, -1, -1, -1);
   if (PAIR && item_b >= 0) {
+    if constexpr (PREFETCH) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int x = 0; x < NKX; ++x) kr[u][x] = kr2[u][x];
+        for (int x = 0; x < NKX; ++x) kr[u][x] = kr2[u][x];
 #pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2)
+      for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-      for (int dg = 0; dg < NDG; ++dg) vr[c2][dg] = vr2[c2][dg];
-    run(item_b, true, pb0, pb1, pb2, pb3, pidv);
+        for (int dg = 0; dg < NDG; ++dg) vr[c2][dg] = vr2[c2][dg];
+      if (pre_b) run(item_b, true, pb0, pb1, pb2, pb3, pidv);
+      else run(item_b, false, -1, -1, -1, -1, -1);
+    } else {
+      run(item_b, false, -1, -1, -1, -1, -1);
+    }
   }
+}
+
+template <int KV, int D, bool PAIR>
+static void launch_nh(const DecodeArgs &a, int nh, dim3 grid, dim3 block, hipStream_t s) {
+  if (nh == 2) hipLaunchKernelGGL((k_decode_mfma<KV, D, PAIR, 2>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((k_decode_mfma<KV, D, PAIR, 1>), grid, block, 0, s, a);
+}
+
+template <int KV, int D>
+static void launch_pair(const DecodeArgs &a, bool pair, int nh, dim3 grid, dim3 block, hipStream_t s) {
+  if (pair) launch_nh<KV, D, true>(a, nh, grid, block, s);
+  else launch_nh<KV, D, false>(a, nh, grid, block, s);
 }
 
 hipError_t launch_decode_mfma(const pa_kv_pool &p, const DecodeArgs &a, hipStream_t s) {
   const bool pair = a.pair_stride > 0;
   const int units = (pair ? a.pair_stride : a.n_items) * a.num_kv_heads;
   const dim3 grid((units + kDecodeWaves - 1) / kDecodeWaves), block(64 * kDecodeWaves);
-  if (p.kv_dtype == PA_BF16 && p.head_dim == 128) {
-    if (pair) hipLaunchKernelGGL((k_decode_mfma<KV_BF16, 128, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_decode_mfma<KV_BF16, 128, false>), grid, block, 0, s, a);
-  } else if (p.kv_dtype == PA_BF16) {
-    if (pair) hipLaunchKernelGGL((k_decode_mfma<KV_BF16, 64, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_decode_mfma<KV_BF16, 64, false>), grid, block, 0, s, a);
-  } else if (p.head_dim == 128) {
-    if (pair) hipLaunchKernelGGL((k_decode_mfma<KV_FP8, 128, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_decode_mfma<KV_FP8, 128, false>), grid, block, 0, s, a);
-  } else {
-    if (pair) hipLaunchKernelGGL((k_decode_mfma<KV_FP8, 64, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_decode_mfma<KV_FP8, 64, false>), grid, block, 0, s, a);
-  }
+  const int nh = a.max_cols > 16 ? 2 : 1;
+  if (p.kv_dtype == PA_BF16 && p.head_dim == 128) launch_pair<KV_BF16, 128>(a, pair, nh, grid, block, s);
+  else if (p.kv_dtype == PA_BF16) launch_pair<KV_BF16, 64>(a, pair, nh, grid, block, s);
+  else if (p.head_dim == 128) launch_pair<KV_FP8, 128>(a, pair, nh, grid, block, s);
+  else launch_pair<KV_FP8, 64>(a, pair, nh, grid, block, s);
   return hipGetLastError();
 }
 

@@ -444,6 +444,7 @@ struct Plan {
   int32_t part_len = 0;
   int32_t kstart = 0;                            // first key of the split-K items (the cascade's prefix end)
   int32_t pair_stride = 0;                       // paired layout: items b and pair_stride + b share a wave
+  int32_t max_cols = 0;                          // largest (row, head) column count of a decode item
   size_t off_dec = 0, off_merge = 0, off_extw = 0, off_pre = 0, off_rtok = 0, off_rslot = 0, off_wseg = 0;
   size_t off_ml = 0, off_o = 0, bytes = 0;
 };
@@ -488,6 +489,19 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
   const int Hkv = p.num_kv_heads, g = Hq / Hkv;
   const bool ext_ok = extend_supported(p, q_dtype) && env_flag("PA_DISABLE_EXTEND") == false;
   const int ext_min = extend_min_rows();
+  // PA_MULTIROW=1: short chunks (2 .. 32 / g rows, such as the draft tokens
+  // of a verify step) on the matrix-core split-K kernel: one kind-1 item
+  // covers all the chunk's rows, each (row, q head) pair an MFMA column, so
+  // the request's K/V are read once per kv head at decode bandwidth (the
+  // extend kernel leaves most of its 128 columns empty).  Measured on the
+  // verify workload (64 chunks of 2..8 rows, g = 4): the split-K kernel
+  // takes 118 us against the extend kernel's 131, but its pieces' merge
+  // (11 us) and the rows' write (9 us as a scatter launch, 8.5 us inside
+  // the last piece) make the step slower (0.136-0.137 ms against 0.131), so
+  // the extend kernel stays the default.
+  const bool multi_ok = p.kv_dtype != PA_F32 && env_flag("PA_MULTIROW");
+  auto multi = [&](int32_t c) { return multi_ok && c >= 2 && (int64_t)c * g <= 32; };
+  auto on_ext = [&](int32_t c) { return ext_ok && c >= ext_min && !multi(c); };
   std::vector<int32_t> ext_reqs;                 // requests on the MFMA extend kernel, planned after the loop
 
   // Shared prefix (cascade): the split-K rows' first P keys are the same
@@ -506,7 +520,7 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
   int32_t prefix_rows = 0;
   for (int32_t i = 0; i < b.num_seqs && cascade; ++i) {
     const int32_t c = q[i + 1] - q[i];
-    if (c == 0 || (ext_ok && c >= ext_min)) continue;
+    if (c == 0 || on_ext(c)) continue;
     if (L[i] - c < P) cascade = false;
     if (plan.prefix_req < 0) plan.prefix_req = i;
     prefix_rows += c;
@@ -533,8 +547,9 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
   int32_t max_keys = 0;
   for (int32_t i = 0; i < b.num_seqs; ++i) {
     const int32_t c = q[i + 1] - q[i];
-    if (c == 0 || (ext_ok && c >= ext_min)) continue;
-    for (int32_t t = 0; t < c; ++t) {
+    if (c == 0 || on_ext(c)) continue;
+    // (a multi-row chunk is one unit over the keys of its last row)
+    for (int32_t t = multi(c) ? c - 1 : 0; t < c; ++t) {
       const int32_t k = std::max(0, (causal ? (L[i] - c + t + 1) : L[i]) - kstart);
       tok_keys.push_back(k);
       key_work += k;
@@ -694,18 +709,63 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
       plan.row_slot0.push_back(plan.n_slots);
       plan.merge.push_back(MergeItem{tok, plan.n_slots, n_kc + nseg, 0});
       for (int32_t r = 0; r < nseg; ++r)
-        plan.dec.push_back(DecodeItem{tok, i, bnd[r], bnd[r + 1], plan.n_slots + n_kc + r, wpos(r), {0, 0}});
+        plan.dec.push_back(DecodeItem{tok, i, bnd[r], bnd[r + 1], plan.n_slots + n_kc + r, wpos(r), 1, 0, 0});
       plan.n_slots += n_kc + nseg;
     } else if (nseg == 1) {
-      plan.dec.push_back(DecodeItem{tok, i, bnd[0], bnd[1], -1, wpos(0), {0, 0}});
+      plan.dec.push_back(DecodeItem{tok, i, bnd[0], bnd[1], -1, wpos(0), 1, 0, 0});
     } else {
       plan.merge.push_back(MergeItem{tok, plan.n_slots, nseg, 0});
       for (int32_t r = 0; r < nseg; ++r)
-        plan.dec.push_back(DecodeItem{tok, i, bnd[r], bnd[r + 1], plan.n_slots + r, wpos(r), {0, 0}});
+        plan.dec.push_back(DecodeItem{tok, i, bnd[r], bnd[r + 1], plan.n_slots + r, wpos(r), 1, 0, 0});
       plan.n_slots += nseg;
     }
   };
+  // A multi-row chunk's key segments (those of its last row, whose limit is
+  // L[i]) -> kind-1 items; row t's partial of segment r is at slot
+  // part + t * stride, so each row's slots are consecutive for its merge.
+  auto emit_rows = [&](int32_t i, const int32_t *bnd, int32_t nseg) {
+    const int32_t c = q[i + 1] - q[i], tok0 = q[i];
+    auto item = [&](int32_t r, int32_t part, int32_t stride) {
+      plan.dec.push_back(DecodeItem{tok0, i, bnd[r], bnd[r + 1], part, L[i], (int16_t)c, 1, stride});
+    };
+    if (cascade) {
+      const int32_t per = n_kc + nseg;           // the prefix chunks, then the segments
+      for (int32_t t = 0; t < c; ++t) {
+        plan.row_token.push_back(tok0 + t);
+        plan.row_slot0.push_back(plan.n_slots + t * per);
+        plan.merge.push_back(MergeItem{tok0 + t, plan.n_slots + t * per, per, 0});
+      }
+      for (int32_t r = 0; r < nseg; ++r) item(r, plan.n_slots + n_kc + r, per);
+      plan.n_slots += c * per;
+    } else if (nseg == 1) {
+      item(0, -1, 0);
+    } else {
+      for (int32_t t = 0; t < c; ++t) plan.merge.push_back(MergeItem{tok0 + t, plan.n_slots + t * nseg, nseg, 0});
+      for (int32_t r = 0; r < nseg; ++r) item(r, plan.n_slots + r, nseg);
+      plan.n_slots += c * nseg;
+    }
+  };
   std::vector<int32_t> bnd;
+  // key segments of a unit whose keys end at nvis: its pieces of the paired
+  // layout (the packing visited the units in this order, with the same step
+  // counts), or partitions of `part` keys from kstart
+  auto segments = [&](int32_t nvis) {
+    bnd.clear();
+    if (paired) {
+      const int64_t st = std::max<int64_t>(0, (int64_t)nvis - kstart + kKeysPerIter - 1) / kKeysPerIter;
+      bnd.push_back(std::min(nvis, kstart));
+      for (int64_t o = 0; o < st && piece_next < pieces.size();) {
+        const auto &pc = pieces[piece_next++];
+        o = pc[3];
+        bnd.push_back((int32_t)std::min<int64_t>(nvis, kstart + (int64_t)kKeysPerIter * o));
+        dec_pos.push_back(pc[0]);
+      }
+    } else {
+      for (int64_t k = kstart; k < nvis; k += part) bnd.push_back((int32_t)k);
+      bnd.push_back(nvis);
+    }
+    if (bnd.size() == 1 && !cascade) bnd.insert(bnd.begin(), 0);
+  };
 
   for (int32_t i = 0; i < b.num_seqs; ++i) {
     const int32_t c = q[i + 1] - q[i];
@@ -713,43 +773,42 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
     // KV update: a split-K request with one new token has it written by the
     // decode unit that holds its last key; every other new token is written
     // by the scatter pass that runs before the attention kernels
-    const bool own_write = kv_update && c == 1 && !(ext_ok && c >= ext_min);
+    const bool own_write = kv_update && c == 1 && !on_ext(c);
     // a request of one key-split extend item per kv head: the item writes
-    // the request's new rows itself (no other item reads them)
-    const bool ext_self = kv_update && ext_ok && c >= ext_min && (int64_t)c * g <= kExtCols;
-    if (kv_update && !own_write && !ext_self)
+    // the request's new rows itself (no other item reads them); so does the
+    // last piece of a multi-row chunk
+    const bool ext_self = kv_update && on_ext(c) && (int64_t)c * g <= kExtCols;
+    const bool rows_self = kv_update && multi(c);
+    if (kv_update && !own_write && !ext_self && !rows_self)
       for (int32_t pos = L[i] - c; pos < L[i];) {
         const int32_t end = std::min(L[i], (pos / kBlock + 1) * kBlock);
         plan.wseg.push_back(WriteSeg{i, q[i] + pos - (L[i] - c), pos, end - pos});
         pos = end;
       }
-    if (ext_ok && c >= ext_min) {
+    if (on_ext(c)) {
       ext_reqs.push_back(i);
       continue;
     }
-    for (int32_t t = 0; t < c; ++t) {
-      const int32_t tok = q[i] + t;
-      const int32_t nvis = causal ? (L[i] - c + t + 1) : L[i];
-      bnd.clear();
-      if (paired) {
-        // this token's pieces (the packing visited the tokens in this
-        // order, with the same step counts)
-        const int64_t st = std::max<int64_t>(0, (int64_t)nvis - kstart + kKeysPerIter - 1) / kKeysPerIter;
-        bnd.push_back(std::min(nvis, kstart));
-        for (int64_t o = 0; o < st && piece_next < pieces.size();) {
-          const auto &pc = pieces[piece_next++];
-          o = pc[3];
-          bnd.push_back((int32_t)std::min<int64_t>(nvis, kstart + (int64_t)kKeysPerIter * o));
-          dec_pos.push_back(pc[0]);
-        }
-      } else {
-        // partitions of `part` keys from kstart
-        for (int64_t k = kstart; k < nvis; k += part) bnd.push_back((int32_t)k);
-        bnd.push_back(nvis);
+    if (multi(c)) {
+      segments(L[i]);
+      // the chunk's own keys [L - c, L) all in the last piece, which writes
+      // them (the boundary moves down to the block holding key L - c; the
+      // piece before it keeps at least 64 - 47 keys, since pieces other than
+      // the last hold multiples of 64 keys and c <= 32)
+      if (rows_self && bnd.size() > 2) {
+        int32_t &last = bnd[bnd.size() - 2];
+        last = std::min(last, (L[i] - c) / kBlock * kBlock);
       }
-      if (bnd.size() == 1 && !cascade) bnd.insert(bnd.begin(), 0);
-      emit_token(tok, i, bnd.data(), (int32_t)bnd.size() - 1, own_write);
+      emit_rows(i, bnd.data(), (int32_t)bnd.size() - 1);
+      plan.max_cols = std::max(plan.max_cols, c * g);
+      continue;
     }
+    for (int32_t t = 0; t < c; ++t) {
+      const int32_t nvis = causal ? (L[i] - c + t + 1) : L[i];
+      segments(nvis);
+      emit_token(q[i] + t, i, bnd.data(), (int32_t)bnd.size() - 1, own_write);
+    }
+    plan.max_cols = std::max(plan.max_cols, g);
   }
   // Extend items, all run by one launch of the wide kernel.
   //  * A request with at most kExtCols (token, head) columns per kv head is
@@ -935,32 +994,50 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
 }
 
 // Host-side consistency of a plan's split-K work (PA_CHECK_PLAN=1, for
-// tests): every item lies inside its row, and each split-K token's items
-// cover its keys [kstart, visible end) once, in order, with distinct partial
-// slots.  Returns null or what is wrong.
-static const char *check_decode_plan(const Plan &plan, const pa_batch &b, int causal) {
+// tests): every item lies inside its request, and each split-K row's items
+// cover its keys [kstart, visible end) once, in order (a multi-row item's
+// range ends at its last row's limit, which covers every row of it), with
+// distinct partial slots.  Returns null or what is wrong.
+static const char *check_decode_plan(const Plan &plan, const pa_batch &b, int causal, bool kv_update) {
   const int32_t *q = b.query_start_loc_host, *L = b.seq_lens_host;
-  std::vector<std::vector<const DecodeItem *>> by_tok(b.num_tokens);
+  struct Use { const DecodeItem *d; int32_t slot; };
+  std::vector<std::vector<Use>> by_tok(b.num_tokens);
   for (const DecodeItem &d : plan.dec) {
     if (d.req < 0 || d.req >= b.num_seqs || d.token < 0 || d.token >= b.num_tokens) return "item row out of range";
-    if (d.token < q[d.req] || d.token >= q[d.req + 1]) return "item token outside its request";
+    if (d.kind != 0 && d.kind != 1) return "unknown item kind";
+    const int32_t c = q[d.req + 1] - q[d.req];
+    const int32_t n = d.kind == 0 ? 1 : d.ntok;
+    if (d.kind == 0 && d.ntok != 1) return "a one-row item with ntok != 1";
+    if (d.kind == 1 && (d.token != q[d.req] || n != c || d.wpos != L[d.req] || n < 2))
+      return "a multi-row item that is not its request's whole chunk";
+    if (d.token < q[d.req] || d.token + n > q[d.req + 1]) return "item rows outside their request";
     if (d.kv_begin < 0 || d.kv_begin >= d.kv_end || d.kv_end > L[d.req]) return "item keys outside the row";
-    if (d.part >= plan.n_slots || d.part < -1) return "partial slot out of range";
-    if (d.wpos != -1 && (d.wpos != L[d.req] - 1 || d.kv_end != L[d.req])) return "bad own-write position";
-    by_tok[d.token].push_back(&d);
+    if (d.kind == 0 && d.wpos != -1 && (d.wpos != L[d.req] - 1 || d.kv_end != L[d.req])) return "bad own-write position";
+    // (with the KV update the last piece stores the rows' K/V: it holds all their keys)
+    if (kv_update && d.kind == 1 && d.kv_end == L[d.req] && d.kv_begin > L[d.req] - n)
+      return "a multi-row item's last piece misses some of its rows' keys";
+    if (kv_update && d.kind == 1 && d.kv_end < L[d.req] && d.kv_end > L[d.req] - n)
+      return "a multi-row item's rows' keys split between pieces";
+    if (d.kind == 1 && (d.kv_begin % kBlock) != 0) return "a multi-row piece that starts inside a block";
+    for (int32_t t = 0; t < n; ++t) {
+      const int32_t slot = d.part < 0 ? -1 : d.part + t * (d.kind == 0 ? 0 : d.stride);
+      if (slot >= plan.n_slots) return "partial slot out of range";
+      by_tok[d.token + t].push_back(Use{&d, slot});
+    }
   }
   std::vector<char> used(plan.n_slots, 0);
   for (int32_t t = 0; t < b.num_tokens; ++t) {
     auto &v = by_tok[t];
     if (v.empty()) continue;
-    std::sort(v.begin(), v.end(), [](const DecodeItem *x, const DecodeItem *y) { return x->kv_begin < y->kv_begin; });
-    const int32_t i = v[0]->req, c = q[i + 1] - q[i];
+    std::sort(v.begin(), v.end(), [](const Use &x, const Use &y) { return x.d->kv_begin < y.d->kv_begin; });
+    const int32_t i = v[0].d->req, c = q[i + 1] - q[i];
     const int32_t nvis = causal ? L[i] - c + (t - q[i]) + 1 : L[i];
-    if (v.front()->kv_begin != plan.kstart || v.back()->kv_end != nvis) return "a token's items do not cover its keys";
+    const int32_t want_end = v[0].d->kind == 1 ? L[i] : nvis;
+    if (v.front().d->kv_begin != plan.kstart || v.back().d->kv_end != want_end) return "a row's items do not cover its keys";
     for (size_t k = 0; k < v.size(); ++k) {
-      if (k && v[k]->kv_begin != v[k - 1]->kv_end) return "a token's items overlap or leave a gap";
-      const int32_t pt = v[k]->part;
-      if (pt < 0 && (v.size() > 1 || plan.kstart > 0)) return "a split token's item without a partial slot";
+      if (k && v[k].d->kv_begin != v[k - 1].d->kv_end) return "a row's items overlap or leave a gap";
+      const int32_t pt = v[k].slot;
+      if (pt < 0 && (v.size() > 1 || plan.kstart > 0)) return "a split row's item without a partial slot";
       if (pt >= 0) {
         if (used[pt]) return "a partial slot used twice";
         used[pt] = 1;
@@ -1058,8 +1135,8 @@ size_t pa_attention_workspace_bytes(const pa_kv_pool *pool, const pa_batch *batc
   Plan plan_nc;
   build_plan(*pool, *batch, num_q_heads, qd, 0, true, plan_nc);
   if (env_flag("PA_CHECK_PLAN")) {
-    const char *why = check_decode_plan(plan, *batch, 1);
-    if (!why) why = check_decode_plan(plan_nc, *batch, 0);
+    const char *why = check_decode_plan(plan, *batch, 1, true);
+    if (!why) why = check_decode_plan(plan_nc, *batch, 0, true);
     if (why) {
       fail(PA_ERR_VALIDATION, "plan check: %s", why);
       return 0;
@@ -1272,6 +1349,8 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
     a.block_table = batch->block_table;
     a.items = (const DecodeItem *)(items + plan.off_dec);
     a.pair_stride = plan.pair_stride;
+    a.causal = causal;
+    a.max_cols = plan.max_cols;
     a.part_ml = (float *)(ws + plan.off_ml);
     a.part_o = (float *)(ws + plan.off_o);
     a.n_items = (int32_t)plan.dec.size();

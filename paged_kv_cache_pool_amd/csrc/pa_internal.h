@@ -15,13 +15,21 @@ constexpr int kBlock = 16;           // tokens per pool block (the only size sup
 constexpr int kKeysPerIter = 64;     // keys one wave scores per iteration (4 blocks)
 constexpr int kWavesPerGroup = 4;    // waves per workgroup in the split-K kernels
 
-// One unit of token-parallel (split-K) attention: keys [kv_begin, kv_end) of
-// token `token` (row of the flat stream) belonging to request `req`.  When
-// `part` < 0 the range is the token's whole visible range and the kernel
-// writes the final output; otherwise it writes partial (m, l, o) at slot `part`.
-// When `wpos` >= 0 (attention that includes the KV update) the token is its
-// request's only new token, at position wpos inside this unit's key range:
-// the unit first stores the token's K/V rows into the pool, then attends.
+// One unit of token-parallel (split-K) attention: keys [kv_begin, kv_end),
+// walked through the block table of request `req`, for the query rows of the
+// item's kind:
+//  * kind 0 (ntok = 1): row `token` of the flat stream.  When `wpos` >= 0
+//    (attention that includes the KV update) the row is its request's only
+//    new token, at position wpos inside this unit's key range: the unit first
+//    stores the token's K/V rows into the pool, then attends.
+//  * kind 1: the ntok consecutive rows token .. token + ntok - 1 of request
+//    `req` (a short chunk, such as the draft tokens of a verify step); `wpos`
+//    is the key limit (exclusive) of the last of them, and with a causal mask
+//    row t sees keys below wpos - (ntok - 1 - t).
+// The matrix-core kernel gives each (row, q head) pair one MFMA column, so
+// ntok x g <= 32.  When `part` < 0 the range is every row's whole visible
+// range and the kernel writes the final output; otherwise row t's partial
+// (m, l, o) goes to slot part + t * stride.
 struct DecodeItem {
   int32_t token;
   int32_t req;
@@ -29,8 +37,11 @@ struct DecodeItem {
   int32_t kv_end;
   int32_t part;
   int32_t wpos;
-  int32_t pad[2];
+  int16_t ntok;
+  int16_t kind;
+  int32_t stride;
 };
+static_assert(sizeof(DecodeItem) == 32, "decode items are 32 bytes");
 
 // New tokens whose K/V rows the plan-driven scatter writes: `count` (1..16)
 // consecutive tokens of request `req`, flat rows tok0 .., positions pos0 ..,
@@ -129,6 +140,8 @@ struct DecodeArgs {
   float scale_log2;       // softmax_scale * log2(e) (* k_scale for fp8 pools)
   float v_scale;          // 1 for non-fp8 pools
   int32_t zero;           // always 0 (used to keep per-step loads inside the loop)
+  int32_t causal;         // kind 1 items: rows see keys up to their own position
+  int32_t max_cols;       // largest ntok x g over the items (matrix-core kernel: <= 32)
   // KV update of items with wpos >= 0 (null knew: no update in this launch)
   const void *knew;       // [T][Hkv][D] new K rows (query dtype)
   const void *vnew;

@@ -197,6 +197,45 @@ def test_empty_calls_are_no_ops(B):
     assert _att(B, p, b) == 0
 
 
+def test_planner_multirow_batches(B, monkeypatch):
+    """Short chunks (2 .. 32 / g rows, as in a speculative verify step) as
+    multi-row items of the split-K kernel (PA_MULTIROW=1): on random batches of
+    such chunks mixed with decode rows, GQA ratios 1..16, bf16 and fp8 pools,
+    with and without a shared-prefix hint, the planner's consistency check
+    passes in the paired layout and the partition forms, and with multi-row
+    items off (the default)."""
+    rng = np.random.default_rng(7)
+    for it in range(150):
+        hkv = int(rng.choice([1, 2, 8]))
+        g = int(rng.choice([1, 2, 4, 8, 16]))
+        n = int(rng.integers(1, 40))
+        cmax = max(1, 32 // g)
+        c = rng.integers(1, cmax + 1, n).astype(np.int32)
+        hist = rng.integers(0, 3000, n).astype(np.int32)
+        hint = int(rng.integers(1, 4)) if rng.random() < 0.3 else 0
+        if hint:
+            hist = np.maximum(hist, 16 * hint)
+        sl = (hist + c).astype(np.int32)
+        qsl = np.concatenate([[0], np.cumsum(c)]).astype(np.int32)
+        stride = int(-(-sl.max() // 16))
+        p = _pool(B, kv=str(rng.choice(["bf16", "fp8"])), D=128, H=hkv, nb=stride * n + 64)
+        b = B.PaBatch(n, int(qsl[-1]), 0x3000, 0x4000, 0x5000, stride, qsl.ctypes.data, sl.ctypes.data, hint)
+        hq = hkv * g
+        monkeypatch.setenv("PA_CHECK_PLAN", "1")
+        for multi in ("1", None):
+            for pairs, part in [(None, None), ("2", None), ("0", None), ("0", "64"), ("0", "192")]:
+                for k, v in [("PA_DECODE_PAIRS", pairs), ("PA_PARTITION_KEYS", part),
+                             ("PA_MULTIROW", multi)]:
+                    if v is None:
+                        monkeypatch.delenv(k, raising=False)
+                    else:
+                        monkeypatch.setenv(k, v)
+                nl = B.lib.pa_attention_workspace_bytes(C.byref(p), C.byref(b), hq)
+                assert nl > 0, (it, multi, pairs, part, B.lib.pa_last_error().decode())
+        for k in ("PA_CHECK_PLAN", "PA_PARTITION_KEYS", "PA_DECODE_PAIRS", "PA_MULTIROW"):
+            monkeypatch.delenv(k, raising=False)
+
+
 def test_planner_random_batches(B, monkeypatch):
     """The host planner on random ragged batches (runs on the CPU through the
     workspace size query): decode rows, short and long prefill chunks with

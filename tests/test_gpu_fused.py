@@ -102,6 +102,20 @@ def _fused_and_separate(R, w, **kw):
     return fused, sep
 
 
+# routes of a short chunk (2 .. 32 / g rows): multi-row items of the split-K
+# kernel (PA_MULTIROW), one split-K unit per row, or the MFMA extend kernel
+# (the default)
+ROUTES = {"multi": {"PA_MULTIROW": "1"}, "rows": {"PA_EXTEND_MIN_ROWS": "64"},
+          "extend": {"PA_EXTEND_MIN_ROWS": "2"}}
+
+
+def _route(monkeypatch, route):
+    for k in ("PA_MULTIROW", "PA_EXTEND_MIN_ROWS"):
+        monkeypatch.delenv(k, raising=False)
+    for k, v in ROUTES[route].items():
+        monkeypatch.setenv(k, v)
+
+
 @pytest.mark.parametrize("seed", range(30))
 def test_fused_equals_separate_random(R, seed):
     """Random ragged batches over every pool type, head size and GQA ratio:
@@ -127,20 +141,20 @@ def test_fused_equals_separate_random(R, seed):
 
 
 @pytest.mark.parametrize("pairs", ["0", "1", "2"])
-@pytest.mark.parametrize("min_rows", ["16", "2"])
+@pytest.mark.parametrize("route", ["multi", "rows", "extend"])
 @pytest.mark.parametrize("kv", [W.BF16, W.FP8])
-def test_fused_decode_partitions_and_verify_rows(R, monkeypatch, kv, min_rows, pairs):
+def test_fused_decode_partitions_and_verify_rows(R, monkeypatch, kv, route, pairs):
     """Decode rows split into 64-key partitions or into the paired layout's
     pieces, one wave per bin or per piece (the newest key is written by the
     row's last item, which may hold that key alone), next to
     speculative-verify-sized chunks of 2 to 8 rows and one prefill chunk.  The
     chunks' K/V are written by the scatter pass before the attention kernels
-    read them; the verify chunks run on the split-K kernel (threshold 16) or on
-    the MFMA extend kernel (threshold 2, the default)."""
+    read them; the verify chunks run as multi-row items of the split-K kernel,
+    as one split-K unit per row, or on the MFMA extend kernel (the default)."""
     monkeypatch.setenv("PA_PARTITION_KEYS", "64")
     monkeypatch.setenv("PA_DECODE_PAIRS", pairs)
-    monkeypatch.setenv("PA_EXTEND_MIN_ROWS", min_rows)
-    say("fused partitions + verify rows", kv, "extend threshold", min_rows, "pairs", pairs)
+    _route(monkeypatch, route)
+    say("fused partitions + verify rows", kv, "route", route, "pairs", pairs)
     nc = [64, 0, 127, 128, 300, 5, 64, 200, 40]
     ns = [1, 1, 1, 1, 1, 4, 8, 2, 24]
     w = W.build(f"fused_parts_{kv}", 7, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
@@ -169,6 +183,49 @@ def test_fused_cascade(R, monkeypatch, kv, pairs):
     _assert_same_pool(fused.pool, sep.pool)
     _assert_pool_is_oracle(w, fused.pool)
     _check_out(w, fused)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_multirow_chunks_random(R, monkeypatch, seed):
+    """Random batches of short chunks (1 .. 32 / g rows over random histories)
+    as multi-row items: g in {1, 2, 4, 8, 16} (so 16 or 32 MFMA columns),
+    head dims 64 and 128, bf16 and fp8 pools, causal and not, in the paired
+    layout (one wave per bin or per piece) and with forced 64-key partitions,
+    so rows' causal limits fall inside, at the start of and after key pieces.
+    Both step forms: pool bytes and slots exact, every row against the
+    oracle."""
+    rng = np.random.default_rng(seed + 500)
+    monkeypatch.setenv("PA_MULTIROW", "1")
+    kv = [W.BF16, W.FP8][seed % 2]
+    g = [1, 2, 4, 8, 16][(seed // 2) % 5]
+    D = [128, 64][(seed // 10) % 2]
+    causal = seed % 7 != 3
+    pairs, part = [("1", None), ("2", None), ("0", "64")][seed % 3]
+    monkeypatch.setenv("PA_DECODE_PAIRS", pairs)
+    if part:
+        monkeypatch.setenv("PA_PARTITION_KEYS", part)
+    n = int(rng.integers(1, 12))
+    ns = rng.integers(1, max(1, 32 // g) + 1, n)
+    nc = rng.integers(0, 400, n)
+    say("multi-row random", seed, kv, "g", g, "D", D, "causal", causal, "pairs", pairs, "part", part,
+        "rows", ns.tolist())
+    w = W.build(f"multirow_{seed}", seed + 500, num_q_heads=2 * g, num_kv_heads=2, head_dim=D,
+                block_size=16, num_blocks=int(sum(-(-(a + b) // 16) for a, b in zip(nc, ns))) + 6,
+                kv_dtype=kv, io_dtype=W.BF16, num_computed=nc.astype(np.int32),
+                num_scheduled=ns.astype(np.int32))
+    fused = R.GpuStep(w, fused=True, causal=causal)
+    fused.run()
+    sep = R.GpuStep(w, causal=causal)
+    sep.run()
+    torch.cuda.synchronize()
+    assert (fused.slots.cpu().numpy() == _want_slots(w)).all()
+    _assert_same_pool(fused.pool, sep.pool)
+    _assert_pool_is_oracle(w, fused.pool)
+    for step in (fused, sep):
+        ref = O.run_step(w, causal=causal).out
+        err = np.abs(step.out_f64() - ref)
+        assert np.isfinite(step.out_f64()).all()
+        assert err.max() <= TOL[kv], (float(err.max()), np.unravel_index(err.argmax(), err.shape))
 
 
 def test_fused_page_mixed_batch(R):
@@ -220,14 +277,15 @@ def test_fused_rejects_null_rows(R):
     assert st == 1
 
 
-@pytest.mark.parametrize("min_rows", ["16", "2"])
-def test_spec_verify_workload(R, monkeypatch, min_rows):
+@pytest.mark.parametrize("route", ["multi", "rows", "extend"])
+def test_spec_verify_workload(R, monkeypatch, route):
     """The speculative-verify workload (64 requests with 2..8 draft tokens after
-    long histories) with the verify chunks on the split-K kernel (threshold 16)
-    and on the MFMA extend kernel (threshold 2), one call with the KV update:
-    every row against the oracle, slots exact."""
-    monkeypatch.setenv("PA_EXTEND_MIN_ROWS", min_rows)
-    say("spec verify, extend threshold", min_rows)
+    long histories) with the verify chunks as multi-row items of the split-K
+    kernel, as one split-K unit per row, and on the MFMA extend kernel (the
+    default), one call with the KV update: every row against the oracle,
+    slots exact."""
+    _route(monkeypatch, route)
+    say("spec verify, route", route)
     w = W.make(6)
     step = R.GpuStep(w, fused=True)
     step.run()
