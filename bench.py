@@ -319,32 +319,39 @@ def load_traffic(kernel, workload):
 
 
 def cascade_prefix(w, seq_lens, qsl, ext_min_rows=2, extend_on=True, hint=True):
-    """Keys of the shared prefix that the library's cascade pass takes over
-    from the split-K rows (0 when it does not apply): the same rule as the
-    library's plan."""
+    """Keys of the shared prefix that the library's cascade takes over from the
+    split-K rows (0 when it does not apply), and whether the split-K launch
+    computes the prefix rows' prefix part itself (prefix items, rather than
+    the MFMA prefix pass): the same rules as the library's plan."""
     P = w.shared_prefix_blocks * w.block_size if hint else 0
     mfma_ok = w.kv_dtype in ("bf16", "fp8") and w.head_dim == 128 and w.io_dtype == "bf16"
     if P == 0 or not mfma_ok or os.environ.get("PA_DISABLE_CASCADE", "0") not in ("", "0"):
-        return 0
+        return 0, False
     rows = 0
     for i in range(w.num_seqs):
         c, L = int(qsl[i + 1] - qsl[i]), int(seq_lens[i])
         if c == 0 or (extend_on and c >= ext_min_rows and mfma_ok):
             continue
         if L - c < P:
-            return 0
+            return 0, False
         rows += c
-    return P if rows else 0
+    if not rows:
+        return 0, False
+    in_decode = rows * (w.num_q_heads // w.num_kv_heads) <= 1024 and \
+        os.environ.get("PA_PREFIX_PASS", "0") in ("", "0")
+    return P, in_decode
 
 
-def algorithmic_work(w, seq_lens, qsl, ext_min_rows=2, extend_on=True, prefix=0, fused=False):
+def algorithmic_work(w, seq_lens, qsl, ext_min_rows=2, extend_on=True, prefix=0, fused=False,
+                     prefix_in_decode=False):
     """Bytes the split-K decode kernel must move, flops the extend kernel must
-    do and flops of the shared-prefix pass, per step, by the per-unit formulas
-    in the design notes.  With a shared prefix of `prefix` keys taken over by
-    the cascade pass, the split-K rows' bytes count their own keys only.  In
-    the step with the KV update (`fused`), a decode row of a one-token request
-    takes its newest key from the input rows and also writes them to the
-    pool."""
+    do and flops of the shared-prefix attention, per step, by the per-unit
+    formulas in the design notes.  With a shared prefix of `prefix` keys, the
+    split-K rows' bytes count their own keys, and the prefix's K/V once per
+    kv head when the split-K launch computes the prefix part itself
+    (`prefix_in_decode`).  In the step with the KV update (`fused`), a
+    decode row of a one-token request takes its newest key from the input
+    rows and also writes them to the pool."""
     b_kv, b_io = ELEM[w.kv_dtype], ELEM[w.io_dtype]
     H, Hq, D, S = w.num_kv_heads, w.num_q_heads, w.head_dim, w.block_size
     dec_bytes = 0
@@ -366,6 +373,8 @@ def algorithmic_work(w, seq_lens, qsl, ext_min_rows=2, extend_on=True, prefix=0,
                 if fused and c == 1:
                     dec_bytes += H * D * 2 * (b_io - b_kv) + H * D * 2 * b_kv
                 pre_flops += 4 * Hq * D * prefix
+    if prefix_in_decode:
+        dec_bytes += prefix * H * D * 2 * b_kv
     return dec_bytes, ext_flops, ext_bytes, pre_flops
 
 
@@ -525,9 +534,11 @@ def main():
     qsl, sl = B.prepare_metadata(w.num_computed, w.num_scheduled)
     ext_on = os.environ.get("PA_DISABLE_EXTEND", "0") in ("", "0")
     ext_min = int(os.environ.get("PA_EXTEND_MIN_ROWS", "2"))
-    prefix = cascade_prefix(w, sl, qsl, ext_min, ext_on, hint=step.batch.num_common_prefix_blocks > 0)
+    prefix, prefix_in_decode = cascade_prefix(w, sl, qsl, ext_min, ext_on,
+                                              hint=step.batch.num_common_prefix_blocks > 0)
     dec_bytes, ext_flops, ext_bytes, pre_flops = algorithmic_work(
-        w, sl, qsl, ext_min, ext_on and "k_extend" in kernels, prefix, fused=not a.separate)
+        w, sl, qsl, ext_min, ext_on and "k_extend" in kernels, prefix, fused=not a.separate,
+        prefix_in_decode=prefix_in_decode)
 
     # dominant kernel: the attention kernel that takes the longer time.  The
     # extend kernel is priced against MFMA when its work is compute-heavy
@@ -629,12 +640,14 @@ def main():
         "placement": placement,
     }
     if dom == "k_decode":
-        uniq = unique_kv_bytes(w, sl, qsl, prefix)
+        uniq = unique_kv_bytes(w, sl, qsl, 0 if prefix_in_decode else prefix)
         out["decode_kv_bytes_logical"] = dec_bytes
         out["decode_kv_bytes_unique"] = uniq
         out["decode_kv_gbps_unique"] = round(uniq / (kernels["k_decode"]["avg_us"] * 1e-6) / 1e9, 1)
-    if pre_flops and "k_prefix" in kernels:
+    if prefix:
         out["prefix_keys"] = prefix
+        out["prefix_attention"] = "split-K prefix items" if prefix_in_decode else "MFMA prefix pass"
+    if pre_flops and "k_prefix" in kernels:
         out["prefix_tflops"] = round(pre_flops / (kernels["k_prefix"]["avg_us"] * 1e-6) / 1e12, 1)
     if ext_flops:
         out["extend_tflops"] = round(ext_flops / (kernels["k_extend"]["avg_us"] * 1e-6) / 1e12, 1) \

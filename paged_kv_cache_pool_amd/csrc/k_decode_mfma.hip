@@ -200,7 +200,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     const int wpos = kind == 0 ? aux : -1;
     const bool wnew = wpos >= 0 && a.knew != nullptr;
     const int kv_last = wnew ? kv_end - 1 : kv_end;   // end of the keys read from the pool
-    const int32_t *__restrict__ btrow = a.block_table + (int64_t)req * a.bt_stride;
+    const int32_t *__restrict__ btrow = kind == 2 ? a.prefix_bt : a.block_table + (int64_t)req * a.bt_stride;
     // ---- columns: lane column 16 hf + r of half hf is (row ct, head ch) ----
     const bool rows_causal = kind == 1 && a.causal != 0;
     int ct[NH], ch[NH], clim[NH];
@@ -217,6 +217,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     }
     // keys from which some column can be cut off (the masked steps start there)
     const int cut = rows_causal ? min(kv_last, aux - (ntok - 1)) : kv_last;
+    // flat row (q / output row) of each half's column
+    int crow[NH];
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf) crow[hf] = kind == 2 ? a.row_token[token + ct[hf]] : token + ct[hf];
     // ---- Q^T operand of each half: column r = (row ct, head ch) (zero when invalid) ----
     // (invalid columns are cleared with a mask, not a branch: a branch around
     // a loaded register makes the compiler wait for each load in turn)
@@ -224,7 +228,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
 #pragma unroll
     for (int hf = 0; hf < NH; ++hf) {
       const uint16_t *qrow =
-          (const uint16_t *)a.q + ((int64_t)(token + ct[hf]) * a.num_q_heads + qh0 + ch[hf]) * D;
+          (const uint16_t *)a.q + ((int64_t)crow[hf] * a.num_q_heads + qh0 + ch[hf]) * D;
       uint4 v[NS];
 #pragma unroll
       for (int c = 0; c < NS; ++c) v[c] = *(const uint4 *)(qrow + qdim(c));
@@ -518,7 +522,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
 #pragma unroll
     for (int hf = 0; hf < NH; ++hf) {
       if (!cval[hf]) continue;
-      const int row = token + ct[hf];
+      const int row = crow[hf];
       const int qh = qh0 + ch[hf];
       if (part < 0) {
         const float f = a.v_scale / l_tot[hf];
@@ -531,7 +535,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
           *(uint2 *)(orow + 16 * dg) = w;
         }
       } else {
-        const int slot = part + ct[hf] * stride;
+        const int slot = kind == 2 ? a.row_slot0[token + ct[hf]] + part : part + ct[hf] * stride;
         float *po = a.part_o + ((int64_t)slot * a.num_q_heads + qh) * D + 4 * j;
 #pragma unroll
         for (int dg = 0; dg < NDG; ++dg) {
@@ -561,7 +565,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     const int kv_last = own ? kv_end - 1 : kv_end;
     // a kind-1 piece that stores its rows' K/V first is not read ahead
     const bool stores_rows = ikind == 1 && a.knew != nullptr && kv_end == iaux;
-    const int32_t *__restrict__ btrow = a.block_table + (int64_t)req * a.bt_stride;
+    const int32_t *__restrict__ btrow = ikind == 2 ? a.prefix_bt : a.block_table + (int64_t)req * a.bt_stride;
     // ---- block ids: lane group j reads block j of a step ----
     // (the read itself is unconditional, at an index clamped to the row's last
     // block, so that no branch sits between the step's loads)

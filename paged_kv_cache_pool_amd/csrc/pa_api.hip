@@ -445,6 +445,7 @@ struct Plan {
   int32_t kstart = 0;                            // first key of the split-K items (the cascade's prefix end)
   int32_t pair_stride = 0;                       // paired layout: items b and pair_stride + b share a wave
   int32_t max_cols = 0;                          // largest (row, head) column count of a decode item
+  bool pre_dec = false;                          // the prefix rows' prefix attention as kind-2 decode items
   size_t off_dec = 0, off_merge = 0, off_extw = 0, off_pre = 0, off_rtok = 0, off_rslot = 0, off_wseg = 0;
   size_t off_ml = 0, off_o = 0, bytes = 0;
 };
@@ -530,6 +531,25 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
   const int32_t kstart = cascade ? P : 0;        // first key of the split-K rows' own work
   plan.kstart = kstart;
 
+  // The prefix rows' attention over the shared prefix: by the split-K kernel
+  // as kind-2 items (units of 16 / g prefix rows, one MFMA column per (row,
+  // q head), packed with the rows' own work into one launch) while the
+  // prefix rows have at most kPrefixDecodeCols columns per kv head;
+  // otherwise (or with PA_PREFIX_PASS=1) by the MFMA prefix pass.  On the
+  // fp8 shared-prefix workload (128 rows, g = 4, a 2048-key prefix) the step
+  // takes 0.050 ms against 0.058 with the prefix pass, whose launch, the
+  // split-K launch and the merge ran one after the other.  A prefix item
+  // reads each K/V byte for 16 columns where the prefix pass's tile feeds
+  // 128, so many prefix rows go to the prefix pass.
+  constexpr int64_t kPrefixDecodeCols = 1024;
+  bool any_multi = false;
+  for (int32_t i = 0; i < b.num_seqs && cascade; ++i) any_multi |= multi(q[i + 1] - q[i]);
+  const bool pre_dec = cascade && (int64_t)prefix_rows * g <= kPrefixDecodeCols && !any_multi &&
+                       !env_flag("PA_PREFIX_PASS");
+  const int32_t pre_rows = std::max(1, 16 / g);  // prefix rows per kind-2 unit
+  const int32_t n_pre_units = pre_dec ? (prefix_rows + pre_rows - 1) / pre_rows : 0;
+  plan.pre_dec = pre_dec;
+
   // Partition length of the split-K rows (a unit = one token's keys in one
   // partition, for one kv head: one wave).
   //  * One launch round: all units resident at once, at most 8 per compute
@@ -545,6 +565,11 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
   std::vector<int32_t> tok_keys;
   int64_t key_work = 0;
   int32_t max_keys = 0;
+  for (int32_t u = 0; u < n_pre_units; ++u) {   // kind-2 units first: keys [0, P)
+    tok_keys.push_back(P);
+    key_work += P;
+    max_keys = std::max(max_keys, P);
+  }
   for (int32_t i = 0; i < b.num_seqs; ++i) {
     const int32_t c = q[i + 1] - q[i];
     if (c == 0 || on_ext(c)) continue;
@@ -645,7 +670,13 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
     }
   }
   const bool paired = pair_T > 0;
-  const bool pair_waves = getenv("PA_DECODE_PAIRS") && atoi(getenv("PA_DECODE_PAIRS")) == 2;
+  // two waves per SIMD by default when prefix items share the launch: their
+  // keys come from L2 and a step is bound by latency, which a second wave
+  // hides (measured on the fp8 shared-prefix workload: split-K launch 36 us
+  // against 52 us with one wave per SIMD; the prefix pass and a split-K
+  // launch of the rows' own keys took 20 + 26 us)
+  const char *pair_env = getenv("PA_DECODE_PAIRS");
+  const bool pair_waves = pair_env ? atoi(pair_env) == 2 : pre_dec;
   std::vector<std::array<int32_t, 4>> pieces;
   if (paired) {
     const int64_t m = bins_for(pair_T, &pieces);
@@ -689,7 +720,7 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
   // column blocks x chunks (a workgroup costs several microseconds to start
   // and finish, so one round of longer chunks beats two of shorter ones)
   int32_t n_kc = 0, kc_len = 0;
-  if (cascade) {
+  if (cascade && !pre_dec) {
     const int64_t ncb = ((int64_t)prefix_rows * g + kExtCols - 1) / kExtCols;
     const int64_t max_kc = (P + 63) / 64;
     n_kc = (int32_t)std::min<int64_t>(max_kc, std::max<int64_t>(1, 256 / (Hkv * ncb)));
@@ -701,16 +732,21 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
   // partial slots and the token's merge entry (outside the cascade a token of
   // one segment has none: its item writes the output).  own: the segment
   // that ends at the row's last key also writes the row's new K/V.
+  // prefix partials of a prefix row: the pieces of its kind-2 unit, or the
+  // prefix pass's chunks
+  std::vector<int32_t> pre_np;
+  auto npre = [&](size_t row_idx) { return pre_dec ? pre_np[row_idx / pre_rows] : n_kc; };
   auto emit_token = [&](int32_t tok, int32_t i, const int32_t *bnd, int32_t nseg, bool own) {
     auto wpos = [&](int32_t r) { return own && bnd[r + 1] == L[i] ? L[i] - 1 : -1; };
     if (cascade) {
-      // slots: the prefix chunks, then the segments of keys [P, nvis)
+      const int32_t n_pre = npre(plan.row_token.size());
+      // slots: the prefix partials, then the segments of keys [P, nvis)
       plan.row_token.push_back(tok);
       plan.row_slot0.push_back(plan.n_slots);
-      plan.merge.push_back(MergeItem{tok, plan.n_slots, n_kc + nseg, 0});
+      plan.merge.push_back(MergeItem{tok, plan.n_slots, n_pre + nseg, 0});
       for (int32_t r = 0; r < nseg; ++r)
-        plan.dec.push_back(DecodeItem{tok, i, bnd[r], bnd[r + 1], plan.n_slots + n_kc + r, wpos(r), 1, 0, 0});
-      plan.n_slots += n_kc + nseg;
+        plan.dec.push_back(DecodeItem{tok, i, bnd[r], bnd[r + 1], plan.n_slots + n_pre + r, wpos(r), 1, 0, 0});
+      plan.n_slots += n_pre + nseg;
     } else if (nseg == 1) {
       plan.dec.push_back(DecodeItem{tok, i, bnd[0], bnd[1], -1, wpos(0), 1, 0, 0});
     } else {
@@ -749,23 +785,36 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
   // key segments of a unit whose keys end at nvis: its pieces of the paired
   // layout (the packing visited the units in this order, with the same step
   // counts), or partitions of `part` keys from kstart
-  auto segments = [&](int32_t nvis) {
+  auto segments = [&](int32_t nvis, int32_t start) {
     bnd.clear();
     if (paired) {
-      const int64_t st = std::max<int64_t>(0, (int64_t)nvis - kstart + kKeysPerIter - 1) / kKeysPerIter;
-      bnd.push_back(std::min(nvis, kstart));
+      const int64_t st = std::max<int64_t>(0, (int64_t)nvis - start + kKeysPerIter - 1) / kKeysPerIter;
+      bnd.push_back(std::min(nvis, start));
       for (int64_t o = 0; o < st && piece_next < pieces.size();) {
         const auto &pc = pieces[piece_next++];
         o = pc[3];
-        bnd.push_back((int32_t)std::min<int64_t>(nvis, kstart + (int64_t)kKeysPerIter * o));
+        bnd.push_back((int32_t)std::min<int64_t>(nvis, start + (int64_t)kKeysPerIter * o));
         dec_pos.push_back(pc[0]);
       }
     } else {
-      for (int64_t k = kstart; k < nvis; k += part) bnd.push_back((int32_t)k);
+      for (int64_t k = start; k < nvis; k += part) bnd.push_back((int32_t)k);
       bnd.push_back(nvis);
     }
     if (bnd.size() == 1 && !cascade) bnd.insert(bnd.begin(), 0);
   };
+
+  // kind-2 units: prefix rows r0 .. r0 + nr - 1 (indices into the row list
+  // that the rows' own emission below builds in the same order), piece r's
+  // partial at slot row_slot0[row] + r
+  for (int32_t u = 0; u < n_pre_units; ++u) {
+    const int32_t r0 = u * pre_rows, nr = std::min(pre_rows, prefix_rows - r0);
+    segments(P, 0);
+    const int32_t nseg = (int32_t)bnd.size() - 1;
+    pre_np.push_back(nseg);
+    for (int32_t r = 0; r < nseg; ++r)
+      plan.dec.push_back(DecodeItem{r0, plan.prefix_req, bnd[r], bnd[r + 1], r, 0, (int16_t)nr, 2, 0});
+    plan.max_cols = std::max(plan.max_cols, nr * g);
+  }
 
   for (int32_t i = 0; i < b.num_seqs; ++i) {
     const int32_t c = q[i + 1] - q[i];
@@ -790,7 +839,7 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
       continue;
     }
     if (multi(c)) {
-      segments(L[i]);
+      segments(L[i], kstart);
       // the chunk's own keys [L - c, L) all in the last piece, which writes
       // them (the boundary moves down to the block holding key L - c; the
       // piece before it keeps at least 64 - 47 keys, since pieces other than
@@ -805,7 +854,7 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
     }
     for (int32_t t = 0; t < c; ++t) {
       const int32_t nvis = causal ? (L[i] - c + t + 1) : L[i];
-      segments(nvis);
+      segments(nvis, kstart);
       emit_token(q[i] + t, i, bnd.data(), (int32_t)bnd.size() - 1, own_write);
     }
     plan.max_cols = std::max(plan.max_cols, g);
@@ -952,7 +1001,7 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
 
   // Prefix items: all chunks of one kv head read the same blocks, so each kv
   // head is pinned to one XCD (workgroup b runs on XCD b % 8).
-  if (cascade) {
+  if (cascade && !pre_dec) {
     constexpr int kXcds = 8;
     std::vector<std::vector<PrefixItem>> qx(kXcds);
     const int32_t cols = prefix_rows * g;
@@ -1002,9 +1051,25 @@ static const char *check_decode_plan(const Plan &plan, const pa_batch &b, int ca
   const int32_t *q = b.query_start_loc_host, *L = b.seq_lens_host;
   struct Use { const DecodeItem *d; int32_t slot; };
   std::vector<std::vector<Use>> by_tok(b.num_tokens);
+  const int32_t n_rows = (int32_t)plan.row_token.size();
   for (const DecodeItem &d : plan.dec) {
+    if (d.kind < 0 || d.kind > 2) return "unknown item kind";
+    if (d.kind == 2) {
+      // prefix rows row_token[token ..] over keys of the common prefix
+      if (!plan.pre_dec) return "a prefix item without the prefix in the split-K kernel";
+      if (d.req != plan.prefix_req || d.token < 0 || d.ntok < 1 || d.token + d.ntok > n_rows) return "prefix item rows out of range";
+      if (d.kv_begin < 0 || d.kv_begin >= d.kv_end || d.kv_end > plan.kstart) return "prefix item keys outside the prefix";
+      if ((d.kv_begin % kBlock) != 0) return "a prefix piece that starts inside a block";
+      for (int32_t t = 0; t < d.ntok; ++t) {
+        const int32_t row = plan.row_token[d.token + t];
+        const int32_t slot = plan.row_slot0[d.token + t] + d.part;
+        if (row < 0 || row >= b.num_tokens) return "prefix row out of range";
+        if (d.part < 0 || slot >= plan.n_slots) return "prefix partial slot out of range";
+        by_tok[row].push_back(Use{&d, slot});
+      }
+      continue;
+    }
     if (d.req < 0 || d.req >= b.num_seqs || d.token < 0 || d.token >= b.num_tokens) return "item row out of range";
-    if (d.kind != 0 && d.kind != 1) return "unknown item kind";
     const int32_t c = q[d.req + 1] - q[d.req];
     const int32_t n = d.kind == 0 ? 1 : d.ntok;
     if (d.kind == 0 && d.ntok != 1) return "a one-row item with ntok != 1";
@@ -1025,15 +1090,22 @@ static const char *check_decode_plan(const Plan &plan, const pa_batch &b, int ca
       by_tok[d.token + t].push_back(Use{&d, slot});
     }
   }
+  // a row's keys start at 0, or after the prefix when the prefix pass covers it
+  const int32_t first_key = plan.pre_dec ? 0 : plan.kstart;
   std::vector<char> used(plan.n_slots, 0);
   for (int32_t t = 0; t < b.num_tokens; ++t) {
     auto &v = by_tok[t];
     if (v.empty()) continue;
     std::sort(v.begin(), v.end(), [](const Use &x, const Use &y) { return x.d->kv_begin < y.d->kv_begin; });
-    const int32_t i = v[0].d->req, c = q[i + 1] - q[i];
+    const DecodeItem *own = nullptr;          // an item of the row's own request
+    for (const Use &u : v)
+      if (u.d->kind != 2) own = u.d;
+    if (!own) return "a prefix row without its own keys";
+    const int32_t i = own->req, c = q[i + 1] - q[i];
+    if (t < q[i] || t >= q[i + 1]) return "a row's items belong to another request";
     const int32_t nvis = causal ? L[i] - c + (t - q[i]) + 1 : L[i];
-    const int32_t want_end = v[0].d->kind == 1 ? L[i] : nvis;
-    if (v.front().d->kv_begin != plan.kstart || v.back().d->kv_end != want_end) return "a row's items do not cover its keys";
+    const int32_t want_end = own->kind == 1 ? L[i] : nvis;
+    if (v.front().d->kv_begin != first_key || v.back().d->kv_end != want_end) return "a row's items do not cover its keys";
     for (size_t k = 0; k < v.size(); ++k) {
       if (k && v[k].d->kv_begin != v[k - 1].d->kv_end) return "a row's items overlap or leave a gap";
       const int32_t pt = v[k].slot;
@@ -1043,6 +1115,13 @@ static const char *check_decode_plan(const Plan &plan, const pa_batch &b, int ca
         used[pt] = 1;
       }
     }
+  }
+  // every slot a merge reads is written (the prefix pass's chunks count as
+  // written when it runs)
+  for (const MergeItem &m : plan.merge) {
+    if (m.first < 0 || m.count < 1 || m.first + m.count > plan.n_slots) return "merge slots out of range";
+    for (int32_t k = 0; k < m.count; ++k)
+      if (!used[m.first + k] && !(plan.kstart > 0 && !plan.pre_dec)) return "a merged slot that no item writes";
   }
   return nullptr;
 }
@@ -1206,8 +1285,9 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
     if (!plan.dec.empty()) memcpy(host + plan.off_dec, plan.dec.data(), plan.dec.size() * sizeof(DecodeItem));
     if (!plan.merge.empty()) memcpy(host + plan.off_merge, plan.merge.data(), plan.merge.size() * sizeof(MergeItem));
     if (!plan.extw.empty()) memcpy(host + plan.off_extw, plan.extw.data(), plan.extw.size() * sizeof(ExtendItem));
-    if (!plan.pre.empty()) {
-      memcpy(host + plan.off_pre, plan.pre.data(), plan.pre.size() * sizeof(PrefixItem));
+    if (!plan.pre.empty()) memcpy(host + plan.off_pre, plan.pre.data(), plan.pre.size() * sizeof(PrefixItem));
+    // the prefix row list: read by the prefix pass and by kind-2 decode items
+    if (!plan.row_token.empty()) {
       memcpy(host + plan.off_rtok, plan.row_token.data(), plan.row_token.size() * sizeof(int32_t));
       memcpy(host + plan.off_rslot, plan.row_slot0.data(), plan.row_slot0.size() * sizeof(int32_t));
     }
@@ -1350,6 +1430,11 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
     a.items = (const DecodeItem *)(items + plan.off_dec);
     a.pair_stride = plan.pair_stride;
     a.causal = causal;
+    if (plan.pre_dec) {
+      a.row_token = (const int32_t *)(items + plan.off_rtok);
+      a.row_slot0 = (const int32_t *)(items + plan.off_rslot);
+      a.prefix_bt = batch->block_table + (int64_t)plan.prefix_req * batch->bt_stride;
+    }
     a.max_cols = plan.max_cols;
     a.part_ml = (float *)(ws + plan.off_ml);
     a.part_o = (float *)(ws + plan.off_o);

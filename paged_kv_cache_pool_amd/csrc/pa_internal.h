@@ -26,10 +26,15 @@ constexpr int kWavesPerGroup = 4;    // waves per workgroup in the split-K kerne
 //    `req` (a short chunk, such as the draft tokens of a verify step); `wpos`
 //    is the key limit (exclusive) of the last of them, and with a causal mask
 //    row t sees keys below wpos - (ntok - 1 - t).
+//  * kind 2 (shared prefix): the rows row_token[token .. token + ntok - 1] of
+//    the prefix row list, over keys [kv_begin, kv_end) of the common prefix,
+//    walked through the block-table row `prefix_bt` (no mask: the prefix lies
+//    in every row's history); row t's partial goes to slot
+//    row_slot0[token + t] + part.
 // The matrix-core kernel gives each (row, q head) pair one MFMA column, so
-// ntok x g <= 32.  When `part` < 0 the range is every row's whole visible
-// range and the kernel writes the final output; otherwise row t's partial
-// (m, l, o) goes to slot part + t * stride.
+// ntok x g <= 32.  Kinds 0 and 1: when `part` < 0 the range is every row's
+// whole visible range and the kernel writes the final output; otherwise row
+// t's partial (m, l, o) goes to slot part + t * stride.
 struct DecodeItem {
   int32_t token;
   int32_t req;
@@ -141,6 +146,10 @@ struct DecodeArgs {
   float v_scale;          // 1 for non-fp8 pools
   int32_t zero;           // always 0 (used to keep per-step loads inside the loop)
   int32_t causal;         // kind 1 items: rows see keys up to their own position
+  // kind 2 items (shared prefix)
+  const int32_t *row_token;   // flat row of each prefix row
+  const int32_t *row_slot0;   // first partial slot of each prefix row
+  const int32_t *prefix_bt;   // block-table row whose leading entries are the common prefix
   int32_t max_cols;       // largest ntok x g over the items (matrix-core kernel: <= 32)
   // KV update of items with wpos >= 0 (null knew: no update in this launch)
   const void *knew;       // [T][Hkv][D] new K rows (query dtype)

@@ -166,14 +166,18 @@ def test_fused_decode_partitions_and_verify_rows(R, monkeypatch, kv, route, pair
     _check_out(w, fused)
 
 
+@pytest.mark.parametrize("prefix_pass", ["", "1"])
 @pytest.mark.parametrize("pairs", ["0", "1", "2"])
 @pytest.mark.parametrize("kv", [W.BF16, W.FP8])
-def test_fused_cascade(R, monkeypatch, kv, pairs):
-    """The shared-prefix pass with the KV update: the decode rows' own keys
-    (written inside the split-K kernel) follow the prefix; partition form or
-    paired layout (one wave per bin or per piece)."""
+def test_fused_cascade(R, monkeypatch, kv, pairs, prefix_pass):
+    """The shared prefix with the KV update: the decode rows' own keys
+    (written inside the split-K kernel) follow the prefix, whose attention
+    comes from prefix items of the split-K kernel or from the MFMA prefix
+    pass (PA_PREFIX_PASS=1); partition form or paired layout (one wave per
+    bin or per piece)."""
     monkeypatch.setenv("PA_DECODE_PAIRS", pairs)
-    say("fused cascade", kv, "pairs", pairs)
+    monkeypatch.setenv("PA_PREFIX_PASS", prefix_pass)
+    say("fused cascade", kv, "pairs", pairs, "prefix pass", prefix_pass)
     own = [0, 1, 17, 33, 60, 9, 5]
     w = W.build(f"fused_casc_{kv}", 11, num_q_heads=8, num_kv_heads=2, head_dim=128,
                 block_size=16, num_blocks=80, kv_dtype=kv, io_dtype=W.BF16,

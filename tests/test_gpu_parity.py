@@ -303,13 +303,16 @@ def _cascade_workload(kv, g, seed=11):
                    num_scheduled=ns, shared_prefix_tokens=48)
 
 
+@pytest.mark.parametrize("prefix_pass", ["", "1"])
 @pytest.mark.parametrize("kv", [W.BF16, W.FP8])
 @pytest.mark.parametrize("g", [1, 4, 8, 16])
-def test_cascade_shared_prefix(R, kv, g):
+def test_cascade_shared_prefix(R, monkeypatch, kv, g, prefix_pass):
     """Cascade attention: the rows' attention over the shared prefix comes from
-    the MFMA prefix pass and is merged with their own keys; equal to the
-    oracle (plain attention), with and without the hint."""
-    say("cascade", kv, "g", g)
+    prefix items of the split-K kernel (or, with PA_PREFIX_PASS=1, from the
+    MFMA prefix pass) and is merged with their own keys; equal to the oracle
+    (plain attention), with and without the hint."""
+    monkeypatch.setenv("PA_PREFIX_PASS", prefix_pass)
+    say("cascade", kv, "g", g, "prefix pass", prefix_pass)
     w = _cascade_workload(kv, g)
     assert w.shared_prefix_blocks == 3
     for hint in (True, False):
@@ -317,6 +320,33 @@ def test_cascade_shared_prefix(R, kv, g):
         step.run()
         torch.cuda.synchronize()
         _check_attention(w, step)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_cascade_many_rows(R, monkeypatch, case):
+    """Many decode rows over one shared prefix (40 .. 300 rows, g 1 .. 16, so
+    that the prefix rows' columns fall below and above the split-K kernel's
+    limit for prefix items), bf16 and fp8, in the paired layout and with
+    forced 64-key partitions (many prefix pieces per unit), causal: every row
+    against the oracle."""
+    rng = np.random.default_rng(900 + case)
+    kv = [W.BF16, W.FP8][case % 2]
+    g = [1, 4, 16, 8][(case // 2) % 4]
+    rows = [300, 40, 60, 150][(case // 2) % 4]
+    if case >= 6:
+        monkeypatch.setenv("PA_DECODE_PAIRS", "0")
+        monkeypatch.setenv("PA_PARTITION_KEYS", "64")
+    own = rng.integers(0, 200, rows)
+    P = 16 * int(rng.integers(4, 40))
+    say("cascade many rows", case, kv, "g", g, "rows", rows, "prefix", P)
+    w = W.build(f"casc_many_{case}", 900 + case, num_q_heads=2 * g, num_kv_heads=2, head_dim=128,
+                block_size=16, num_blocks=int(sum(-(-(P + o + 1) // 16) for o in own)) + 8,
+                kv_dtype=kv, io_dtype=W.BF16, num_computed=(P + own).astype(np.int32),
+                num_scheduled=np.ones(rows, np.int32), shared_prefix_tokens=P)
+    step = R.GpuStep(w)
+    step.run()
+    torch.cuda.synchronize()
+    _check_attention(w, step)
 
 
 def test_cascade_hint_ignored_when_not_history(R):
