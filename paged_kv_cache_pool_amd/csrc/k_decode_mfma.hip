@@ -221,6 +221,31 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     int crow[NH];
 #pragma unroll
     for (int hf = 0; hf < NH; ++hf) crow[hf] = kind == 2 ? a.row_token[token + ct[hf]] : token + ct[hf];
+    // ---- block ids: lane group j reads block j of a step ----
+    // (the read itself is unconditional, at an index clamped to the row's last
+    // block, so that no branch sits between the step's loads)
+    const int last_bi = kv_last > 0 ? (kv_last - 1) >> 4 : 0;
+    auto ids_of = [&](int itx) {
+      const int bi = (itx >> 4) + j;
+      const int id = btrow[bi < last_bi ? bi : last_bi];
+      return bi <= last_bi ? id : -1;
+    };
+    // ---- the first step's K/V: read before the Q operands and the new key's
+    // work below, so that their latency overlaps (the first step never reads
+    // the new key's slot).  A kind-1 piece that stores its rows' K/V reads
+    // after the stores. ----
+    auto issue_first = [&]() {
+      const int idv = ids_of(kv_begin);
+      b0 = blk(idv, 0), b1 = blk(idv, 1), b2 = blk(idv, 2), b3 = blk(idv, 3);
+      idv_next = ids_of(kv_begin + kKeysPerIter);
+      issue_k(kr, b0, b1, b2, b3);
+      asm volatile("" ::: "memory");              // K before V, as in the loop
+      issue_v(vr, b0, b1, b2, b3);
+      asm volatile("" ::: "memory");
+    };
+    const bool rows_first = kind == 1 && a.knew != nullptr && kv_end == aux;
+    if (!pre && !rows_first && kv_begin < kv_last) issue_first();
+
     // ---- Q^T operand of each half: column r = (row ct, head ch) (zero when invalid) ----
     // (invalid columns are cleared with a mask, not a branch: a branch around
     // a loaded register makes the compiler wait for each load in turn)
@@ -253,15 +278,6 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
       wblk = uniform(btrow[wpos / kBlock]);
     }
 
-    // ---- block ids: lane group j reads block j of a step ----
-    // (the read itself is unconditional, at an index clamped to the row's last
-    // block, so that no branch sits between the step's loads)
-    const int last_bi = kv_last > 0 ? (kv_last - 1) >> 4 : 0;
-    auto ids_of = [&](int itx) {
-      const int bi = (itx >> 4) + j;
-      const int id = btrow[bi < last_bi ? bi : last_bi];
-      return bi <= last_bi ? id : -1;
-    };
     float m_run[NH], l_run[NH];                    // per half, column r; l_run: this lane's keys only
     f32x4_t o[NH][NDG];
 #pragma unroll
@@ -344,7 +360,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     // the last piece, which ends at aux) stores the rows' K/V into the pool
     // first, and its key loop then reads them like any other key.  No other
     // wave reads those slots in this launch.
-    if (kind == 1 && a.knew != nullptr && kv_end == aux) {
+    if (rows_first) {
       constexpr int NCH = D / E;                 // 16-byte pool chunks per row
       for (int w = lane; w < ntok * NCH; w += 64) {
         const int t = w / NCH, chn = w - t * NCH;
@@ -363,16 +379,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
       asm volatile("" ::: "memory");             // and no read below moves above them
     }
 
-    // ---- the first step's K/V ----
-    if (!pre && kv_begin < kv_last) {
-      const int idv = ids_of(kv_begin);
-      b0 = blk(idv, 0), b1 = blk(idv, 1), b2 = blk(idv, 2), b3 = blk(idv, 3);
-      idv_next = ids_of(kv_begin + kKeysPerIter);
-      issue_k(kr, b0, b1, b2, b3);
-      asm volatile("" ::: "memory");              // K before V, as in the loop
-      issue_v(vr, b0, b1, b2, b3);
-      asm volatile("" ::: "memory");
-    }
+    // ---- the first step's K/V, when the rows' own keys came first ----
+    if (!pre && rows_first && kv_begin < kv_last) issue_first();
 
     // ---- key loop ----
     for (int it = kv_begin; it < kv_last; it += kKeysPerIter) {

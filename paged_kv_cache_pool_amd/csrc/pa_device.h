@@ -62,27 +62,26 @@ __device__ __forceinline__ f32x2_t fp8x2_to_f32(uint32_t w, bool hi_word) {
 // 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, exponent field 0
 // subnormal (m * 2^-9), largest finite magnitude 448 (code 0x7E), code 0x7F
 // (and 0xFF) NaN, no infinity.  Rounding: nearest, ties to even; magnitudes
-// of 448 or more saturate to 448; NaN encodes as 0x7F.
+// of 448 or more saturate to 448; NaN encodes as 0x7F.  Branch-free: the
+// normal, subnormal, saturated and NaN codes are all formed and one is
+// selected (early returns made the compiler emit four nested branches per
+// element, each with its exec-mask bookkeeping).
 __device__ __forceinline__ uint32_t e4m3_encode(float y) {
   const uint32_t u = __float_as_uint(y);
   const uint32_t sign = (u >> 24) & 0x80u;
   const uint32_t a = u & 0x7fffffffu;
-  if (a > 0x7f800000u) return 0x7fu;                    // NaN
-  if (a >= 0x43e00000u) return sign | 0x7eu;            // >= 448 (incl. inf)
-  if (a < 0x3c800000u) {                                // below 2^-6: subnormal codes
-    // value / 2^-9 rounded to the nearest integer, ties to even (0..8; 8 is
-    // the smallest normal, whose code is also 8)
-    const float q = __builtin_rintf(__uint_as_float(a) * 512.0f);
-    return sign | (uint32_t)q;
-  }
-  const uint32_t exp = (a >> 23) - 127 + 7;             // 1..15
-  const uint32_t man = a & 0x7fffffu;
-  uint32_t code = (exp << 3) | (man >> 20);
-  const uint32_t rem = man & 0xfffffu;
-  // round half to even on the 20 dropped bits; a carry into the exponent is
-  // the correct next code
-  code += (rem > 0x80000u || (rem == 0x80000u && (code & 1u))) ? 1u : 0u;
-  return sign | code;
+  // normal codes (2^-6 <= |y| < 448): exponent 1..15 and the top 3 mantissa
+  // bits, rounded half to even on the 20 dropped bits (a carry into the
+  // exponent is the correct next code)
+  const uint32_t code_n = (((a >> 23) - 120u) << 3) | ((a >> 20) & 7u);
+  const uint32_t rem = a & 0xfffffu;
+  const uint32_t up = (rem > 0x80000u ? 1u : 0u) | (rem == 0x80000u ? (code_n & 1u) : 0u);
+  // subnormal codes (|y| < 2^-6): |y| / 2^-9 rounded to the nearest integer,
+  // ties to even (0..8; 8 is the smallest normal, whose code is also 8)
+  const uint32_t code_s = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  uint32_t code = a < 0x3c800000u ? code_s : code_n + up;
+  code = a >= 0x43e00000u ? 0x7eu : code;       // >= 448 (incl. inf)
+  return a > 0x7f800000u ? 0x7fu : (sign | code);
 }
 
 // ---------------------------------------------------------------------------
