@@ -422,12 +422,40 @@ __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
   const float *ml = a.part_ml + ((int64_t)first * a.num_q_heads + qh) * 2;
   const int64_t ml_stride = (int64_t)a.num_q_heads * 2;
 
+  const int sub = lane / LPP, d4 = lane % LPP;
+  const float *po = a.part_o + ((int64_t)first * a.num_q_heads + qh) * D + 4 * d4;
+  const int64_t po_stride = (int64_t)a.num_q_heads * D;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  float m = -INFINITY, l = 0.0f;
+  if (count <= PPI * U && count <= 64) {
+    // few partials (the usual case): every read (the partial outputs and both
+    // (m, l) layouts) is issued at once, so the merge waits for one round trip
+    float4 v[U];
+    float mr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = sub + u * PPI;
+      const int rc = r < count ? r : 0;          // in range; its weight is dropped below
+      v[u] = *(const float4 *)(po + rc * po_stride);
+      mr[u] = r < count ? ml[rc * ml_stride] : -INFINITY;
+    }
+    const float m_lane = lane < count ? ml[lane * ml_stride] : -INFINITY;
+    const float l_lane = lane < count ? ml[lane * ml_stride + 1] : 0.0f;
+    m = wave_max_dpp(m_lane);
+    l = wave_sum_dpp(m_lane != -INFINITY ? fmaf(__builtin_amdgcn_exp2f(m_lane - m), l_lane, 0.0f) : 0.0f);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w = mr[u] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mr[u] - m);
+      acc.x = fmaf(w, v[u].x, acc.x);
+      acc.y = fmaf(w, v[u].y, acc.y);
+      acc.z = fmaf(w, v[u].z, acc.z);
+      acc.w = fmaf(w, v[u].w, acc.w);
+    }
+  } else {
   // m = max_r m_r, l = sum_r 2^(m_r - m) l_r (a partial without keys has m_r = -inf)
-  float m = -INFINITY;
   for (int r0 = 0; r0 < count; r0 += 64)
     if (r0 + lane < count) m = fmaxf(m, ml[(r0 + lane) * ml_stride]);
   m = wave_max_dpp(m);
-  float l = 0.0f;
   for (int r0 = 0; r0 < count; r0 += 64) {
     const int r = r0 + lane;
     if (r < count) {
@@ -438,10 +466,6 @@ __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
   l = wave_sum_dpp(l);
 
   // O = sum_r 2^(m_r - m) o_r / l
-  const int sub = lane / LPP, d4 = lane % LPP;
-  const float *po = a.part_o + ((int64_t)first * a.num_q_heads + qh) * D + 4 * d4;
-  const int64_t po_stride = (int64_t)a.num_q_heads * D;
-  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   for (int r0 = sub; r0 < count; r0 += PPI * U) {
     float4 v[U];
     float mr[U];
@@ -460,6 +484,7 @@ __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
       acc.z = fmaf(w, v[u].z, acc.z);
       acc.w = fmaf(w, v[u].w, acc.w);
     }
+  }
   }
   // sum the PPI groups (lanes d4, d4 + LPP, ...)
 #pragma unroll
