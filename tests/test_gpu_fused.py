@@ -301,7 +301,7 @@ def test_spec_verify_workload(R, monkeypatch, route):
 # ------------------------------------------------------------- HIP graphs --
 
 @pytest.mark.parametrize("plan_copy", ["", "1"])
-@pytest.mark.parametrize("cfg,fused", [(1, True), (1, False), (2, True), (6, True)])
+@pytest.mark.parametrize("cfg,fused", [(1, True), (1, False), (2, True), (5, True), (6, True)])
 def test_graph_capture_replays(R, monkeypatch, cfg, fused, plan_copy):
     """A step captured into a HIP graph (torch's stream capture around the
     library's calls) replays the same batch: every replay equals the eager

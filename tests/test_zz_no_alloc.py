@@ -2,10 +2,11 @@
 through the C ABI, against the entry point with a workspace
 (pa_write_kv_attention) on the same inputs.
 
-Two calls in a row on one device share the library's static scratch: the
-mixed 2048-token step (every kernel of the path: the scatter pass, the wide
-extend launch, the split-K decode and the merge), then a smaller batch (the
-source-map page's mixed batch).  Each call's slots, pool bytes and output
+Calls in a row on one device share the library's static scratch: the mixed
+2048-token step (every kernel of the path: the scatter pass, the wide extend
+launch, the split-K decode and the merge), the fp8 shared-prefix step (prefix
+items and the prefix row lists in the split-K launch), then a smaller batch
+(the source-map page's mixed batch).  Each call's slots, pool bytes and output
 must equal the workspace entry point's exactly (same plan, same kernels), and
 the output must match the oracle within the attention tolerance.  A batch
 whose plan does not fit the static scratch is refused before any launch.
@@ -43,7 +44,7 @@ def test_noalloc_matches_workspace_entry_point():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     from paged_kv_cache_pool_amd import binding as B
     from paged_kv_cache_pool_amd import runner
-    for w in (W.make(3), _page_mixed()):
+    for w in (W.make(3), W.make(5), _page_mixed()):
         say("workload", w.name, "tokens", w.num_tokens)
         ref_step = runner.GpuStep(w, fused=True)       # pa_write_kv_attention, own workspace
         ref_step.run()
