@@ -114,6 +114,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   static_assert(NH == 1 || NH == 2, "one or two column halves");
   constexpr bool F8 = KV == KV_FP8;
   constexpr bool PREFETCH = PAIR && NH == 1;     // the second item's first step read at the start
+  // the new key after the key loop in the paired form (one wave per SIMD):
+  // measured 4 % faster on the decode layer; the single-item forms keep it
+  // first (two waves per SIMD: registers for its inputs are short, and the
+  // fp8 shared-prefix step was 2 % slower with it last)
+  constexpr bool LATE_KEY = PAIR;
   constexpr int PB = KvTraits<KV>::bytes;
   constexpr int E = 16 / PB;                     // elements per 16-byte K chunk row
   constexpr int TILE = D * kBlock * PB;          // bytes per (block, head) tile
@@ -266,7 +271,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     // ---- the new key's inputs (kind 0) ----
     uint4 kin[NS];
     uint2 vin[NDG];
-    int wblk = -1;
+    int wblk_v = -1;                               // (made uniform after the key loop)
     if (wnew) {
       const int64_t th = (int64_t)token * a.num_kv_heads + kvh;
       const uint16_t *krow = (const uint16_t *)a.knew + th * D;
@@ -275,7 +280,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
       for (int c = 0; c < NS; ++c) kin[c] = *(const uint4 *)(krow + qdim(c));
 #pragma unroll
       for (int dg = 0; dg < NDG; ++dg) vin[dg] = *(const uint2 *)(vrow + dg * 16 + 4 * j);
-      wblk = uniform(btrow[wpos / kBlock]);
+      wblk_v = btrow[wpos / kBlock];
     }
 
     float m_run[NH], l_run[NH];                    // per half, column r; l_run: this lane's keys only
@@ -288,7 +293,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
       for (int dg = 0; dg < NDG; ++dg) o[hf][dg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
 
-    // ---- the new key (kind 0, half 0): first softmax step, then its rows into the pool ----
+    // ---- the new key (kind 0, half 0): one online-softmax update with the
+    // value the pool will hold, then its rows go into the pool.  With the
+    // state still empty (m = -inf, l = 0, o = 0) the update is exactly the
+    // first step (m = s, l = 1, o = v).  Where the registers allow it
+    // (LATE_KEY), it runs after the key loop (the online softmax does not
+    // depend on the order), which keeps the wait for its inputs and its
+    // encoding off the path to the first K/V. ----
+    auto new_key = [&]() {
+    const int wblk = wnew ? uniform(wblk_v) : -1;
     if (wnew && kvh == 0 && lane == 0 && a.slots_out)
       a.slots_out[token] = (int64_t)wblk * kBlock + wpos % kBlock;
     if (wnew && wblk >= 0 && wblk < a.num_blocks) {
@@ -305,8 +318,12 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
         }
       }
       sp = sum_x32(sum_x16(sp));
-      m_run[0] = sp * a.scale_log2;
-      l_run[0] = j == 0 ? 1.0f : 0.0f;
+      const float s_new = sp * a.scale_log2;
+      const float mn = fmaxf(m_run[0], s_new);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[0] - mn);   // 0 when the loop saw no key
+      const float p_new = __builtin_amdgcn_exp2f(s_new - mn);
+      l_run[0] = l_run[0] * alpha + (j == 0 ? p_new : 0.0f);
+      m_run[0] = mn;
       uint32_t vb[NDG][4];
 #pragma unroll
       for (int dg = 0; dg < NDG; ++dg) {
@@ -314,7 +331,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           vb[dg][i] = pool_bits<KV_BF16, KV>((w[i >> 1] >> (16 * (i & 1))) & 0xffffu, a.enc_v_scale);
-          o[0][dg][i] = pool_value<KV>(vb[dg][i]);
+          o[0][dg][i] = fmaf(p_new, pool_value<KV>(vb[dg][i]), o[0][dg][i] * alpha);
         }
       }
       // K element d of slot off sits at (d / E) * 256 + off * 16 + (d % E) * PB
@@ -354,6 +371,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
         }
       }
     }
+    };
+    if constexpr (!LATE_KEY) new_key();
 
     // ---- kind 1, attention with the KV update: the piece holding the rows'
     // own keys (positions aux - ntok .. aux - 1; the plan puts all of them in
@@ -522,6 +541,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
       b0 = n0, b1 = n1, b2 = n2, b3 = n3;
       idv_next = idv_next2;
     }
+
+    if constexpr (LATE_KEY) new_key();
 
     // ---- totals and output: lane (r, j) holds dims 16 dg + 4 j + i of its column ----
     float l_tot[NH];
