@@ -108,42 +108,50 @@ __global__ __launch_bounds__(256) void k_write_new(const WriteArgs a) {
   constexpr int TILE = D * kBlock * PB;     // bytes of one (block, head) tile
   constexpr int NVEC = TILE / 16;           // 16-byte vectors per tile
   __shared__ __attribute__((aligned(16))) uint8_t vt[TILE];
-  __shared__ WriteSeg seg_s;
-  __shared__ int32_t blk_s;
 
+  // The input rows are read first, the block id after them: the rows
+  // depend on the segment only, so both reads are in flight together and the
+  // workgroup waits for one round trip instead of two.
+  constexpr int NIT = (kBlock * NCH + 255) / 256;   // chunks per thread (a segment holds <= 16 tokens)
   const int tid = threadIdx.x;
   const int h = (int)(blockIdx.x % (unsigned)a.num_kv_heads);
   const int si = (int)(blockIdx.x / (unsigned)a.num_kv_heads);
-  if (tid == 0) {
-    const WriteSeg sg = a.segs[si];
-    seg_s = sg;
-    blk_s = a.block_table[(int64_t)sg.req * a.bt_stride + sg.pos0 / kBlock];
-  }
-  __syncthreads();
-  const WriteSeg sg = seg_s;
-  const int blk = blk_s;
+  const WriteSeg sg = a.segs[si];
   const int off0 = sg.pos0 % kBlock;
-  if (a.slots_out && h == 0 && tid < sg.count)
-    a.slots_out[sg.tok0 + tid] = (int64_t)blk * kBlock + off0 + tid;
-  if (blk < 0 || blk >= a.num_blocks) return;   // slot outside the pool: not written
-
+  KvChunkIn<IN, KV> in[NIT];
+#pragma unroll
+  for (int k = 0; k < NIT; ++k) {
+    const int w = tid + 256 * k;
+    if (w < sg.count * NCH) {
+      const int t = w / NCH, c = w % NCH;
+      const int64_t th = (int64_t)(sg.tok0 + t) * a.num_kv_heads + h;
+      in[k] = load_kv_chunk<IN, KV>((const char *)a.key + th * D * IB, (const char *)a.value + th * D * IB, c);
+    }
+  }
+  asm volatile("" ::: "memory");                 // the rows' reads are issued before the block id's
+  const int blk = a.block_table[(int64_t)sg.req * a.bt_stride + sg.pos0 / kBlock];
+  const bool in_pool = blk >= 0 && blk < a.num_blocks;   // else the slots are not written
   const int64_t tile = ((int64_t)blk * a.num_kv_heads + h) * TILE;
-  for (int w = tid; w < sg.count * NCH; w += blockDim.x) {
+#pragma unroll
+  for (int k = 0; k < NIT; ++k) {
+    const int w = tid + 256 * k;
+    if (w >= sg.count * NCH) continue;
     const int t = w / NCH, c = w % NCH;
-    const int64_t th = (int64_t)(sg.tok0 + t) * a.num_kv_heads + h;
-    const KvChunkIn<IN, KV> in = load_kv_chunk<IN, KV>((const char *)a.key + th * D * IB,
-                                                       (const char *)a.value + th * D * IB, c);
-    *(uint4 *)((char *)a.k_cache + tile + c * (kBlock * 16) + (off0 + t) * 16) = k_chunk_bits<IN, KV>(in, a.k_scale);
+    if (in_pool)
+      *(uint4 *)((char *)a.k_cache + tile + c * (kBlock * 16) + (off0 + t) * 16) = k_chunk_bits<IN, KV>(in[k], a.k_scale);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const uint32_t b = v_elem_bits<IN, KV>(in, e, a.v_scale);
+      const uint32_t b = v_elem_bits<IN, KV>(in[k], e, a.v_scale);
       uint8_t *p = vt + ((c * E + e) * kBlock + off0 + t) * PB;
       if constexpr (PB == 4) *(uint32_t *)p = b;
       else if constexpr (PB == 2) *(uint16_t *)p = (uint16_t)b;
       else *p = (uint8_t)b;
     }
   }
+  if (a.slots_out && h == 0 && tid < sg.count)
+    a.slots_out[sg.tok0 + tid] = (int64_t)blk * kBlock + off0 + tid;
   __syncthreads();
+  if (!in_pool) return;                          // (uniform: every thread returns)
   // a vector holds E consecutive slots of one dim row
   char *vdst = (char *)a.v_cache + tile;
   for (int w = tid; w < NVEC; w += blockDim.x) {
