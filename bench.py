@@ -69,7 +69,10 @@ def parse():
                     help="also time the other form of the step (same pool and inputs)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured once into a HIP graph and replayed "
-                         "(same batch every replay)")
+                         "(same batch every replay), and --graph-layers steps on as many pools "
+                         "(the attention layers of one model step) eagerly and as one graph")
+    ap.add_argument("--graph-layers", type=int, default=8,
+                    help="layers (each its own pool and inputs) of the multi-layer graph timing")
     return ap.parse_args()
 
 
@@ -502,6 +505,7 @@ def main():
         step.fused = not a.separate
 
     graph_ms = None
+    graph_layers = None
     if a.graph:
         # the step captured on a side stream, then replayed on the step's
         # stream: warm back-to-back replays, against the warm eager figure
@@ -527,6 +531,48 @@ def main():
         torch.cuda.synchronize()
         graph_ms = round(e0.elapsed_time(e1) / a.steps, 5)
         del g
+        # the attention layers of one model step: --graph-layers steps, each on
+        # its own pool and inputs, launched eagerly back to back against one
+        # graph holding all of them (launch gaps between layers are paid once
+        # per graph), warm, per layer
+        nl = max(1, a.graph_layers)
+        layers = [step] + [runner.GpuStep(w, stream=stream, fused=step.fused) for _ in range(nl - 1)]
+        for _ in range(a.warmup):
+            for ly in layers:
+                ly.run()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(a.steps):
+            for ly in layers:
+                ly.run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        eager_layer = e0.elapsed_time(e1) / (a.steps * nl)
+        gs.wait_stream(stream)
+        for ly in layers:
+            ly.stream = gs
+        with torch.cuda.stream(gs):
+            for ly in layers:
+                ly.run()
+        gs.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=gs):
+            for ly in layers:
+                ly.run()
+        for ly in layers:
+            ly.stream = stream
+        torch.cuda.synchronize()
+        for _ in range(a.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(a.steps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        graph_layers = {"layers": nl, "eager_ms_per_layer_warm": round(eager_layer, 5),
+                        "replay_ms_per_layer_warm": round(e0.elapsed_time(e1) / (a.steps * nl), 5)}
+        del g, layers
     del scratch
 
     T = w.num_tokens
@@ -636,6 +682,7 @@ def main():
         **({("ms_per_step_one_call" if a.separate else "ms_per_step_separate_calls"): other}
            if other is not None else {}),
         **({"ms_per_step_graph_replay_warm": graph_ms} if graph_ms is not None else {}),
+        **({"graph_layers": graph_layers} if graph_layers is not None else {}),
         "decode_kv_gbps": roof["achieved"] if dom == "k_decode" else None,
         "placement": placement,
     }

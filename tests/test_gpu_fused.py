@@ -351,6 +351,56 @@ def test_graph_capture_replays(R, monkeypatch, cfg, fused, plan_copy):
     assert not torch.equal(replayed.view(torch.uint8), eager.view(torch.uint8))
 
 
+@pytest.mark.parametrize("plan_copy", ["", "1"])
+def test_graph_of_several_layers(R, monkeypatch, plan_copy):
+    """The attention layers of one model step captured into one HIP graph:
+    four one-call steps, each on its own pool and inputs (a decode layer, a
+    mixed batch with a prefill chunk, the verify shape, the fp8 shared-prefix
+    shape, at reduced sizes), captured in turn on one stream.  Every replay
+    gives each layer's eager output bit for bit, with eager calls of another
+    batch between replays, and each matches the oracle; after new query
+    contents in two of the layers, the next replay matches the oracle for
+    them."""
+    monkeypatch.setenv("PA_GRAPH_PLAN_COPY", plan_copy)
+    ws = [W.llama8b_decode(seed=3, num_seqs=24, lo=100, hi=1200, num_blocks=2200),
+          W.mixed_step(seed=4, num_decode=12, lo=64, hi=900, chunk_a=96, chunk_b=200,
+                       chunk_b_cached=150, num_blocks=900),
+          W.spec_verify(seed=5, num_seqs=10, lo=80, hi=700, num_blocks=600),
+          W.prefix_fp8_decode(seed=6, num_seqs=20, prefix=256, lo=16, hi=120, num_blocks=400)]
+    s = torch.cuda.Stream()
+    layers = [R.GpuStep(w, stream=s, fused=True) for w in ws]
+    eager = []
+    for w, ly in zip(ws, layers):
+        say("layer", w.name)
+        with torch.cuda.stream(s):
+            ly.run()
+        s.synchronize()
+        _check_out(w, ly)
+        eager.append(ly.out.clone())
+    other = R.GpuStep(W.make(1, seed=7), fused=True)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for ly in layers:
+            ly.run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        say("several-layer graph replay", rep, "plan copy", plan_copy)
+        for ly in layers:
+            ly.out.fill_(float("nan"))
+        other.run()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, ly in enumerate(layers):
+            assert torch.equal(ly.out.view(torch.uint8), eager[k].view(torch.uint8)), (rep, k)
+    for k in (0, 2):
+        layers[k].query.mul_(0.5)
+    g.replay()
+    torch.cuda.synchronize()
+    for k, (w, ly) in enumerate(zip(ws, layers)):
+        _check_out(dataclasses.replace(w, query=_halved(w)) if k in (0, 2) else w, ly)
+
+
 def test_graph_capture_rejects_validation(R, monkeypatch):
     from paged_kv_cache_pool_amd import binding as B
     say("graph capture + PA_VALIDATE")
