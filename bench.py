@@ -346,7 +346,7 @@ def cascade_prefix(w, seq_lens, qsl, ext_min_rows=2, extend_on=True, hint=True):
 
 
 def algorithmic_work(w, seq_lens, qsl, ext_min_rows=2, extend_on=True, prefix=0, fused=False,
-                     prefix_in_decode=False):
+                     prefix_in_decode=False, scatter_in_decode=False):
     """Bytes the split-K decode kernel must move, flops the extend kernel must
     do and flops of the shared-prefix attention, per step, by the per-unit
     formulas in the design notes.  With a shared prefix of `prefix` keys, the
@@ -354,7 +354,11 @@ def algorithmic_work(w, seq_lens, qsl, ext_min_rows=2, extend_on=True, prefix=0,
     kv head when the split-K launch computes the prefix part itself
     (`prefix_in_decode`).  In the step with the KV update (`fused`), a
     decode row of a one-token request takes its newest key from the input
-    rows and also writes them to the pool."""
+    rows and also writes them to the pool; when the split-K launch also
+    carries the scatter of the prefill chunks' rows (`scatter_in_decode`),
+    their input rows read and pool rows written count as its bytes too (a
+    chunk of at most 128 (row, head) columns per kv head writes its own rows
+    in the extend kernel)."""
     b_kv, b_io = ELEM[w.kv_dtype], ELEM[w.io_dtype]
     H, Hq, D, S = w.num_kv_heads, w.num_q_heads, w.head_dim, w.block_size
     dec_bytes = 0
@@ -369,6 +373,8 @@ def algorithmic_work(w, seq_lens, qsl, ext_min_rows=2, extend_on=True, prefix=0,
         if use_ext:
             ext_flops += 4 * Hq * D * sum(L - c + t + 1 for t in range(c))
             ext_bytes += L * H * D * 2 * b_kv + c * Hq * D * 2 * b_io
+            if scatter_in_decode and c * (Hq // H) > 128:
+                dec_bytes += c * H * D * 2 * (b_io + b_kv)
         else:
             for t in range(c):
                 Lv = L - c + t + 1
@@ -582,9 +588,13 @@ def main():
     ext_min = int(os.environ.get("PA_EXTEND_MIN_ROWS", "2"))
     prefix, prefix_in_decode = cascade_prefix(w, sl, qsl, ext_min, ext_on,
                                               hint=step.batch.num_common_prefix_blocks > 0)
+    # the scatter of the chunks' rows rides in the split-K launch when no
+    # launch of its own ran (one-call step with split-K rows)
+    scatter_in_decode = (not a.separate and "k_decode" in kernels and "k_write_new" not in kernels
+                         and "k_extend" in kernels)
     dec_bytes, ext_flops, ext_bytes, pre_flops = algorithmic_work(
         w, sl, qsl, ext_min, ext_on and "k_extend" in kernels, prefix, fused=not a.separate,
-        prefix_in_decode=prefix_in_decode)
+        prefix_in_decode=prefix_in_decode, scatter_in_decode=scatter_in_decode)
 
     # dominant kernel: the attention kernel that takes the longer time.  The
     # extend kernel is priced against MFMA when its work is compute-heavy

@@ -137,7 +137,21 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   // PAIR: wave (bin, kv head) runs item bin, then item pair_stride + bin when
   // there is one.  Otherwise one item per wave.
   const int n_first = PAIR ? a.pair_stride : a.n_items;
-  if (unit >= n_first * a.num_kv_heads) return;
+  if (unit >= n_first * a.num_kv_heads) {
+    // a scatter workgroup: no decode unit reads these rows, so they are
+    // written beside the decode work (in the launch's tail, as compute units
+    // free up) instead of by a launch of their own before it
+    const int u = unit - n_first * a.num_kv_heads;
+    if (u < a.n_wseg_units) {
+      __shared__ __attribute__((aligned(16))) uint8_t vt[TILE];
+      const int h = u % a.num_kv_heads;
+      const WriteSeg sg = a.wseg[u / a.num_kv_heads];
+      scatter_segment<KV_BF16, KV, D, 64>(sg.req, sg.tok0, sg.pos0, sg.count, h, a.num_kv_heads, a.knew, a.vnew,
+                                          a.block_table, a.bt_stride, a.num_blocks, a.k_store, a.v_store,
+                                          a.enc_k_scale, a.enc_v_scale, a.slots_out, vt, threadIdx.x);
+    }
+    return;
+  }
   const int bin = unit / a.num_kv_heads;
   const int kvh = unit - bin * a.num_kv_heads;
   const int g = a.g;
@@ -650,7 +664,8 @@ static void launch_pair(const DecodeArgs &a, bool pair, int nh, dim3 grid, dim3 
 
 hipError_t launch_decode_mfma(const pa_kv_pool &p, const DecodeArgs &a, hipStream_t s) {
   const bool pair = a.pair_stride > 0;
-  const int units = (pair ? a.pair_stride : a.n_items) * a.num_kv_heads;
+  static_assert(kDecodeWaves == 1, "scatter workgroups follow the decode units one to one");
+  const int units = (pair ? a.pair_stride : a.n_items) * a.num_kv_heads + a.n_wseg_units;
   const dim3 grid((units + kDecodeWaves - 1) / kDecodeWaves), block(64 * kDecodeWaves);
   const int nh = a.max_cols > 16 ? 2 : 1;
   if (p.kv_dtype == PA_BF16 && p.head_dim == 128) launch_pair<KV_BF16, 128>(a, pair, nh, grid, block, s);

@@ -90,85 +90,19 @@ __global__ __launch_bounds__(256) void k_write_kv(const void *__restrict__ key,
 // block.  Token n of the segment at position p goes to slot
 // block_table[req][p / 16] * 16 + p % 16, which is also stored to slots_out[n]
 // when that pointer is set.  One workgroup per (segment, kv head) fills the
-// segment's slots of the head's K and V tiles:
-//  K: one thread per (token, 16-byte chunk), one 16-byte store each (the
-//     chunks of consecutive slots are contiguous in the chunk-major tile);
-//  V: the tokens' elements are first placed in LDS in the tile's own
-//     dimension-major layout, then the tile is written as 16-byte vectors;
-//     a vector that also covers slots outside the segment is written
-//     element by element, leaving the other slots untouched.
-// Used by the attention call that includes the KV update.
+// segment's slots of the head's K and V tiles (scatter_segment).  Used by the
+// attention call that includes the KV update when no split-K launch carries
+// the segments.
 template <int IN, int KV, int D>
 __global__ __launch_bounds__(256) void k_write_new(const WriteArgs a) {
   const StagingRelease staging_release{a.release};
-  constexpr int IB = KvTraits<IN>::bytes;
-  constexpr int PB = KvTraits<KV>::bytes;
-  constexpr int E = 16 / PB;                // elements per 16 bytes of the pool
-  constexpr int NCH = D / E;                // chunks per key row
-  constexpr int TILE = D * kBlock * PB;     // bytes of one (block, head) tile
-  constexpr int NVEC = TILE / 16;           // 16-byte vectors per tile
-  __shared__ __attribute__((aligned(16))) uint8_t vt[TILE];
-
-  // The input rows are read first, the block id after them: the rows
-  // depend on the segment only, so both reads are in flight together and the
-  // workgroup waits for one round trip instead of two.
-  constexpr int NIT = (kBlock * NCH + 255) / 256;   // chunks per thread (a segment holds <= 16 tokens)
-  const int tid = threadIdx.x;
+  __shared__ __attribute__((aligned(16))) uint8_t vt[D * kBlock * KvTraits<KV>::bytes];
   const int h = (int)(blockIdx.x % (unsigned)a.num_kv_heads);
   const int si = (int)(blockIdx.x / (unsigned)a.num_kv_heads);
   const WriteSeg sg = a.segs[si];
-  const int off0 = sg.pos0 % kBlock;
-  KvChunkIn<IN, KV> in[NIT];
-#pragma unroll
-  for (int k = 0; k < NIT; ++k) {
-    const int w = tid + 256 * k;
-    if (w < sg.count * NCH) {
-      const int t = w / NCH, c = w % NCH;
-      const int64_t th = (int64_t)(sg.tok0 + t) * a.num_kv_heads + h;
-      in[k] = load_kv_chunk<IN, KV>((const char *)a.key + th * D * IB, (const char *)a.value + th * D * IB, c);
-    }
-  }
-  asm volatile("" ::: "memory");                 // the rows' reads are issued before the block id's
-  const int blk = a.block_table[(int64_t)sg.req * a.bt_stride + sg.pos0 / kBlock];
-  const bool in_pool = blk >= 0 && blk < a.num_blocks;   // else the slots are not written
-  const int64_t tile = ((int64_t)blk * a.num_kv_heads + h) * TILE;
-#pragma unroll
-  for (int k = 0; k < NIT; ++k) {
-    const int w = tid + 256 * k;
-    if (w >= sg.count * NCH) continue;
-    const int t = w / NCH, c = w % NCH;
-    if (in_pool)
-      *(uint4 *)((char *)a.k_cache + tile + c * (kBlock * 16) + (off0 + t) * 16) = k_chunk_bits<IN, KV>(in[k], a.k_scale);
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const uint32_t b = v_elem_bits<IN, KV>(in[k], e, a.v_scale);
-      uint8_t *p = vt + ((c * E + e) * kBlock + off0 + t) * PB;
-      if constexpr (PB == 4) *(uint32_t *)p = b;
-      else if constexpr (PB == 2) *(uint16_t *)p = (uint16_t)b;
-      else *p = (uint8_t)b;
-    }
-  }
-  if (a.slots_out && h == 0 && tid < sg.count)
-    a.slots_out[sg.tok0 + tid] = (int64_t)blk * kBlock + off0 + tid;
-  __syncthreads();
-  if (!in_pool) return;                          // (uniform: every thread returns)
-  // a vector holds E consecutive slots of one dim row
-  char *vdst = (char *)a.v_cache + tile;
-  for (int w = tid; w < NVEC; w += blockDim.x) {
-    const int s0 = (w * E) % kBlock;          // first slot of the vector
-    if (s0 >= off0 && s0 + E <= off0 + sg.count) {
-      *(uint4 *)(vdst + w * 16) = *(const uint4 *)(vt + w * 16);
-    } else if (s0 + E > off0 && s0 < off0 + sg.count) {
-      for (int e = 0; e < E; ++e) {
-        const int sl = s0 + e;
-        if (sl < off0 || sl >= off0 + sg.count) continue;
-        const int o = w * 16 + e * PB;
-        if constexpr (PB == 4) *(uint32_t *)(vdst + o) = *(const uint32_t *)(vt + o);
-        else if constexpr (PB == 2) *(uint16_t *)(vdst + o) = *(const uint16_t *)(vt + o);
-        else vdst[o] = (char)vt[o];
-      }
-    }
-  }
+  scatter_segment<IN, KV, D, 256>(sg.req, sg.tok0, sg.pos0, sg.count, h, a.num_kv_heads, a.key, a.value,
+                                  a.block_table, a.bt_stride, a.num_blocks, a.k_cache, a.v_cache, a.k_scale,
+                                  a.v_scale, a.slots_out, vt, threadIdx.x);
 }
 
 template <int IN, int KV>

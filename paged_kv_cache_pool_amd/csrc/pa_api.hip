@@ -440,6 +440,7 @@ struct Plan {
   // plan-driven scatter writes before the attention kernels (the others are
   // written by their decode unit, DecodeItem::wpos)
   std::vector<WriteSeg> wseg;
+  bool wseg_read_by_dec = false;                 // some split-K rows read keys the scatter writes
   int32_t n_slots = 0;
   int32_t part_len = 0;
   int32_t kstart = 0;                            // first key of the split-K items (the cascade's prefix end)
@@ -828,12 +829,14 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
     // last piece of a multi-row chunk
     const bool ext_self = kv_update && on_ext(c) && (int64_t)c * g <= kExtCols;
     const bool rows_self = kv_update && multi(c);
-    if (kv_update && !own_write && !ext_self && !rows_self)
+    if (kv_update && !own_write && !ext_self && !rows_self) {
+      plan.wseg_read_by_dec |= !on_ext(c);        // the request's own split-K rows read them
       for (int32_t pos = L[i] - c; pos < L[i];) {
         const int32_t end = std::min(L[i], (pos / kBlock + 1) * kBlock);
         plan.wseg.push_back(WriteSeg{i, q[i] + pos - (L[i] - c), pos, end - pos});
         pos = end;
       }
+    }
     if (on_ext(c)) {
       ext_reqs.push_back(i);
       continue;
@@ -1333,8 +1336,74 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
 
   hipError_t e = hipSuccess;
   // KV update, first part: the new rows no decode unit writes itself (slots
-  // derived on the fly), before any kernel that may read them
-  if (!plan.wseg.empty()) {
+  // derived on the fly), before any kernel that may read them.  When only
+  // extend items read them and there is split-K work on the matrix-core
+  // kernel, extra workgroups of that launch write them, and it runs before
+  // the extend and prefix kernels; otherwise (split-K rows of the same
+  // requests read them, PA_SCATTER_LAUNCH=1, fp32 pools, no split-K rows) a
+  // launch of its own does, first.
+  const bool fused_scatter = !plan.wseg.empty() && !plan.dec.empty() && !plan.wseg_read_by_dec &&
+                             pool->kv_dtype != PA_F32 && !fork && !env_flag("PA_SCATTER_LAUNCH");
+  // the split-K launch (with the scatter workgroups when it carries them)
+  auto run_decode = [&]() -> pa_status {
+    if (plan.dec.empty()) return PA_OK;
+    DecodeArgs a{};
+    a.q = query;
+    a.out = output;
+    a.k_cache = pool->k_cache;
+    a.v_cache = pool->v_cache;
+    a.block_table = batch->block_table;
+    a.items = (const DecodeItem *)(items + plan.off_dec);
+    a.pair_stride = plan.pair_stride;
+    a.causal = causal;
+    if (plan.pre_dec) {
+      a.row_token = (const int32_t *)(items + plan.off_rtok);
+      a.row_slot0 = (const int32_t *)(items + plan.off_rslot);
+      a.prefix_bt = batch->block_table + (int64_t)plan.prefix_req * batch->bt_stride;
+    }
+    a.max_cols = plan.max_cols;
+    a.part_ml = (float *)(ws + plan.off_ml);
+    a.part_o = (float *)(ws + plan.off_o);
+    a.n_items = (int32_t)plan.dec.size();
+    a.bt_stride = batch->bt_stride;
+    a.num_blocks = pool->num_blocks;
+    a.num_kv_heads = pool->num_kv_heads;
+    a.num_q_heads = num_q_heads;
+    a.g_total = g_total;
+    a.scale_log2 = softmax_scale * log2e * kscale;
+    a.v_scale = vscale;
+    if (kvu) {
+      a.knew = kvu->key;
+      a.vnew = kvu->value;
+      a.slots_out = kvu->slot_mapping;
+      a.k_store = pool->k_cache;
+      a.v_store = pool->v_cache;
+      a.enc_k_scale = kscale;
+      a.enc_v_scale = vscale;
+    }
+    if (fused_scatter) {
+      a.wseg = (const WriteSeg *)(items + plan.off_wseg);
+      a.n_wseg_units = (int32_t)plan.wseg.size() * pool->num_kv_heads;
+    }
+    // q heads per launch: the whole GQA group where the registers allow it,
+    // otherwise the group is covered by several launches (fp32 pools)
+    const int g_max = 16;
+    for (int h0 = 0; h0 < g_total; h0 += g_max) {
+      a.h0 = h0;
+      a.g = std::min(g_max, g_total - h0);
+      const int g_tmpl = a.g <= 1 ? 1 : a.g <= 2 ? 2 : a.g <= 4 ? 4 : a.g <= 8 ? 8 : 16;
+      a.release = release;
+      release = nullptr;
+      e = launch_decode(*pool, q_dtype, a, g_tmpl, s);
+      if (e != hipSuccess) return hip_fail(e, "k_decode launch");
+      a.knew = a.vnew = nullptr;                  // rows written by the first launch
+      a.slots_out = nullptr;
+      a.n_wseg_units = 0;
+    }
+    return PA_OK;
+  };
+  if (fused_scatter && (st = run_decode()) != PA_OK) return st;
+  if (!plan.wseg.empty() && !fused_scatter) {
     WriteArgs w{};
     w.key = kvu->key;
     w.value = kvu->value;
@@ -1420,56 +1489,7 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
     e = launch_prefix(*pool, x, s);
     if (e != hipSuccess) return hip_fail(e, "k_prefix launch");
   }
-  if (!plan.dec.empty()) {
-    DecodeArgs a{};
-    a.q = query;
-    a.out = output;
-    a.k_cache = pool->k_cache;
-    a.v_cache = pool->v_cache;
-    a.block_table = batch->block_table;
-    a.items = (const DecodeItem *)(items + plan.off_dec);
-    a.pair_stride = plan.pair_stride;
-    a.causal = causal;
-    if (plan.pre_dec) {
-      a.row_token = (const int32_t *)(items + plan.off_rtok);
-      a.row_slot0 = (const int32_t *)(items + plan.off_rslot);
-      a.prefix_bt = batch->block_table + (int64_t)plan.prefix_req * batch->bt_stride;
-    }
-    a.max_cols = plan.max_cols;
-    a.part_ml = (float *)(ws + plan.off_ml);
-    a.part_o = (float *)(ws + plan.off_o);
-    a.n_items = (int32_t)plan.dec.size();
-    a.bt_stride = batch->bt_stride;
-    a.num_blocks = pool->num_blocks;
-    a.num_kv_heads = pool->num_kv_heads;
-    a.num_q_heads = num_q_heads;
-    a.g_total = g_total;
-    a.scale_log2 = softmax_scale * log2e * kscale;
-    a.v_scale = vscale;
-    if (kvu) {
-      a.knew = kvu->key;
-      a.vnew = kvu->value;
-      a.slots_out = kvu->slot_mapping;
-      a.k_store = pool->k_cache;
-      a.v_store = pool->v_cache;
-      a.enc_k_scale = kscale;
-      a.enc_v_scale = vscale;
-    }
-    // q heads per launch: the whole GQA group where the registers allow it,
-    // otherwise the group is covered by several launches (fp32 pools)
-    const int g_max = 16;
-    for (int h0 = 0; h0 < g_total; h0 += g_max) {
-      a.h0 = h0;
-      a.g = std::min(g_max, g_total - h0);
-      const int g_tmpl = a.g <= 1 ? 1 : a.g <= 2 ? 2 : a.g <= 4 ? 4 : a.g <= 8 ? 8 : 16;
-      a.release = release;
-      release = nullptr;
-      e = launch_decode(*pool, q_dtype, a, g_tmpl, s);
-      if (e != hipSuccess) return hip_fail(e, "k_decode launch");
-      a.knew = a.vnew = nullptr;                  // rows written by the first launch
-      a.slots_out = nullptr;
-    }
-  }
+  if (!fused_scatter && (st = run_decode()) != PA_OK) return st;
   if (!plan.merge.empty()) {
     MergeArgs m{};
     m.out = output;

@@ -190,6 +190,88 @@ __device__ __forceinline__ void store_kv_chunk(const KvChunkIn<IN, KV> &in, void
   *(uint4 *)kdst = k_chunk_bits<IN, KV>(in, k_scale);
 }
 
+// One block segment of the scatter of new rows, for one kv head h: tokens
+// tok0 .. tok0 + count - 1 (count <= 16) of request req, at positions pos0 ..
+// in logical block pos0 / 16, go to slots block_table[req * bt_stride + pos0 /
+// 16] * 16 + pos0 % 16 + t (also stored to slots_out when it is set and
+// h == 0); a block id outside the pool leaves the pool untouched.  NT threads
+// (tid 0 .. NT - 1) of one workgroup; vt: LDS for the head's V tile.
+//  K: one thread per (token, 16-byte chunk), one 16-byte store each (the
+//     chunks of consecutive slots are contiguous in the chunk-major tile);
+//  V: the tokens' elements are first placed in LDS in the tile's own
+//     dimension-major layout, then the tile is written as 16-byte vectors;
+//     a vector that also covers slots outside the segment is written
+//     element by element, leaving the other slots untouched.
+// The input rows are read before the block id: they depend on the segment
+// only, so both reads are in flight together and the workgroup waits for one
+// round trip instead of two.
+template <int IN, int KV, int D, int NT>
+__device__ __forceinline__ void scatter_segment(int req, int tok0, int pos0, int count, int h, int num_kv_heads,
+                                                const void *key, const void *value, const int32_t *block_table,
+                                                int64_t bt_stride, int num_blocks, void *k_cache, void *v_cache,
+                                                float k_scale, float v_scale, int64_t *slots_out, uint8_t *vt,
+                                                int tid) {
+  constexpr int S = 16;                          // slots per block
+  constexpr int IB = KvTraits<IN>::bytes;
+  constexpr int PB = KvTraits<KV>::bytes;
+  constexpr int E = 16 / PB;                     // elements per 16 bytes of the pool
+  constexpr int NCH = D / E;                     // chunks per key row
+  constexpr int TILE = D * S * PB;               // bytes of one (block, head) tile
+  constexpr int NVEC = TILE / 16;                // 16-byte vectors per tile
+  constexpr int NIT = (S * NCH + NT - 1) / NT;   // chunks per thread
+  const int off0 = pos0 % S;
+  KvChunkIn<IN, KV> in[NIT];
+#pragma unroll
+  for (int k = 0; k < NIT; ++k) {
+    const int w = tid + NT * k;
+    if (w < count * NCH) {
+      const int t = w / NCH, c = w % NCH;
+      const int64_t th = (int64_t)(tok0 + t) * num_kv_heads + h;
+      in[k] = load_kv_chunk<IN, KV>((const char *)key + th * D * IB, (const char *)value + th * D * IB, c);
+    }
+  }
+  asm volatile("" ::: "memory");                 // the rows' reads are issued before the block id's
+  const int blk = block_table[(int64_t)req * bt_stride + pos0 / S];
+  const bool in_pool = blk >= 0 && blk < num_blocks;   // else the slots are not written
+  const int64_t tile = ((int64_t)blk * num_kv_heads + h) * TILE;
+#pragma unroll
+  for (int k = 0; k < NIT; ++k) {
+    const int w = tid + NT * k;
+    if (w >= count * NCH) continue;
+    const int t = w / NCH, c = w % NCH;
+    if (in_pool)
+      *(uint4 *)((char *)k_cache + tile + c * (S * 16) + (off0 + t) * 16) = k_chunk_bits<IN, KV>(in[k], k_scale);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const uint32_t b = v_elem_bits<IN, KV>(in[k], e, v_scale);
+      uint8_t *p = vt + ((c * E + e) * S + off0 + t) * PB;
+      if constexpr (PB == 4) *(uint32_t *)p = b;
+      else if constexpr (PB == 2) *(uint16_t *)p = (uint16_t)b;
+      else *p = (uint8_t)b;
+    }
+  }
+  if (slots_out && h == 0 && tid < count) slots_out[tok0 + tid] = (int64_t)blk * S + off0 + tid;
+  __syncthreads();
+  if (!in_pool) return;                          // (uniform: every thread returns)
+  // a vector holds E consecutive slots of one dim row
+  char *vdst = (char *)v_cache + tile;
+  for (int w = tid; w < NVEC; w += NT) {
+    const int s0 = (w * E) % S;                  // first slot of the vector
+    if (s0 >= off0 && s0 + E <= off0 + count) {
+      *(uint4 *)(vdst + w * 16) = *(const uint4 *)(vt + w * 16);
+    } else if (s0 + E > off0 && s0 < off0 + count) {
+      for (int e = 0; e < E; ++e) {
+        const int sl = s0 + e;
+        if (sl < off0 || sl >= off0 + count) continue;
+        const int o = w * 16 + e * PB;
+        if constexpr (PB == 4) *(uint32_t *)(vdst + o) = *(const uint32_t *)(vt + o);
+        else if constexpr (PB == 2) *(uint16_t *)(vdst + o) = *(const uint16_t *)(vt + o);
+        else vdst[o] = (char)vt[o];
+      }
+    }
+  }
+}
+
 // Wave-wide reductions (64 lanes).
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll

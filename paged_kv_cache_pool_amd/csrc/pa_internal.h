@@ -160,6 +160,12 @@ struct DecodeArgs {
   float enc_k_scale;      // pool scales for the fp8 encode, 1 otherwise
   float enc_v_scale;
   int32_t *release;       // or null: release flag of the stream's previous staging buffer
+  // The new rows of other requests (prefill chunks) scattered by extra
+  // one-wave workgroups after the decode ones (matrix-core kernel, attention
+  // with the KV update): workgroup n_dec + u writes segment u / num_kv_heads
+  // of wseg for kv head u % num_kv_heads, from knew / vnew.
+  const WriteSeg *wseg;
+  int32_t n_wseg_units;   // 0: none
 };
 
 struct MergeArgs {
