@@ -628,6 +628,19 @@ __global__ __launch_bounds__(512, 1) void k_extend_wide(const ExtendArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
+  if (blockIdx.x >= (unsigned)a.n_items) {
+    // a merge workgroup (the extend items come first, so these run in the
+    // launch's tail as compute units free up): one (merge item, q head) per wave
+    const int unit = (int)(blockIdx.x - a.n_items) * 8 + wave;
+    if (unit < a.n_merge_units) {
+      const int mi = unit / a.num_q_heads;
+      const int qh = unit - mi * a.num_q_heads;
+      const MergeItem it = a.mitems[mi];
+      merge_unit<kXD, false>(uniform(it.first), uniform(it.count), uniform(it.token), qh, a.num_q_heads,
+                             a.part_ml, a.part_o, a.out, lane);
+    }
+    return;
+  }
   const int g = a.g;
   const ExtendItem item = a.items[blockIdx.x];
   if (uniform(item.mode) != 0) {                 // a key-split item (kExtCols columns)
@@ -880,7 +893,7 @@ static hipError_t launch_wide_t(int n, const ExtendArgs &a, hipStream_t s) {
     }
   }
   prof_begin("k_extend", s);
-  hipLaunchKernelGGL((k_extend_wide<KV>), dim3(n), dim3(512), kWLds, s, a);
+  hipLaunchKernelGGL((k_extend_wide<KV>), dim3(n + (a.n_merge_units + 7) / 8), dim3(512), kWLds, s, a);
   prof_end(s);
   return hipGetLastError();
 }

@@ -441,6 +441,7 @@ struct Plan {
   // written by their decode unit, DecodeItem::wpos)
   std::vector<WriteSeg> wseg;
   bool wseg_read_by_dec = false;                 // some split-K rows read keys the scatter writes
+  bool ext_merge = false;                        // some merge items combine extend key pieces
   int32_t n_slots = 0;
   int32_t part_len = 0;
   int32_t kstart = 0;                            // first key of the split-K items (the cascade's prefix end)
@@ -938,6 +939,7 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
         const int32_t c = q[i + 1] - q[i];
         req_np[i] = (int32_t)std::max<int64_t>(1, std::min<int64_t>(np, tmin[i]));
         if (req_np[i] > 1) {
+          plan.ext_merge = true;
           req_base[i] = plan.n_slots;
           for (int32_t t = 0; t < c; ++t) plan.merge.push_back(MergeItem{q[i] + t, plan.n_slots + t * req_np[i], req_np[i], 0});
           plan.n_slots += c * req_np[i];
@@ -1402,8 +1404,9 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
     }
     return PA_OK;
   };
-  if (fused_scatter && (st = run_decode()) != PA_OK) return st;
-  if (!plan.wseg.empty() && !fused_scatter) {
+  // the scatter as a launch of its own
+  auto run_scatter = [&]() -> pa_status {
+    if (plan.wseg.empty() || fused_scatter) return PA_OK;
     WriteArgs w{};
     w.key = kvu->key;
     w.value = kvu->value;
@@ -1422,14 +1425,11 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
     release = nullptr;
     e = launch_write_new(*pool, q_dtype, w, s);
     if (e != hipSuccess) return hip_fail(e, "k_write_new launch");
-  }
-  // the extend kernel goes to the side stream when decode work runs beside it
-  if (fork) {
-    if ((e = hipEventRecord(side->fork, s)) != hipSuccess) return hip_fail(e, "fork record");
-    if ((e = hipStreamWaitEvent(side->stream, side->fork, 0)) != hipSuccess) return hip_fail(e, "fork wait");
-    xs = side->stream;
-  }
-  if (!plan.extw.empty()) {
+    return PA_OK;
+  };
+  // the extend launch, with the merge workgroups when it carries them
+  auto run_extend = [&](bool with_merge) -> pa_status {
+    if (plan.extw.empty()) return PA_OK;
     ExtendArgs x{};
     x.q = query;
     x.out = output;
@@ -1458,12 +1458,19 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
       x.enc_k_scale = kscale;
       x.enc_v_scale = vscale;
     }
+    if (with_merge) {
+      x.mitems = (const MergeItem *)(items + plan.off_merge);
+      x.n_merge_units = (int32_t)plan.merge.size() * num_q_heads;
+    }
     x.release = release;
     release = nullptr;
     e = launch_extend_wide(*pool, x, xs);
     if (e != hipSuccess) return hip_fail(e, "k_extend_wide launch");
-  }
-  if (!plan.pre.empty()) {
+    return PA_OK;
+  };
+  // the shared-prefix pass
+  auto run_prefix = [&]() -> pa_status {
+    if (plan.pre.empty()) return PA_OK;
     ExtendArgs x{};
     x.q = query;
     x.k_cache = pool->k_cache;
@@ -1488,9 +1495,11 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
     release = nullptr;
     e = launch_prefix(*pool, x, s);
     if (e != hipSuccess) return hip_fail(e, "k_prefix launch");
-  }
-  if (!fused_scatter && (st = run_decode()) != PA_OK) return st;
-  if (!plan.merge.empty()) {
+    return PA_OK;
+  };
+  // the merge as a launch of its own
+  auto run_merge = [&]() -> pa_status {
+    if (plan.merge.empty()) return PA_OK;
     MergeArgs m{};
     m.out = output;
     m.part_ml = (const float *)(ws + plan.off_ml);
@@ -1500,6 +1509,33 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
     m.num_q_heads = num_q_heads;
     e = launch_merge(q_dtype, pool->head_dim, m, s);
     if (e != hipSuccess) return hip_fail(e, "k_merge launch");
+    return PA_OK;
+  };
+
+  // Launch order.  The extend launch carries the merge of the split-K (and
+  // prefix-pass) partials when the extend items do not produce partials of
+  // their own (PA_MERGE_LAUNCH=1: a launch of its own), so the split-K launch
+  // and the prefix pass run before it; without the side stream the order is
+  // scatter (when not carried), split-K (with the carried scatter), prefix,
+  // extend (with the merge), merge (when not carried).
+  if (fork) {
+    // the extend kernel on the side stream, beside the split-K work
+    if ((st = run_scatter()) != PA_OK) return st;
+    if ((e = hipEventRecord(side->fork, s)) != hipSuccess) return hip_fail(e, "fork record");
+    if ((e = hipStreamWaitEvent(side->stream, side->fork, 0)) != hipSuccess) return hip_fail(e, "fork wait");
+    xs = side->stream;
+    if ((st = run_extend(false)) != PA_OK) return st;
+    if ((st = run_prefix()) != PA_OK) return st;
+    if ((st = run_decode()) != PA_OK) return st;
+    if ((st = run_merge()) != PA_OK) return st;
+  } else {
+    const bool merge_in_extend = !plan.merge.empty() && !plan.extw.empty() && !plan.ext_merge &&
+                                 !env_flag("PA_MERGE_LAUNCH");
+    if ((st = run_scatter()) != PA_OK) return st;
+    if ((st = run_decode()) != PA_OK) return st;
+    if ((st = run_prefix()) != PA_OK) return st;
+    if ((st = run_extend(merge_in_extend)) != PA_OK) return st;
+    if (!merge_in_extend && (st = run_merge()) != PA_OK) return st;
   }
   if (fork) {
     if ((e = hipEventRecord(side->join, xs)) != hipSuccess) return hip_fail(e, "join record");

@@ -348,4 +348,107 @@ __device__ __forceinline__ float wave_sum_dpp(float x) {
   return (lane_f32(x, 0) + lane_f32(x, 16)) + (lane_f32(x, 32) + lane_f32(x, 48));
 }
 
+// Merge of partitions: one wave per (token, q head).  Every lane reads one
+// partition's (m, l) (64 per round), so the maximum and the weights come from
+// one wave reduction instead of a chain of dependent loads; the partial
+// outputs are then summed with the weights.  Partials first .. first + count
+// - 1 of q head qh (m in log2 units, l, o with v_scale applied) -> output row
+// `token`.  Lanes are split into PPI groups of D / 4 lanes; group s takes
+// partials r = s, s + PPI, ... and each of its lanes 4 dims of them (one float4
+// per partial), so one load instruction reads PPI whole partials and each lane
+// keeps U of them in flight.
+template <int D, bool F32OUT>
+__device__ __forceinline__ void merge_unit(int first, int count, int token, int qh, int num_q_heads,
+                                           const float *part_ml, const float *part_o, void *out, int lane) {
+  constexpr int LPP = D / 4;                     // lanes per partial
+  constexpr int PPI = 64 / LPP;                  // partials per load instruction
+  constexpr int U = 8;
+  const float *ml = part_ml + ((int64_t)first * num_q_heads + qh) * 2;
+  const int64_t ml_stride = (int64_t)num_q_heads * 2;
+
+  const int sub = lane / LPP, d4 = lane % LPP;
+  const float *po = part_o + ((int64_t)first * num_q_heads + qh) * D + 4 * d4;
+  const int64_t po_stride = (int64_t)num_q_heads * D;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  float m = -INFINITY, l = 0.0f;
+  if (count <= PPI * U && count <= 64) {
+    // few partials (the usual case): every read (the partial outputs and both
+    // (m, l) layouts) is issued at once, so the merge waits for one round trip
+    float4 v[U];
+    float mr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = sub + u * PPI;
+      const int rc = r < count ? r : 0;          // in range; its weight is dropped below
+      v[u] = *(const float4 *)(po + rc * po_stride);
+      mr[u] = r < count ? ml[rc * ml_stride] : -INFINITY;
+    }
+    const float m_lane = lane < count ? ml[lane * ml_stride] : -INFINITY;
+    const float l_lane = lane < count ? ml[lane * ml_stride + 1] : 0.0f;
+    m = wave_max_dpp(m_lane);
+    l = wave_sum_dpp(m_lane != -INFINITY ? fmaf(__builtin_amdgcn_exp2f(m_lane - m), l_lane, 0.0f) : 0.0f);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w = mr[u] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mr[u] - m);
+      acc.x = fmaf(w, v[u].x, acc.x);
+      acc.y = fmaf(w, v[u].y, acc.y);
+      acc.z = fmaf(w, v[u].z, acc.z);
+      acc.w = fmaf(w, v[u].w, acc.w);
+    }
+  } else {
+    // m = max_r m_r, l = sum_r 2^(m_r - m) l_r (a partial without keys has m_r = -inf)
+    for (int r0 = 0; r0 < count; r0 += 64)
+      if (r0 + lane < count) m = fmaxf(m, ml[(r0 + lane) * ml_stride]);
+    m = wave_max_dpp(m);
+    for (int r0 = 0; r0 < count; r0 += 64) {
+      const int r = r0 + lane;
+      if (r < count) {
+        const float mr = ml[r * ml_stride];
+        if (mr != -INFINITY) l = fmaf(__builtin_amdgcn_exp2f(mr - m), ml[r * ml_stride + 1], l);
+      }
+    }
+    l = wave_sum_dpp(l);
+
+    // O = sum_r 2^(m_r - m) o_r / l
+    for (int r0 = sub; r0 < count; r0 += PPI * U) {
+      float4 v[U];
+      float mr[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int r = r0 + u * PPI;
+        const int rc = r < count ? r : r0;         // in range; its weight is dropped below
+        v[u] = *(const float4 *)(po + rc * po_stride);
+        mr[u] = r < count ? ml[rc * ml_stride] : -INFINITY;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float w = mr[u] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mr[u] - m);
+        acc.x = fmaf(w, v[u].x, acc.x);
+        acc.y = fmaf(w, v[u].y, acc.y);
+        acc.z = fmaf(w, v[u].z, acc.z);
+        acc.w = fmaf(w, v[u].w, acc.w);
+      }
+    }
+  }
+  // sum the PPI groups (lanes d4, d4 + LPP, ...)
+#pragma unroll
+  for (int o = LPP; o < 64; o <<= 1) {
+    acc.x += __shfl_xor(acc.x, o, 64);
+    acc.y += __shfl_xor(acc.y, o, 64);
+    acc.z += __shfl_xor(acc.z, o, 64);
+    acc.w += __shfl_xor(acc.w, o, 64);
+  }
+  if (sub != 0) return;
+  const float inv = 1.0f / l;
+  const int64_t idx = ((int64_t)token * num_q_heads + qh) * D + 4 * d4;
+  if constexpr (F32OUT) {
+    *(float4 *)((float *)out + idx) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  } else {
+    uint2 w2;
+    w2.x = (uint32_t)f32_to_bf16(acc.x * inv) | ((uint32_t)f32_to_bf16(acc.y * inv) << 16);
+    w2.y = (uint32_t)f32_to_bf16(acc.z * inv) | ((uint32_t)f32_to_bf16(acc.w * inv) << 16);
+    *(uint2 *)((uint16_t *)out + idx) = w2;
+  }
+}
+
 }  // namespace pa

@@ -211,6 +211,12 @@ struct ExtendArgs {
   float enc_k_scale;          // pool scales for the fp8 encode, 1 otherwise
   float enc_v_scale;
   int32_t *release;           // or null: release flag of the stream's previous staging buffer
+  // The merge of the split-K partials (of an earlier launch of the call)
+  // carried by extra workgroups after the extend items: workgroup n_items + b
+  // merges units 8 b .. 8 b + 7, unit u being q head u % num_q_heads of
+  // merge item u / num_q_heads, into `out`.
+  const MergeItem *mitems;
+  int32_t n_merge_units;      // 0: none
 };
 
 constexpr int kExtCols = 128;        // columns per extend workgroup (4 x 32, keys split over 2 waves)

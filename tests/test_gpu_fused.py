@@ -353,31 +353,43 @@ def test_graph_capture_replays(R, monkeypatch, cfg, fused, plan_copy):
 
 @pytest.mark.parametrize("kv", [W.BF16, W.FP8])
 @pytest.mark.parametrize("launch", ["", "1"])
-def test_scatter_carried_by_split_k_launch(R, monkeypatch, kv, launch):
-    """The one-call step's scatter of prefill-chunk rows: carried by
-    workgroups appended to the split-K launch (the default when only extend
-    items read the rows), or as a launch of its own (PA_SCATTER_LAUNCH=1).
-    Decode rows, chunks whose rows the extend items write themselves, and
-    wide chunks with history (ragged segments at both ends of a block).  Pool bytes and
-    slots equal the oracle's and the three-call form's, outputs match the
-    oracle, and the launch profile shows which form ran."""
+def test_scatter_and_merge_carried_by_other_launches(R, monkeypatch, kv, launch):
+    """The one-call step of a mixed batch: the scatter of prefill-chunk rows
+    is carried by workgroups appended to the split-K launch (the default when
+    only extend items read the rows), and the merge of the split-K partials by
+    workgroups appended to the extend launch; or each runs as a launch of its
+    own (PA_SCATTER_LAUNCH=1, PA_MERGE_LAUNCH=1).  Decode rows (long enough to
+    be cut into pieces), chunks whose rows the extend items write themselves,
+    and wide chunks with history (ragged segments at both ends of a block).
+    Pool bytes and slots equal the oracle's and the three-call form's,
+    outputs match the oracle, and the launch profile shows which form ran."""
     from paged_kv_cache_pool_amd import binding as B
     monkeypatch.setenv("PA_SCATTER_LAUNCH", launch)
-    say("scatter carried by the split-K launch, kv", kv, "own launch", launch)
+    monkeypatch.setenv("PA_MERGE_LAUNCH", launch)
+    monkeypatch.setenv("PA_PARTITION_KEYS", "128")
+    monkeypatch.setenv("PA_DECODE_PAIRS", "0")
+    say("scatter and merge carried by other launches, kv", kv, "own launches", launch)
     w = W.build(f"carried_{kv}", 21, num_q_heads=16, num_kv_heads=4, head_dim=128, block_size=16,
                 num_blocks=260, kv_dtype=kv, io_dtype=W.BF16,
                 num_computed=[300, 0, 77, 1000, 45, 513, 64],
                 num_scheduled=[1, 70, 1, 150, 9, 200, 1])
     B.profile_enable(True)
-    fused, sep = _fused_and_separate(R, w)
+    fused = R.GpuStep(w, fused=True)
+    fused.run()
     torch.cuda.synchronize()
     n_scatter, _ = B.profile_read("k_write_new")
+    n_merge, _ = B.profile_read("k_merge")
     B.profile_enable(False)
     assert (n_scatter == 0) == (launch == ""), n_scatter
+    assert (n_merge == 0) == (launch == ""), n_merge
+    sep = R.GpuStep(w)
+    sep.run()
+    torch.cuda.synchronize()
     assert (fused.slots.cpu().numpy() == sep.slots.cpu().numpy()).all()
     _assert_same_pool(fused.pool, sep.pool)
     _assert_pool_is_oracle(w, fused.pool)
     _check_out(w, fused)
+    _check_out(w, sep)
 
 
 @pytest.mark.parametrize("plan_copy", ["", "1"])
