@@ -376,7 +376,10 @@ const char *pa_last_error(void);
  * runs on.  pa_profile_read() waits for the recorded events and returns,
  * for the kernel named `kernel`, the number of launches and their summed
  * duration in milliseconds since the last reset.  Enabling or disabling
- * resets the records.  Launches captured into a HIP graph are not timed. */
+ * resets the records.  Launches captured into a HIP graph are not timed.
+ * Work that rides in another kernel's launch is timed with that launch: the
+ * one-call scatter of prefill rows in "k_decode" when no "k_write_new" runs,
+ * the merge of split-K partials in "k_extend" when no "k_merge" runs. */
 pa_status pa_profile_enable(int32_t enable);
 pa_status pa_profile_read(const char *kernel, int32_t *launches, double *total_ms);
 
