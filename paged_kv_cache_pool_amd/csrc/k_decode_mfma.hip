@@ -319,18 +319,67 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     if (wnew && kvh == 0 && lane == 0 && a.slots_out)
       a.slots_out[token] = (int64_t)wblk * kBlock + wpos % kBlock;
     if (wnew && wblk >= 0 && wblk < a.num_blocks) {
-      uint32_t kb[NS][8];
-      float sp = 0.0f;
+      uint32_t kb[NS][8], vb[NDG][4];
+      if constexpr (F8) {
+        // The 16 lanes of a lane group hold the same D / 4 input elements of
+        // K and of V; each encodes D / 64 of them, and the codes go round
+        // through LDS (the encoder's division and rounding would otherwise
+        // run 16 times over).
+        constexpr int EPL = D / 64;              // elements per lane
+        __shared__ __attribute__((aligned(16))) uint8_t codes[2][4][D / 4];   // [K, V][lane group][element]
 #pragma unroll
-      for (int c = 0; c < NS; ++c) {
-        const uint32_t w[4] = {kin[c].x, kin[c].y, kin[c].z, kin[c].w};
+        for (int u = 0; u < EPL; ++u) {
+          const int x = r * EPL + u;             // K element x: dims qdim(x / 8) + x % 8; V element x: 16 (x / 4) + 4 j + x % 4
+          uint32_t kw = 0, vw = 0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t raw = (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-          kb[c][e] = pool_bits<KV_BF16, KV>(raw, a.enc_k_scale);
-          sp = fmaf((float)qop[0][c][e], pool_value<KV>(kb[c][e]), sp);
+          for (int c = 0; c < NS; ++c)
+            if (c == (x >> 3)) {
+              const uint32_t w[4] = {kin[c].x, kin[c].y, kin[c].z, kin[c].w};
+#pragma unroll
+              for (int h = 0; h < 4; ++h)
+                if (h == ((x & 7) >> 1)) kw = w[h];
+            }
+#pragma unroll
+          for (int dg = 0; dg < NDG; ++dg)
+            if (dg == (x >> 2)) vw = (x & 2) ? vin[dg].y : vin[dg].x;
+          codes[0][j][x] = (uint8_t)pool_bits<KV_BF16, KV>((kw >> (16 * (x & 1))) & 0xffffu, a.enc_k_scale);
+          codes[1][j][x] = (uint8_t)pool_bits<KV_BF16, KV>((vw >> (16 * (x & 1))) & 0xffffu, a.enc_v_scale);
+        }
+        __syncthreads();                         // (one wave: the codes are in LDS)
+        uint32_t kw[D / 16], vw[D / 16];
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i) {
+          kw[i] = ((const uint32_t *)codes[0][j])[i];
+          vw[i] = ((const uint32_t *)codes[1][j])[i];
+        }
+#pragma unroll
+        for (int c = 0; c < NS; ++c)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) kb[c][e] = (kw[(8 * c + e) >> 2] >> (8 * (e & 3))) & 0xffu;
+#pragma unroll
+        for (int dg = 0; dg < NDG; ++dg)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vb[dg][i] = (vw[(4 * dg + i) >> 2] >> (8 * i)) & 0xffu;
+      } else {
+#pragma unroll
+        for (int c = 0; c < NS; ++c) {
+          const uint32_t w[4] = {kin[c].x, kin[c].y, kin[c].z, kin[c].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) kb[c][e] = pool_bits<KV_BF16, KV>((w[e >> 1] >> (16 * (e & 1))) & 0xffffu, a.enc_k_scale);
+        }
+#pragma unroll
+        for (int dg = 0; dg < NDG; ++dg) {
+          const uint32_t w[2] = {vin[dg].x, vin[dg].y};
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            vb[dg][i] = pool_bits<KV_BF16, KV>((w[i >> 1] >> (16 * (i & 1))) & 0xffffu, a.enc_v_scale);
         }
       }
+      float sp = 0.0f;
+#pragma unroll
+      for (int c = 0; c < NS; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sp = fmaf((float)qop[0][c][e], pool_value<KV>(kb[c][e]), sp);
       sp = sum_x32(sum_x16(sp));
       const float s_new = sp * a.scale_log2;
       const float mn = fmaxf(m_run[0], s_new);
@@ -338,16 +387,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
       const float p_new = __builtin_amdgcn_exp2f(s_new - mn);
       l_run[0] = l_run[0] * alpha + (j == 0 ? p_new : 0.0f);
       m_run[0] = mn;
-      uint32_t vb[NDG][4];
 #pragma unroll
-      for (int dg = 0; dg < NDG; ++dg) {
-        const uint32_t w[2] = {vin[dg].x, vin[dg].y};
+      for (int dg = 0; dg < NDG; ++dg)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          vb[dg][i] = pool_bits<KV_BF16, KV>((w[i >> 1] >> (16 * (i & 1))) & 0xffffu, a.enc_v_scale);
-          o[0][dg][i] = fmaf(p_new, pool_value<KV>(vb[dg][i]), o[0][dg][i] * alpha);
-        }
-      }
+        for (int i = 0; i < 4; ++i) o[0][dg][i] = fmaf(p_new, pool_value<KV>(vb[dg][i]), o[0][dg][i] * alpha);
       // K element d of slot off sits at (d / E) * 256 + off * 16 + (d % E) * PB
       // of the tile; V element d at (d * 16 + off) * PB
       const int off = wpos % kBlock;
