@@ -345,7 +345,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
           codes[0][j][x] = (uint8_t)pool_bits<KV_BF16, KV>((kw >> (16 * (x & 1))) & 0xffffu, a.enc_k_scale);
           codes[1][j][x] = (uint8_t)pool_bits<KV_BF16, KV>((vw >> (16 * (x & 1))) & 0xffffu, a.enc_v_scale);
         }
-        __syncthreads();                         // (one wave: the codes are in LDS)
+        // one wave per workgroup: its LDS writes are done once lgkmcnt is 0
+        // (no barrier, which would also wait for the first K/V in flight)
+        static_assert(kDecodeWaves == 1, "the codes' exchange is within one wave");
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         uint32_t kw[D / 16], vw[D / 16];
 #pragma unroll
         for (int i = 0; i < D / 16; ++i) {
