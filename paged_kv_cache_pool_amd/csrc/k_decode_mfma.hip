@@ -43,10 +43,13 @@
 // wave per SIMD); the single-item form keeps two waves per SIMD.
 //
 // KV update (items with wpos >= 0, the row's own new token at position
-// kv_end - 1): the new key enters the softmax first, with the value the pool
-// will hold (the scatter's own encoding), and its K/V rows are stored into
-// the pool; the key loop stops before it.  No wave reads that slot in this
-// launch.
+// kv_end - 1): the new key enters the softmax with the value the pool will
+// hold (the scatter's own encoding; before the key loop, or after it in the
+// paired form), and its K/V rows are stored into the pool; the key loop
+// stops before it.  No wave reads that slot in this launch.  One-wave
+// workgroups appended after the decode units may also scatter other
+// requests' new rows (prefill chunks read only by the extend kernel, which
+// runs after this launch).
 #include <type_traits>
 
 #include "pa_device.h"

@@ -41,6 +41,11 @@
 // conflicted one 8).
 // The copy writes lane i's 16 bytes at base + 16 i, so each lane's source
 // address is chosen to produce these layouts.
+//
+// The wide launch (k_extend_wide) also runs the wide layout (256 columns
+// per workgroup, below) and, after its extend items, workgroups that merge
+// the split-K partials of the same call (merge_unit), so that the merge needs
+// no launch of its own.
 #include <mutex>
 #include <vector>
 
