@@ -407,7 +407,7 @@ __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
   if (unit >= a.n_items * a.num_q_heads) return;
   const int item_idx = unit / a.num_q_heads;
   const int qh = unit - item_idx * a.num_q_heads;
-  const MergeItem it = a.items[item_idx];
+  const MergeItem it = a.inline_items ? a.inl[item_idx] : a.items[item_idx];
   merge_unit<D, F32OUT>(uniform(it.first), uniform(it.count), uniform(it.token), qh, a.num_q_heads, a.part_ml,
                         a.part_o, a.out, lane);
 }

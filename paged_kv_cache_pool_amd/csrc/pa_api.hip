@@ -1507,6 +1507,10 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
     m.items = (const MergeItem *)(items + plan.off_merge);
     m.n_items = (int32_t)plan.merge.size();
     m.num_q_heads = num_q_heads;
+    if (plan.merge.size() <= (size_t)kMergeInline) {
+      m.inline_items = 1;
+      memcpy(m.inl, plan.merge.data(), plan.merge.size() * sizeof(MergeItem));
+    }
     e = launch_merge(q_dtype, pool->head_dim, m, s);
     if (e != hipSuccess) return hip_fail(e, "k_merge launch");
     return PA_OK;
