@@ -392,6 +392,39 @@ def test_scatter_and_merge_carried_by_other_launches(R, monkeypatch, kv, launch)
     _check_out(w, sep)
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_carried_work_random(R, seed):
+    """Random mixed batches that take both carried paths by default: decode
+    rows over long histories (cut into pieces, so rows are merged) and
+    prefill chunks of more than 128 (row, head) columns per kv head with
+    history (their rows scattered by the split-K launch), bf16 and fp8 pools,
+    g in {1, 2, 4, 8, 16}.  One call against the three-call form (pool bytes
+    and slots exact) and against the oracle (every row)."""
+    rng = np.random.default_rng(seed + 900)
+    kv = [W.BF16, W.FP8][seed % 2]
+    g = [1, 2, 4, 8, 16][seed % 5]
+    hkv = int(rng.choice([1, 2, 4]))
+    n_dec = int(rng.integers(2, 9))
+    n_ext = int(rng.integers(1, 4))
+    lo_c = -(-129 // g)                          # more than 128 columns per kv head
+    nc = [int(x) for x in rng.integers(200, 2500, n_dec)] + [int(x) for x in rng.integers(0, 700, n_ext)]
+    ns = [1] * n_dec + [int(x) for x in rng.integers(lo_c, lo_c + 300, n_ext)]
+    order = rng.permutation(len(nc))
+    nc = [nc[k] for k in order]
+    ns = [ns[k] for k in order]
+    nb = sum(-(-(a + b) // 16) for a, b in zip(nc, ns)) + 16
+    say("carried random", seed, kv, "g", g, "hkv", hkv, "computed", nc, "scheduled", ns)
+    w = W.build(f"carried_rand_{seed}", seed + 900, num_q_heads=hkv * g, num_kv_heads=hkv, head_dim=128,
+                block_size=16, num_blocks=nb, kv_dtype=kv, io_dtype=W.BF16,
+                num_computed=nc, num_scheduled=ns)
+    fused, sep = _fused_and_separate(R, w)
+    assert (fused.slots.cpu().numpy() == sep.slots.cpu().numpy()).all()
+    _assert_same_pool(fused.pool, sep.pool)
+    _assert_pool_is_oracle(w, fused.pool)
+    _check_out(w, fused)
+    _check_out(w, sep)
+
+
 @pytest.mark.parametrize("plan_copy", ["", "1"])
 def test_graph_of_several_layers(R, monkeypatch, plan_copy):
     """The attention layers of one model step captured into one HIP graph:
