@@ -151,7 +151,7 @@ def traffic_ingest(a):
            "hbm_bytes_written": round(write_b), "hbm_bytes": round(read_b + write_b)}
     cmd = f"python bench.py --config {a.config} --steps 5 --warmup 2 --cpu-seconds 0"
     text = [f"# HBM traffic of {a.kernel}, workload {w.name}", "",
-            "Counters (one pass each, on the GPU box, from the repository root):", "",
+            "Counters (one pass each, on the MI355X, from the repository root):", "",
             "```",
             f"rocprofv3 --pmc FETCH_SIZE -d <fetch> -o run --output-format csv -- {cmd}",
             f"rocprofv3 --pmc WRITE_SIZE -d <write> -o run --output-format csv -- {cmd}",
@@ -226,7 +226,7 @@ def counters_ingest(a):
            "dispatches": n, "derived": {k: round(v, 4) for k, v in derived.items()}}
     cmd = f"python bench.py --config {a.config} --steps 5 --warmup 2 --cpu-seconds 0"
     text = [f"# Hardware counters of {a.kernel}, workload {w.name}", "",
-            "One rocprofv3 --pmc pass per counter group, on the GPU box, from the repository root:", "",
+            "One rocprofv3 --pmc pass per counter group, on the MI355X, from the repository root:", "",
             "```",
             f"rocprofv3 --pmc <counters of one pass> -d <pass folder> -o run --output-format csv -- {cmd}",
             f"python bench.py --config {a.config} --kernel {a.kernel} --counters-ingest <pass folders>",
