@@ -21,7 +21,9 @@ Prints one JSON line: tokens/s (whole step), the dominant kernel against its
 roofline (HIP events recorded around every launch on the stream it runs on,
 over K more cold steps), the extend kernel against the bf16 MFMA peak when
 the step has prefill rows, and the CPU oracle timed on this host on the same
-workload.
+workload.  Beside the published peaks, each roofline also gives its fraction
+of what plain device work reaches in the same run (a 1 GiB read for HBM, the
+vendor BLAS on an 8192^3 bf16 GEMM for MFMA; measured_ceilings).
 """
 import argparse
 import json
@@ -305,6 +307,43 @@ def trace_summary(a):
     print(path)
 
 
+def measured_ceilings(stream, scratch):
+    """What plain device work reaches on this GPU in the same run, beside the
+    published peaks: a 1 GiB read (torch's max over the cold-flush buffer), a
+    512 MiB device copy (bytes read + written) and an 8192^3 bf16 GEMM
+    (torch.mm, the vendor BLAS); medians of 10 timed runs after 3 untimed."""
+    import torch
+
+    def med_ms(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+        for e0, e1 in ev:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+
+    read_b = scratch.numel() * scratch.element_size()
+    t_read = med_ms(lambda: scratch.max())
+    src = torch.empty(1 << 29, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    t_copy = med_ms(lambda: dst.copy_(src))
+    del src, dst
+    n = 8192
+    x = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    y = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    t_mm = med_ms(lambda: torch.mm(x, y))
+    del x, y
+    return {"hbm_read_gbps": round(read_b / (t_read * 1e-3) / 1e9, 1),
+            "hbm_copy_gbps": round(2 * (1 << 29) / (t_copy * 1e-3) / 1e9, 1),
+            "bf16_gemm_tflops": round(2 * n ** 3 / (t_mm * 1e-3) / 1e12, 1),
+            "how": "1 GiB read (max), 512 MiB copy (read + written bytes), 8192^3 bf16 torch.mm; "
+                   "medians of 10"}
+
+
 def load_traffic(kernel, workload):
     """Measured HBM bytes per launch, or None when absent or taken on other sources."""
     path = traffic_record_path(kernel, workload)
@@ -579,6 +618,7 @@ def main():
         graph_layers = {"layers": nl, "eager_ms_per_layer_warm": round(eager_layer, 5),
                         "replay_ms_per_layer_warm": round(e0.elapsed_time(e1) / (a.steps * nl), 5)}
         del g, layers
+    ceilings = measured_ceilings(stream, scratch)
     del scratch
 
     T = w.num_tokens
@@ -633,6 +673,13 @@ def main():
                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                     "traffic": load_traffic("k_extend", w.name),
                     "algorithmic_flops_per_launch": ext_flops}
+
+    # the same achieved figures against what plain device work reaches here
+    for r in (roof, roof_ext):
+        if r is None:
+            continue
+        ceil = ceilings["hbm_read_gbps"] if r["bound"] == "hbm" else ceilings["bf16_gemm_tflops"]
+        r["frac_of_measured"] = round(r["achieved"] / ceil, 4)
 
     cpu = None
     if a.cpu_seconds > 0:
@@ -695,6 +742,7 @@ def main():
         **({"graph_layers": graph_layers} if graph_layers is not None else {}),
         "decode_kv_gbps": roof["achieved"] if dom == "k_decode" else None,
         "placement": placement,
+        "measured_ceilings": ceilings,
     }
     if dom == "k_decode":
         uniq = unique_kv_bytes(w, sl, qsl, 0 if prefix_in_decode else prefix)
