@@ -426,16 +426,30 @@ def algorithmic_work(w, seq_lens, qsl, ext_min_rows=2, extend_on=True, prefix=0,
     return dec_bytes, ext_flops, ext_bytes, pre_flops
 
 
-def unique_kv_bytes(w, seq_lens, qsl, prefix=0):
-    """K+V bytes of the distinct pool slots the decode rows read (a block shared
-    by several requests counts once; keys before `prefix` are the cascade
-    pass's): what HBM must deliver at least once."""
+def table_walk_kv_bytes(w, seq_lens, qsl, ext_min_rows=2, extend_on=True):
+    """K+V bytes of every split-K row's whole visible key range, each row
+    walking its own block table (a shared prefix counts once per row): the
+    per-request work that the shared-prefix pass takes over."""
+    b_kv, H, D = ELEM[w.kv_dtype], w.num_kv_heads, w.head_dim
+    total = 0
+    for i in range(w.num_seqs):
+        c, L = int(qsl[i + 1] - qsl[i]), int(seq_lens[i])
+        if c == 0 or (extend_on and c >= ext_min_rows and w.kv_dtype in ("bf16", "fp8") and D == 128):
+            continue
+        total += sum(L - c + t + 1 for t in range(c)) * H * D * 2 * b_kv
+    return total
+
+
+def unique_kv_bytes(w, seq_lens, qsl, prefix=0, ext_min_rows=2, extend_on=True):
+    """K+V bytes of the distinct pool slots the split-K rows read (a block
+    shared by several requests counts once; keys before `prefix` are the
+    cascade pass's): what HBM must deliver at least once."""
     b_kv = ELEM[w.kv_dtype]
     S = w.block_size
     seen = {}
     for i in range(w.num_seqs):
         c, L = int(qsl[i + 1] - qsl[i]), int(seq_lens[i])
-        if c == 0:
+        if c == 0 or (extend_on and c >= ext_min_rows and w.kv_dtype in ("bf16", "fp8") and w.head_dim == 128):
             continue
         for b in range(prefix // S, -(-L // S)):
             blk = int(w.block_table[i, b])
@@ -745,10 +759,18 @@ def main():
         "measured_ceilings": ceilings,
     }
     if dom == "k_decode":
-        uniq = unique_kv_bytes(w, sl, qsl, 0 if prefix_in_decode else prefix)
-        out["decode_kv_bytes_logical"] = dec_bytes
+        # pool K/V bytes by two counts beside the algorithmic ones: every row
+        # walking its own block table (logical), and the distinct slots read
+        # (unique); they differ where requests share blocks
+        t_us = kernels["k_decode"]["avg_us"]
+        logical = table_walk_kv_bytes(w, sl, qsl, ext_min, ext_on and "k_extend" in kernels)
+        uniq = unique_kv_bytes(w, sl, qsl, 0 if prefix_in_decode else prefix, ext_min,
+                               ext_on and "k_extend" in kernels)
+        out["decode_kv_bytes_algorithmic"] = dec_bytes
+        out["decode_kv_bytes_logical"] = logical
+        out["decode_kv_gbps_logical"] = round(logical / (t_us * 1e-6) / 1e9, 1)
         out["decode_kv_bytes_unique"] = uniq
-        out["decode_kv_gbps_unique"] = round(uniq / (kernels["k_decode"]["avg_us"] * 1e-6) / 1e9, 1)
+        out["decode_kv_gbps_unique"] = round(uniq / (t_us * 1e-6) / 1e9, 1)
     if prefix:
         out["prefix_keys"] = prefix
         out["prefix_attention"] = "split-K prefix items" if prefix_in_decode else "MFMA prefix pass"
