@@ -384,6 +384,13 @@ def cascade_prefix(w, seq_lens, qsl, ext_min_rows=2, extend_on=True, hint=True):
     return P, in_decode
 
 
+def multirow_chunk(w, c):
+    """Whether the library runs a chunk of c rows as one multi-row split-K item
+    (PA_MULTIROW=1: 2 <= c and c * g <= 32, bf16 and fp8 pools), as its plan does."""
+    on = os.environ.get("PA_MULTIROW", "0") not in ("", "0")
+    return on and w.kv_dtype != "f32" and c >= 2 and c * (w.num_q_heads // w.num_kv_heads) <= 32
+
+
 def algorithmic_work(w, seq_lens, qsl, ext_min_rows=2, extend_on=True, prefix=0, fused=False,
                      prefix_in_decode=False, scatter_in_decode=False):
     """Bytes the split-K decode kernel must move, flops the extend kernel must
@@ -397,7 +404,9 @@ def algorithmic_work(w, seq_lens, qsl, ext_min_rows=2, extend_on=True, prefix=0,
     carries the scatter of the prefill chunks' rows (`scatter_in_decode`),
     their input rows read and pool rows written count as its bytes too (a
     chunk of at most 128 (row, head) columns per kv head writes its own rows
-    in the extend kernel)."""
+    in the extend kernel).  A multi-row split-K item reads its request's K/V
+    once for all of its rows (and, in the step with the KV update, writes the
+    rows' new K/V first)."""
     b_kv, b_io = ELEM[w.kv_dtype], ELEM[w.io_dtype]
     H, Hq, D, S = w.num_kv_heads, w.num_q_heads, w.head_dim, w.block_size
     dec_bytes = 0
@@ -408,8 +417,14 @@ def algorithmic_work(w, seq_lens, qsl, ext_min_rows=2, extend_on=True, prefix=0,
         c, L = int(qsl[i + 1] - qsl[i]), int(seq_lens[i])
         if c == 0:
             continue
-        use_ext = extend_on and c >= ext_min_rows and w.kv_dtype in ("bf16", "fp8") and D == 128
-        if use_ext:
+        use_ext = (extend_on and c >= ext_min_rows and w.kv_dtype in ("bf16", "fp8") and D == 128
+                   and not multirow_chunk(w, c))
+        if multirow_chunk(w, c):
+            dec_bytes += (L - prefix) * H * D * 2 * b_kv + c * Hq * D * b_io + (-(-L // S) - prefix // S) * 4
+            if fused:
+                dec_bytes += c * H * D * 2 * (b_io + b_kv)
+            pre_flops += 4 * Hq * D * prefix * c
+        elif use_ext:
             ext_flops += 4 * Hq * D * sum(L - c + t + 1 for t in range(c))
             ext_bytes += L * H * D * 2 * b_kv + c * Hq * D * 2 * b_io
             if scatter_in_decode and c * (Hq // H) > 128:
