@@ -484,7 +484,7 @@ def main():
         trace_summary(a)
         return
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the step runs on one GPU only (no multi-GPU path); --gpus must be 1",
                           "n_gpus": a.gpus}), flush=True)
         sys.exit(2)
 

@@ -87,7 +87,7 @@ typedef struct ihipStream_t *pa_stream_t;
 typedef enum pa_status {
   PA_OK = 0,
   PA_ERR_INVALID_ARG = 1,  /* a null pointer, negative size or inconsistent shape  */
-  PA_ERR_UNSUPPORTED = 2,  /* a valid request this build does not implement        */
+  PA_ERR_UNSUPPORTED = 2,  /* a valid request the library does not implement      */
   PA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required           */
   PA_ERR_VALIDATION = 4,   /* metadata failed the consistency checks (PA_VALIDATE) */
   PA_ERR_HIP = 5,          /* a HIP runtime call failed                            */
