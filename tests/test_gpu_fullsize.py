@@ -1,7 +1,8 @@
 """GPU parity at the workloads' full sizes, every row, both forms of the step.
 
 For each seeded workload (the five reference configurations, the verify
-batch and the long prefill; seeds 1-4 on configurations 1, 2, 3 and 5) the
+batch and the long prefill; seeds 1-4 on configurations 1, 2, 3 and 5, seeds
+1-2 on the long-context decode and the verify batch) the
 HIP path runs once as three calls (pa_slot_mapping -> pa_write_kv ->
 pa_attention) and once as the one call with the KV update
 (pa_write_kv_attention), in the launch configuration bench.py times, and is
@@ -84,7 +85,8 @@ def _compare_rows(w, got, ref):
 
 
 CASES = [(c, 0, f) for c in (1, 2, 3, 4, 5, 6) for f in (False, True)] + \
-        [(c, s, f) for c in (1, 2, 3, 5) for s in (1, 2, 3, 4) for f in (False, True)]
+        [(c, s, f) for c in (1, 2, 3, 5) for s in (1, 2, 3, 4) for f in (False, True)] + \
+        [(c, s, f) for c in (4, 6) for s in (1, 2) for f in (False, True)]
 
 
 @pytest.mark.parametrize("cfg,seed,fused", CASES,
