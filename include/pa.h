@@ -241,8 +241,8 @@ pa_status pa_attention(const pa_kv_pool *pool, const pa_batch *batch, const void
  * for BF16 and FP8 pools, F32 for F32 pools).  slot_mapping: device int64
  * [num_tokens], written with the slots of the new tokens, or NULL.  The
  * other arguments, the workspace (pa_attention_workspace_bytes() covers both
- * calls) and the errors are those of pa_attention; on an error nothing is
- * written.  A request's new tokens must go to slots that no other request
+ * calls) and the errors are those of pa_attention; on an error other than
+ * PA_ERR_HIP nothing is written.  A request's new tokens must go to slots that no other request
  * of the batch reads (a block receiving new tokens belongs to one request,
  * as any KV-cache manager arranges); otherwise the result is undefined. */
 pa_status pa_write_kv_attention(const pa_kv_pool *pool, const pa_batch *batch, const void *query,
