@@ -210,8 +210,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
 
   // One item: keys [kv_begin, kv_last) of its rows.  pre: its first step's
   // K/V are already in kr / vr, from the block ids b0 .. b3 (next: idv_next).
-  auto run = [&](const int item_idx, const bool pre, int b0, int b1, int b2, int b3, int idv_next) {
-    const DecodeItem item = a.items[item_idx];
+  auto run = [&](const DecodeItem item, const bool pre, int b0, int b1, int b2, int b3, int idv_next) {
     const int token = uniform(item.token), req = uniform(item.req);
     const int kv_begin = uniform(item.kv_begin), kv_end = uniform(item.kv_end);
     const int part = uniform(item.part);
@@ -643,44 +642,62 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     }
   };
 
-  // the second item's first step, read now (PREFETCH)
-  uint4 kr2[PREFETCH ? 4 : 1][NKX];
-  VReg vr2[PREFETCH ? 2 : 1][NDG];
+  // The start of a wave: its items, then their first steps' block ids, then
+  // those steps' K/V (the first item's into kr / vr, the second's into kr2 /
+  // vr2 with PREFETCH), each round issued for both items before waiting, so
+  // the first item's loads start after one read of host memory and one of
+  // HBM rather than two of each.
   const int item_b = PAIR && a.pair_stride + bin < a.n_items ? a.pair_stride + bin : -1;
-  int pb0 = -1, pb1 = -1, pb2 = -1, pb3 = -1, pidv = -1;
-  bool pre_b = false;                            // the second item's first step was read ahead
-  if (PREFETCH && item_b >= 0) {
-    const DecodeItem ib = a.items[item_b];
-    const int req = uniform(ib.req), kv_begin = uniform(ib.kv_begin), kv_end = uniform(ib.kv_end);
-    const int ikind = uniform((int)ib.kind), iaux = uniform(ib.wpos);
+  const DecodeItem ia = a.items[bin];
+  DecodeItem ib{};
+  if (PAIR && item_b >= 0) ib = a.items[item_b];
+  // whether an item's first step can be read now (a kind-1 piece that stores
+  // its rows' K/V first reads after the stores), and its block ids: lane
+  // group j reads block j of the step, at an index clamped to the row's last
+  // block (always in the row)
+  struct First {
+    bool ok;
+    int idv, idv_next;
+  };
+  auto first_of = [&](const DecodeItem &it) -> First {
+    const int req = uniform(it.req), kv_begin = uniform(it.kv_begin), kv_end = uniform(it.kv_end);
+    const int ikind = uniform((int)it.kind), iaux = uniform(it.wpos);
     const bool own = ikind == 0 && iaux >= 0 && a.knew != nullptr;
     const int kv_last = own ? kv_end - 1 : kv_end;
-    // a kind-1 piece that stores its rows' K/V first is not read ahead
     const bool stores_rows = ikind == 1 && a.knew != nullptr && kv_end == iaux;
     const int32_t *__restrict__ btrow = ikind == 2 ? a.prefix_bt : a.block_table + (int64_t)req * a.bt_stride;
-    // ---- block ids: lane group j reads block j of a step ----
-    // (the read itself is unconditional, at an index clamped to the row's last
-    // block, so that no branch sits between the step's loads)
     const int last_bi = kv_last > 0 ? (kv_last - 1) >> 4 : 0;
     auto ids_of = [&](int itx) {
       const int bi = (itx >> 4) + j;
       const int id = btrow[bi < last_bi ? bi : last_bi];
       return bi <= last_bi ? id : -1;
     };
-    if (kv_begin < kv_last && !stores_rows) {
-      pre_b = true;
-      const int idv = ids_of(kv_begin);
-      pb0 = blk(idv, 0), pb1 = blk(idv, 1), pb2 = blk(idv, 2), pb3 = blk(idv, 3);
-      pidv = ids_of(kv_begin + kKeysPerIter);
-      if constexpr (PREFETCH) {
-        issue_k(kr2, pb0, pb1, pb2, pb3);
-        asm volatile("" ::: "memory");
-        issue_v(vr2, pb0, pb1, pb2, pb3);
-        asm volatile("" ::: "memory");
-      }
+    return First{kv_begin < kv_last && !stores_rows, ids_of(kv_begin), ids_of(kv_begin + kKeysPerIter)};
+  };
+  const First fa = first_of(ia);
+  First fb{false, -1, -1};
+  if (PREFETCH && item_b >= 0) fb = first_of(ib);
+  int a0 = -1, a1 = -1, a2 = -1, a3 = -1;
+  if (fa.ok) {
+    a0 = blk(fa.idv, 0), a1 = blk(fa.idv, 1), a2 = blk(fa.idv, 2), a3 = blk(fa.idv, 3);
+    issue_k(kr, a0, a1, a2, a3);
+    asm volatile("" ::: "memory");              // K before V, as in the loop
+    issue_v(vr, a0, a1, a2, a3);
+    asm volatile("" ::: "memory");
+  }
+  uint4 kr2[PREFETCH ? 4 : 1][NKX];
+  VReg vr2[PREFETCH ? 2 : 1][NDG];
+  int pb0 = -1, pb1 = -1, pb2 = -1, pb3 = -1;
+  if (PREFETCH && fb.ok) {
+    pb0 = blk(fb.idv, 0), pb1 = blk(fb.idv, 1), pb2 = blk(fb.idv, 2), pb3 = blk(fb.idv, 3);
+    if constexpr (PREFETCH) {
+      issue_k(kr2, pb0, pb1, pb2, pb3);
+      asm volatile("" ::: "memory");
+      issue_v(vr2, pb0, pb1, pb2, pb3);
+      asm volatile("" ::: "memory");
     }
   }
-  run(bin, false, -1, -1, -1, -1, -1);
+  run(ia, fa.ok, a0, a1, a2, a3, fa.idv_next);
   if (PAIR && item_b >= 0) {
     if constexpr (PREFETCH) {
 #pragma unroll
@@ -691,10 +708,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
       for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
         for (int dg = 0; dg < NDG; ++dg) vr[c2][dg] = vr2[c2][dg];
-      if (pre_b) run(item_b, true, pb0, pb1, pb2, pb3, pidv);
-      else run(item_b, false, -1, -1, -1, -1, -1);
+      run(ib, fb.ok, pb0, pb1, pb2, pb3, fb.idv_next);
     } else {
-      run(item_b, false, -1, -1, -1, -1, -1);
+      run(ib, false, -1, -1, -1, -1, -1);
     }
   }
 }
