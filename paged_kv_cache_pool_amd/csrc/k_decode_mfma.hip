@@ -141,11 +141,22 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   // there is one.  Otherwise one item per wave.
   const int n_first = PAIR ? a.pair_stride : a.n_items;
   if (unit >= n_first * a.num_kv_heads) {
-    // a scatter workgroup: no decode unit reads these rows, so they are
-    // written beside the decode work (in the launch's tail, as compute units
-    // free up) instead of by a launch of their own before it
+    // Workgroups after the decode units run in the launch's tail, as compute
+    // units free up.  Scatter workgroups write new rows that no decode unit
+    // reads (instead of a launch of their own before this one); copy
+    // workgroups move the later launches' work lists into device memory.
     const int u = unit - n_first * a.num_kv_heads;
-    if (u < a.n_wseg_units) {
+    if (u >= a.n_wseg_units) {
+      const int v0 = (u - a.n_wseg_units) * kCopyVecsPerUnit;
+      const int v1 = min(v0 + kCopyVecsPerUnit, a.copy_vecs);
+      uint4 t[kCopyVecsPerUnit / 64];
+#pragma unroll
+      for (int k = 0; k < kCopyVecsPerUnit / 64; ++k)
+        if (v0 + 64 * k + lane < v1) t[k] = a.copy_src[v0 + 64 * k + lane];
+#pragma unroll
+      for (int k = 0; k < kCopyVecsPerUnit / 64; ++k)
+        if (v0 + 64 * k + lane < v1) a.copy_dst[v0 + 64 * k + lane] = t[k];
+    } else {
       __shared__ __attribute__((aligned(16))) uint8_t vt[TILE];
       const int h = u % a.num_kv_heads;
       const WriteSeg sg = a.wseg[u / a.num_kv_heads];
@@ -730,7 +741,7 @@ static void launch_pair(const DecodeArgs &a, bool pair, int nh, dim3 grid, dim3 
 hipError_t launch_decode_mfma(const pa_kv_pool &p, const DecodeArgs &a, hipStream_t s) {
   const bool pair = a.pair_stride > 0;
   static_assert(kDecodeWaves == 1, "scatter workgroups follow the decode units one to one");
-  const int units = (pair ? a.pair_stride : a.n_items) * a.num_kv_heads + a.n_wseg_units;
+  const int units = (pair ? a.pair_stride : a.n_items) * a.num_kv_heads + a.n_wseg_units + a.n_copy_units;
   const dim3 grid((units + kDecodeWaves - 1) / kDecodeWaves), block(64 * kDecodeWaves);
   const int nh = a.max_cols > 16 ? 2 : 1;
   if (p.kv_dtype == PA_BF16 && p.head_dim == 128) launch_pair<KV_BF16, 128>(a, pair, nh, grid, block, s);

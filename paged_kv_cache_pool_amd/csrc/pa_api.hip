@@ -1346,6 +1346,16 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
   // launch of its own does, first.
   const bool fused_scatter = !plan.wseg.empty() && !plan.dec.empty() && !plan.wseg_read_by_dec &&
                              pool->kv_dtype != PA_F32 && !fork && !env_flag("PA_SCATTER_LAUNCH");
+  // The work lists of the launches after the split-K one (merge, extend and
+  // prefix-pass items), when they sit in host memory: copy workgroups of the
+  // split-K launch move them to the same offsets in the workspace, so those
+  // launches' waves read them from device memory instead of over PCIe.
+  const char *late = items;                      // where the later launches read their lists
+  const size_t late_bytes = plan.off_rtok - plan.off_merge;
+  const bool stage_late = items != (const char *)workspace && !plan.dec.empty() && late_bytes > 0 &&
+                          (!plan.merge.empty() || !plan.extw.empty() || !plan.pre.empty()) &&
+                          pool->kv_dtype != PA_F32 && !fork && !env_flag("PA_LISTS_IN_HOST");
+  if (stage_late) late = (const char *)workspace;
   // the split-K launch (with the scatter workgroups when it carries them)
   auto run_decode = [&]() -> pa_status {
     if (plan.dec.empty()) return PA_OK;
@@ -1387,6 +1397,12 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
       a.wseg = (const WriteSeg *)(items + plan.off_wseg);
       a.n_wseg_units = (int32_t)plan.wseg.size() * pool->num_kv_heads;
     }
+    if (stage_late) {
+      a.copy_src = (const uint4 *)(items + plan.off_merge);
+      a.copy_dst = (uint4 *)((char *)workspace + plan.off_merge);
+      a.copy_vecs = (int32_t)(late_bytes / 16);
+      a.n_copy_units = (a.copy_vecs + kCopyVecsPerUnit - 1) / kCopyVecsPerUnit;
+    }
     // q heads per launch: the whole GQA group where the registers allow it,
     // otherwise the group is covered by several launches (fp32 pools)
     const int g_max = 16;
@@ -1401,6 +1417,7 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
       a.knew = a.vnew = nullptr;                  // rows written by the first launch
       a.slots_out = nullptr;
       a.n_wseg_units = 0;
+      a.n_copy_units = 0;
     }
     return PA_OK;
   };
@@ -1436,7 +1453,7 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
     x.k_cache = pool->k_cache;
     x.v_cache = pool->v_cache;
     x.block_table = batch->block_table;
-    x.items = (const ExtendItem *)(items + plan.off_extw);
+    x.items = (const ExtendItem *)(late + plan.off_extw);
     x.part_ml = (float *)(ws + plan.off_ml);
     x.part_o = (float *)(ws + plan.off_o);
     x.n_items = (int32_t)plan.extw.size();
@@ -1459,7 +1476,7 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
       x.enc_v_scale = vscale;
     }
     if (with_merge) {
-      x.mitems = (const MergeItem *)(items + plan.off_merge);
+      x.mitems = (const MergeItem *)(late + plan.off_merge);
       x.n_merge_units = (int32_t)plan.merge.size() * num_q_heads;
     }
     x.release = release;
@@ -1475,7 +1492,7 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
     x.q = query;
     x.k_cache = pool->k_cache;
     x.v_cache = pool->v_cache;
-    x.pitems = (const PrefixItem *)(items + plan.off_pre);
+    x.pitems = (const PrefixItem *)(late + plan.off_pre);
     x.row_token = (const int32_t *)(items + plan.off_rtok);
     x.row_slot0 = (const int32_t *)(items + plan.off_rslot);
     x.prefix_bt = batch->block_table + (int64_t)plan.prefix_req * batch->bt_stride;
@@ -1504,7 +1521,7 @@ static pa_status attention_impl(const pa_kv_pool *pool, const pa_batch *batch, c
     m.out = output;
     m.part_ml = (const float *)(ws + plan.off_ml);
     m.part_o = (const float *)(ws + plan.off_o);
-    m.items = (const MergeItem *)(items + plan.off_merge);
+    m.items = (const MergeItem *)(late + plan.off_merge);
     m.n_items = (int32_t)plan.merge.size();
     m.num_q_heads = num_q_heads;
     if (plan.merge.size() <= (size_t)kMergeInline) {

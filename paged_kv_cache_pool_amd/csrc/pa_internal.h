@@ -166,7 +166,16 @@ struct DecodeArgs {
   // of wseg for kv head u % num_kv_heads, from knew / vnew.
   const WriteSeg *wseg;
   int32_t n_wseg_units;   // 0: none
+  // The later launches' work lists moved from the staging buffer (host
+  // memory) into the workspace by one-wave workgroups after those: workgroup
+  // n_dec + n_wseg_units + c copies 16-byte vectors 256 c .. 256 c + 255 of
+  // copy_vecs from copy_src to copy_dst.
+  const uint4 *copy_src;
+  uint4 *copy_dst;
+  int32_t copy_vecs;
+  int32_t n_copy_units;   // 0: none
 };
+constexpr int kCopyVecsPerUnit = 256;
 
 // The merge launch's arguments.  Up to kMergeInline items also travel in the
 // arguments themselves (in device memory when the kernel starts, where the
