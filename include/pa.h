@@ -379,7 +379,9 @@ const char *pa_last_error(void);
  * resets the records.  Launches captured into a HIP graph are not timed.
  * Work that rides in another kernel's launch is timed with that launch: the
  * one-call scatter of prefill rows in "k_decode" when no "k_write_new" runs,
- * the merge of split-K partials in "k_extend" when no "k_merge" runs. */
+ * the copy of the later launches' work lists into the workspace in
+ * "k_decode", the merge of split-K partials in "k_extend" when no "k_merge"
+ * runs. */
 pa_status pa_profile_enable(int32_t enable);
 pa_status pa_profile_read(const char *kernel, int32_t *launches, double *total_ms);
 

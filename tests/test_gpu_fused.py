@@ -523,3 +523,36 @@ def test_staging_ring_across_streams(R):
     torch.cuda.synchronize()
     assert torch.equal(a.out.view(torch.uint8), ref_a.view(torch.uint8))
     assert torch.equal(b.out.view(torch.uint8), ref_b.view(torch.uint8))
+
+
+@pytest.mark.parametrize("case", ["mixed", "prefix_pass"])
+def test_later_work_lists_in_device_or_host_memory(R, monkeypatch, case):
+    """The work lists of the launches after the split-K one (merge, extend and
+    prefix-pass items) are copied into the workspace by copy workgroups of the
+    split-K launch, and read there; with PA_LISTS_IN_HOST=1 they are read
+    from the host staging buffer.  Both give the same output bits and pool
+    bytes, and match the oracle: a mixed batch (split decode rows, prefill
+    chunks, carried scatter and merge) and a shared-prefix batch through the
+    MFMA prefix pass."""
+    if case == "mixed":
+        monkeypatch.setenv("PA_PARTITION_KEYS", "128")
+        w = W.build("lists_mixed", 23, num_q_heads=16, num_kv_heads=4, head_dim=128, block_size=16,
+                    num_blocks=260, kv_dtype=W.BF16, io_dtype=W.BF16,
+                    num_computed=[300, 0, 77, 1000, 45, 513, 64],
+                    num_scheduled=[1, 70, 1, 150, 9, 200, 1])
+    else:
+        monkeypatch.setenv("PA_PREFIX_PASS", "1")
+        w = W.prefix_fp8_decode(seed=5, num_seqs=24, prefix=512, lo=16, hi=200, num_blocks=900)
+    outs = []
+    for in_host in ("", "1"):
+        monkeypatch.setenv("PA_LISTS_IN_HOST", in_host)
+        say("work lists", case, "in host memory" if in_host else "copied to the workspace")
+        step = R.GpuStep(w, fused=True)
+        step.run()
+        torch.cuda.synchronize()
+        _check_out(w, step)
+        outs.append(step)
+    a, b = outs
+    assert torch.equal(a.out.view(torch.uint8), b.out.view(torch.uint8))
+    assert (a.slots.cpu().numpy() == b.slots.cpu().numpy()).all()
+    _assert_same_pool(a.pool, b.pool)
