@@ -147,15 +147,19 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     // workgroups move the later launches' work lists into device memory.
     const int u = unit - n_first * a.num_kv_heads;
     if (u >= a.n_wseg_units) {
+      // four loads per lane in flight (indices clamped to the last vector,
+      // so every read is in bounds), then the stores of the valid ones
+      static_assert(kCopyVecsPerUnit == 256, "four vectors per lane");
       const int v0 = (u - a.n_wseg_units) * kCopyVecsPerUnit;
-      const int v1 = min(v0 + kCopyVecsPerUnit, a.copy_vecs);
-      uint4 t[kCopyVecsPerUnit / 64];
-#pragma unroll
-      for (int k = 0; k < kCopyVecsPerUnit / 64; ++k)
-        if (v0 + 64 * k + lane < v1) t[k] = a.copy_src[v0 + 64 * k + lane];
-#pragma unroll
-      for (int k = 0; k < kCopyVecsPerUnit / 64; ++k)
-        if (v0 + 64 * k + lane < v1) a.copy_dst[v0 + 64 * k + lane] = t[k];
+      const int n = min(kCopyVecsPerUnit, a.copy_vecs - v0);
+      const uint4 *src = a.copy_src + v0;
+      uint4 *dst = a.copy_dst + v0;
+      const uint4 x0 = src[min(lane, n - 1)], x1 = src[min(64 + lane, n - 1)];
+      const uint4 x2 = src[min(128 + lane, n - 1)], x3 = src[min(192 + lane, n - 1)];
+      if (lane < n) dst[lane] = x0;
+      if (64 + lane < n) dst[64 + lane] = x1;
+      if (128 + lane < n) dst[128 + lane] = x2;
+      if (192 + lane < n) dst[192 + lane] = x3;
     } else {
       __shared__ __attribute__((aligned(16))) uint8_t vt[TILE];
       const int h = u % a.num_kv_heads;
@@ -186,6 +190,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
 
   uint4 kr[4][NKX];                              // [S product u][read x]
   VReg vr[2][NDG];                               // [chunk c][dim group]
+  // the second item's first step (PREFETCH), read during the first item's
+  // start, from the block ids pb0 .. pb3
+  uint4 kr2[PREFETCH ? 4 : 1][NKX];
+  VReg vr2[PREFETCH ? 2 : 1][NDG];
+  int pb0 = -1, pb1 = -1, pb2 = -1, pb3 = -1;
   // block of pair c that a lane reads (b0 .. b3: the step's four block ids)
   auto pick = [](int sel, int lo, int hi) { return sel ? hi : lo; };
   auto issue_k = [&](uint4 (&kd)[4][NKX], int b0, int b1, int b2, int b3) {
@@ -221,7 +230,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
 
   // One item: keys [kv_begin, kv_last) of its rows.  pre: its first step's
   // K/V are already in kr / vr, from the block ids b0 .. b3 (next: idv_next).
-  auto run = [&](const DecodeItem item, const bool pre, int b0, int b1, int b2, int b3, int idv_next) {
+  // fetch_next (PREFETCH): once this item's Q loads are issued, the next
+  // item's first step is read into kr2 / vr2 from the ids next_idv, so that
+  // those loads queue behind the Q rows rather than ahead of them.
+  auto run = [&](const DecodeItem item, const bool pre, int b0, int b1, int b2, int b3, int idv_next,
+                 const bool fetch_next, const int next_idv) {
     const int token = uniform(item.token), req = uniform(item.req);
     const int kv_begin = uniform(item.kv_begin), kv_end = uniform(item.kv_end);
     const int part = uniform(item.part);
@@ -282,17 +295,30 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     // (invalid columns are cleared with a mask, not a branch: a branch around
     // a loaded register makes the compiler wait for each load in turn)
     bf16x8_t qop[NH][NS];
+    uint4 qv[NH][NS];
 #pragma unroll
     for (int hf = 0; hf < NH; ++hf) {
       const uint16_t *qrow =
           (const uint16_t *)a.q + ((int64_t)crow[hf] * a.num_q_heads + qh0 + ch[hf]) * D;
-      uint4 v[NS];
 #pragma unroll
-      for (int c = 0; c < NS; ++c) v[c] = *(const uint4 *)(qrow + qdim(c));
+      for (int c = 0; c < NS; ++c) qv[hf][c] = *(const uint4 *)(qrow + qdim(c));
+    }
+    if constexpr (PREFETCH) {
+      if (fetch_next) {
+        asm volatile("" ::: "memory");          // after the Q loads
+        pb0 = blk(next_idv, 0), pb1 = blk(next_idv, 1), pb2 = blk(next_idv, 2), pb3 = blk(next_idv, 3);
+        issue_k(kr2, pb0, pb1, pb2, pb3);
+        asm volatile("" ::: "memory");
+        issue_v(vr2, pb0, pb1, pb2, pb3);
+        asm volatile("" ::: "memory");
+      }
+    }
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf) {
       const uint32_t qm = cval[hf] ? ~0u : 0u;
 #pragma unroll
       for (int c = 0; c < NS; ++c)
-        qop[hf][c] = as_bf16x8(make_uint4(v[c].x & qm, v[c].y & qm, v[c].z & qm, v[c].w & qm));
+        qop[hf][c] = as_bf16x8(make_uint4(qv[hf][c].x & qm, qv[hf][c].y & qm, qv[hf][c].z & qm, qv[hf][c].w & qm));
     }
 
     // ---- the new key's inputs (kind 0) ----
@@ -653,11 +679,12 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     }
   };
 
-  // The start of a wave: its items, then their first steps' block ids, then
-  // those steps' K/V (the first item's into kr / vr, the second's into kr2 /
-  // vr2 with PREFETCH), each round issued for both items before waiting, so
-  // the first item's loads start after one read of host memory and one of
-  // HBM rather than two of each.
+  // The start of a wave: its items, then their first steps' block ids (each
+  // round issued for both items before waiting), then the first item's first
+  // K/V into kr / vr.  The second item's first K/V (PREFETCH) follow the
+  // first item's Q loads, inside its body.  So the first item's loads start
+  // after one read of host memory and one of HBM, and its Q rows do not wait
+  // behind the second item's K/V.
   const int item_b = PAIR && a.pair_stride + bin < a.n_items ? a.pair_stride + bin : -1;
   const DecodeItem ia = a.items[bin];
   DecodeItem ib{};
@@ -696,19 +723,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     issue_v(vr, a0, a1, a2, a3);
     asm volatile("" ::: "memory");
   }
-  uint4 kr2[PREFETCH ? 4 : 1][NKX];
-  VReg vr2[PREFETCH ? 2 : 1][NDG];
-  int pb0 = -1, pb1 = -1, pb2 = -1, pb3 = -1;
-  if (PREFETCH && fb.ok) {
-    pb0 = blk(fb.idv, 0), pb1 = blk(fb.idv, 1), pb2 = blk(fb.idv, 2), pb3 = blk(fb.idv, 3);
-    if constexpr (PREFETCH) {
-      issue_k(kr2, pb0, pb1, pb2, pb3);
-      asm volatile("" ::: "memory");
-      issue_v(vr2, pb0, pb1, pb2, pb3);
-      asm volatile("" ::: "memory");
-    }
-  }
-  run(ia, fa.ok, a0, a1, a2, a3, fa.idv_next);
+  run(ia, fa.ok, a0, a1, a2, a3, fa.idv_next, PREFETCH && fb.ok, fb.idv);
   if (PAIR && item_b >= 0) {
     if constexpr (PREFETCH) {
 #pragma unroll
@@ -719,9 +734,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
       for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
         for (int dg = 0; dg < NDG; ++dg) vr[c2][dg] = vr2[c2][dg];
-      run(ib, fb.ok, pb0, pb1, pb2, pb3, fb.idv_next);
+      run(ib, fb.ok, pb0, pb1, pb2, pb3, fb.idv_next, false, -1);
     } else {
-      run(ib, false, -1, -1, -1, -1, -1);
+      run(ib, false, -1, -1, -1, -1, -1, false, -1);
     }
   }
 }

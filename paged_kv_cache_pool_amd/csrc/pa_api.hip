@@ -628,12 +628,26 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
   // there are n_bins); 0: the partition form above.
   int64_t n_bins = 0, pair_T = 0;
   std::vector<int32_t> tok_steps;
+  // A bin's second piece costs its wave about `pen` steps beyond its keys
+  // (the first piece's end, the second's rows and their Q): per-wave
+  // timelines of the decode layer and the mixed step show two-piece bins
+  // ending 6-10 us after single-piece bins of the same step count.  The
+  // cost is charged only where the bins still fit at the step count T found
+  // without it (a larger T would lengthen every single-piece bin), and not
+  // when the bins' pieces run as waves of their own (below).
+  const char *pair_env = getenv("PA_DECODE_PAIRS");
+  const bool pair_waves = pair_env ? atoi(pair_env) == 2 : pre_dec;
+  int64_t pen = 0;
+  int64_t pen_want = 2;
+  if (const char *v = getenv("PA_PAIR_PENALTY")) pen_want = std::max(0, atoi(v));
+  if (pair_waves) pen_want = 0;
   auto bins_for = [&](int64_t T, std::vector<std::array<int32_t, 4>> *pieces) {
     // greedy packing; pieces: (bin, slot, first step, end step) in token order
     int64_t bins = 0, load = T, np = 2;
     for (size_t x = 0; x < tok_steps.size(); ++x)
       for (int64_t o = 0, st = tok_steps[x]; o < st;) {
-        if (np == 2 || load == T) {
+        if (np == 1) load += pen;
+        if (np == 2 || load >= T) {
           ++bins;
           load = 0;
           np = 0;
@@ -665,6 +679,8 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
           if (bins_for(mid, nullptr) <= n_bins) hi = mid;
           else lo = mid + 1;
         }
+        pen = pen_want;
+        if (pen > 0 && bins_for(hi, nullptr) > n_bins) pen = 0;   // the cost does not fit at this T
         if (hi >= 8 || (penv && atoi(penv) > 0)) pair_T = hi;
       } else {
         n_bins = 0;
@@ -677,8 +693,6 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
   // hides (measured on the fp8 shared-prefix workload: split-K launch 36 us
   // against 52 us with one wave per SIMD; the prefix pass and a split-K
   // launch of the rows' own keys took 20 + 26 us)
-  const char *pair_env = getenv("PA_DECODE_PAIRS");
-  const bool pair_waves = pair_env ? atoi(pair_env) == 2 : pre_dec;
   std::vector<std::array<int32_t, 4>> pieces;
   if (paired) {
     const int64_t m = bins_for(pair_T, &pieces);
