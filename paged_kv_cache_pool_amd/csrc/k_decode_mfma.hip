@@ -369,18 +369,20 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
 #pragma unroll
         for (int u = 0; u < EPL; ++u) {
           const int x = r * EPL + u;             // K element x: dims qdim(x / 8) + x % 8; V element x: 16 (x / 4) + 4 j + x % 4
+          // (the element is picked with masks, not an index into kin / vin,
+          // which the compiler would turn into a private-memory array)
           uint32_t kw = 0, vw = 0;
 #pragma unroll
-          for (int c = 0; c < NS; ++c)
-            if (c == (x >> 3)) {
-              const uint32_t w[4] = {kin[c].x, kin[c].y, kin[c].z, kin[c].w};
+          for (int c = 0; c < NS; ++c) {
+            const uint32_t w[4] = {kin[c].x, kin[c].y, kin[c].z, kin[c].w};
 #pragma unroll
-              for (int h = 0; h < 4; ++h)
-                if (h == ((x & 7) >> 1)) kw = w[h];
-            }
+            for (int h = 0; h < 4; ++h)
+              kw |= w[h] & (0u - (uint32_t)(c == (x >> 3) && h == ((x & 7) >> 1)));
+          }
+          const uint32_t hi_half = 0u - (uint32_t)((x >> 1) & 1);   // .y when set, else .x
 #pragma unroll
           for (int dg = 0; dg < NDG; ++dg)
-            if (dg == (x >> 2)) vw = (x & 2) ? vin[dg].y : vin[dg].x;
+            vw |= ((vin[dg].x & ~hi_half) | (vin[dg].y & hi_half)) & (0u - (uint32_t)(dg == (x >> 2)));
           codes[0][j][x] = (uint8_t)pool_bits<KV_BF16, KV>((kw >> (16 * (x & 1))) & 0xffffu, a.enc_k_scale);
           codes[1][j][x] = (uint8_t)pool_bits<KV_BF16, KV>((vw >> (16 * (x & 1))) & 0xffffu, a.enc_v_scale);
         }
