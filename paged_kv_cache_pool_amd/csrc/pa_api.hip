@@ -661,8 +661,12 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
     return bins;
   };
   {
+    // (not by default when prefix items share the launch: their units are
+    // short and bound by their start, and the partition form spreads them
+    // over more waves; measured on the fp8 shared-prefix workload: 0.0405
+    // against 0.0413 ms per step)
     const char *penv = getenv("PA_DECODE_PAIRS");
-    const bool want = p.kv_dtype != PA_F32 && !(penv && atoi(penv) <= 0);
+    const bool want = p.kv_dtype != PA_F32 && !(penv && atoi(penv) <= 0) && (!pre_dec || (penv && atoi(penv) > 0));
     if (want && (4 * cus) % Hkv == 0 && !tok_keys.empty()) {
       int64_t S = 0, smax = 0;
       for (int32_t k : tok_keys) {
@@ -688,11 +692,11 @@ static void build_plan(const pa_kv_pool &p, const pa_batch &b, int32_t Hq, pa_dt
     }
   }
   const bool paired = pair_T > 0;
-  // two waves per SIMD by default when prefix items share the launch: their
-  // keys come from L2 and a step is bound by latency, which a second wave
-  // hides (measured on the fp8 shared-prefix workload: split-K launch 36 us
-  // against 52 us with one wave per SIMD; the prefix pass and a split-K
-  // launch of the rows' own keys took 20 + 26 us)
+  // (When the paired layout is forced on a launch with prefix items, its
+  // bins run as two waves per SIMD: the prefix keys come from L2 and a step
+  // is bound by latency, which a second wave hides; measured on the fp8
+  // shared-prefix workload: split-K launch 36 us against 52 us with one
+  // wave per SIMD.)
   std::vector<std::array<int32_t, 4>> pieces;
   if (paired) {
     const int64_t m = bins_for(pair_T, &pieces);
