@@ -85,7 +85,11 @@ void prof_begin(const char *name, hipStream_t s) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   ProfRec r{name, prof_event(), prof_event()};
   if (!r.start || !r.stop) return;
-  hipEventRecord(r.start, s);
+  if (hipEventRecord(r.start, s) != hipSuccess) {   // not timed: the events go back
+    g_prof_free.push_back(r.start);
+    g_prof_free.push_back(r.stop);
+    return;
+  }
   g_prof.push_back(r);
   g_prof_open = (int)g_prof.size() - 1;
 }
@@ -93,13 +97,18 @@ void prof_begin(const char *name, hipStream_t s) {
 void prof_end(hipStream_t s) {
   if (!g_prof_on || g_prof_open < 0) return;
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  hipEventRecord(g_prof[g_prof_open].stop, s);
+  if (hipEventRecord(g_prof[g_prof_open].stop, s) != hipSuccess) {   // the launch is not timed
+    const ProfRec r = g_prof.back();           // (the open record is the last one)
+    g_prof.pop_back();
+    g_prof_free.push_back(r.start);
+    g_prof_free.push_back(r.stop);
+  }
   g_prof_open = -1;
 }
 
 static void prof_reset_locked() {
   for (auto &r : g_prof) {
-    hipEventSynchronize(r.stop);
+    (void)hipEventSynchronize(r.stop);         // an error here only loses a timing record
     g_prof_free.push_back(r.start);
     g_prof_free.push_back(r.stop);
   }
@@ -176,7 +185,7 @@ static pa_status stage_acquire(size_t bytes, hipStream_t s, StageSlot **out, int
     slot.pending = false;
   }
   if (slot.cap < bytes) {
-    if (slot.host) hipHostFree(slot.host);
+    if (slot.host) (void)hipHostFree(slot.host);   // released above; nothing reads it
     slot.host = slot.dev = nullptr;
     slot.cap = 0;
     const size_t cap = std::max<size_t>(bytes, 64 << 10);
@@ -1700,7 +1709,8 @@ pa_status pa_placement_check(pa_placement *out) {
   uint32_t *one = ids, *two = one + 2 * n_one, *wide = two + 2 * n_two;
   e = launch_placement_probe(cus, one, two, wide, nullptr);
   if (e == hipSuccess) e = hipMemcpy(h.data(), ids, n_all * sizeof(uint32_t), hipMemcpyDeviceToHost);
-  hipFree(ids);
+  const hipError_t ef = hipFree(ids);
+  if (e == hipSuccess) e = ef;
   if (e != hipSuccess) return hip_fail(e, "placement check: probe");
   // a SIMD: XCD id, and HW_ID's SIMD (bits 5:4) and CU / array / engine
   // fields (bits 15:8); the wave slot and queue pipe fields are left out
