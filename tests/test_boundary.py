@@ -223,16 +223,17 @@ def test_planner_multirow_batches(B, monkeypatch):
         hq = hkv * g
         monkeypatch.setenv("PA_CHECK_PLAN", "1")
         for multi in ("1", None):
-            for pairs, part in [(None, None), ("2", None), ("0", None), ("0", "64"), ("0", "192")]:
+            for pairs, part, charge in [(None, None, None), ("1", None, "0"), ("1", None, "7"), ("2", None, None),
+                                        ("0", None, None), ("0", "64", None), ("0", "192", None)]:
                 for k, v in [("PA_DECODE_PAIRS", pairs), ("PA_PARTITION_KEYS", part),
-                             ("PA_MULTIROW", multi)]:
+                             ("PA_MULTIROW", multi), ("PA_PAIR_PENALTY", charge)]:
                     if v is None:
                         monkeypatch.delenv(k, raising=False)
                     else:
                         monkeypatch.setenv(k, v)
                 nl = B.lib.pa_attention_workspace_bytes(C.byref(p), C.byref(b), hq)
-                assert nl > 0, (it, multi, pairs, part, B.lib.pa_last_error().decode())
-        for k in ("PA_CHECK_PLAN", "PA_PARTITION_KEYS", "PA_DECODE_PAIRS", "PA_MULTIROW"):
+                assert nl > 0, (it, multi, pairs, part, charge, B.lib.pa_last_error().decode())
+        for k in ("PA_CHECK_PLAN", "PA_PARTITION_KEYS", "PA_DECODE_PAIRS", "PA_MULTIROW", "PA_PAIR_PENALTY"):
             monkeypatch.delenv(k, raising=False)
 
 

@@ -194,6 +194,22 @@ def test_attention_long_and_split(R, monkeypatch, pairs):
     _check_attention(w, step)
 
 
+@pytest.mark.parametrize("charge", ["0", "2", "7"])
+def test_paired_bins_second_piece_charge(R, monkeypatch, charge):
+    """The paired layout with the second piece of a bin charged 0, 2 (the
+    default) or 7 steps.  For this batch (40 rows of 512-6000 keys, bins of
+    18 steps) a charge of 2 fits and two-piece bins carry fewer steps, and 7
+    does not fit, so the plan falls back to no charge.  The attention matches
+    the oracle on every row in the one-call form."""
+    monkeypatch.setenv("PA_PAIR_PENALTY", charge)
+    say("paired bins, second-piece charge", charge)
+    w = W.llama8b_decode(seed=11, num_seqs=40, lo=512, hi=6000, num_blocks=16000)
+    step = R.GpuStep(w, fused=True)
+    step.run()
+    torch.cuda.synchronize()
+    _check_attention(w, step)
+
+
 @pytest.mark.parametrize("n,lo,hi", [(200, 512, 1500), (300, 16, 400)])
 def test_attention_many_decode_rows(R, n, lo, hi):
     """Many decode rows on the Llama-3-8B layer shape: 200 rows of 512-1500
